@@ -1,0 +1,240 @@
+"""Seeded synthetic inputs for the routed-expert MoE forward and the fused
+SwiGLU + FP8 quantizer.
+
+This module holds the workload shapes and the random inputs only. It performs
+no step of the method (no routing, no tables, no GEMM, no activation, no
+quantization), so the oracle and the HIP path can both take their inputs from
+here without sharing any of the method's arithmetic.
+
+Generator
+---------
+Every element is a pure function of (tensor key, element index): a 32-bit
+integer hash ("lowbias32", an xorshift-multiply mixer published by C. Wellons
+in the hash-prospector project) feeds four 22-bit uniform integers whose sum
+is an Irwin-Hall(4) variate. Centred and scaled, it approximates N(0, sigma^2)
+with mean 0, the requested variance and tails cut at +-3.46 sigma:
+
+    S = u1 + u2 + u3 + u4          (integer, exact)
+    z = float32(S - 2*(2^22-1)) * float32(sigma / sqrt(4*(2^44-1)/12))
+
+S - mean is below 2^24 in magnitude, so the conversion is exact and the single
+float32 multiply is correctly rounded on any IEEE device. bf16 tensors are
+that float32 value rounded to nearest-even by torch. The arithmetic is written
+in torch int64 ops, so CPU and GPU produce the same bits, and any index range
+of a tensor (one expert's weights, one token's row) can be regenerated alone.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_M32 = 0xFFFFFFFF
+_U22 = (1 << 22) - 1
+_IH_MEAN = 2 * _U22                     # mean of the sum of four uniforms on [0, 2^22-1]
+_IH_STD = math.sqrt(4.0 * ((_U22 + 1) ** 2 - 1) / 12.0)
+
+
+def _mul32(x: torch.Tensor, c: int) -> torch.Tensor:
+    """(x * c) mod 2^32 for 0 <= x < 2^32, kept inside int64 without overflow."""
+    lo = c & 0xFFFF
+    hi = c >> 16
+    return (x * lo + (((x * hi) & 0xFFFF) << 16)) & _M32
+
+
+def _mix32(x: torch.Tensor) -> torch.Tensor:
+    """lowbias32 integer mixer on values in [0, 2^32)."""
+    x = x ^ (x >> 16)
+    x = _mul32(x, 0x7FEB352D)
+    x = x ^ (x >> 15)
+    x = _mul32(x, 0x846CA68B)
+    x = x ^ (x >> 16)
+    return x
+
+
+def _mix32_int(x: int) -> int:
+    x &= _M32
+    x ^= x >> 16
+    x = (x * 0x7FEB352D) & _M32
+    x ^= x >> 15
+    x = (x * 0x846CA68B) & _M32
+    x ^= x >> 16
+    return x
+
+
+def tensor_key(*parts: int) -> int:
+    """32-bit key for a tensor from small integers (workload id, tensor tag, ...)."""
+    k = 0x6A09E667
+    for p in parts:
+        k = _mix32_int(k ^ _mix32_int(int(p) + 0x9E3779B9))
+    return k
+
+
+def _normal_f32_range(key: int, start: int, stop: int, sigma: float,
+                      device: torch.device | str) -> torch.Tensor:
+    n = stop - start
+    if n <= 0:
+        return torch.empty(0, dtype=torch.float32, device=device)
+    i = torch.arange(start, stop, dtype=torch.int64, device=device)
+    base = _mix32(_mix32((i & _M32) ^ key) ^ ((i >> 32) & _M32))
+    h1 = _mix32(base ^ 0x85EBCA6B)
+    h2 = _mix32(base ^ 0xC2B2AE35)
+    h3 = _mix32(base ^ 0x27D4EB2F)
+    del base, i
+    u4 = ((h1 >> 22) | ((h2 >> 22) << 10) | ((h3 >> 22) << 20)) & _U22
+    s = (h1 & _U22) + (h2 & _U22) + (h3 & _U22) + u4
+    del h1, h2, h3, u4
+    z = (s - _IH_MEAN).to(torch.float32)
+    scale = torch.tensor(sigma / _IH_STD, dtype=torch.float32)
+    return z * scale.to(device)
+
+
+def normal_f32(key: int, shape: Sequence[int], sigma: float = 1.0,
+               device: torch.device | str = "cpu", start: int = 0,
+               chunk: int = 1 << 26) -> torch.Tensor:
+    """float32 tensor of `shape` holding elements start.. of the keyed stream."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = torch.empty(n, dtype=torch.float32, device=device)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        out[c0:c1] = _normal_f32_range(key, start + c0, start + c1, sigma, device)
+    return out.view(*shape)
+
+
+def normal_bf16(key: int, shape: Sequence[int], sigma: float = 1.0,
+                device: torch.device | str = "cpu", start: int = 0,
+                chunk: int = 1 << 26) -> torch.Tensor:
+    """bf16 tensor: the float32 stream rounded to nearest-even by torch."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = torch.empty(n, dtype=torch.bfloat16, device=device)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        out[c0:c1] = _normal_f32_range(key, start + c0, start + c1, sigma, device).to(torch.bfloat16)
+    return out.view(*shape)
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    """Raw bit patterns of a bf16 tensor as a host uint16 array."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Workloads
+# --------------------------------------------------------------------------
+TAG_HIDDEN, TAG_LOGITS, TAG_BIAS, TAG_WGU, TAG_WD, TAG_SWGU, TAG_SWD, TAG_QUANT = range(8)
+
+
+@dataclasses.dataclass(frozen=True)
+class MoEConfig:
+    """One routed-expert forward workload.
+
+    hidden [T,H] bf16 ~N(0,1); router logits [T,E] fp32 ~N(0,1) (+ a per-expert
+    Zipf bias when `zipf_s` is set); w_gate_up [E,2F,H] bf16 ~N(0,1/H) with the
+    gate rows first; w_down [E,H,F] bf16 ~N(0,1/F); optional shared expert
+    w_gate_up [2Fs,H] ~N(0,1/H), w_down [H,Fs] ~N(0,1/Fs).
+    """
+    cid: int
+    name: str
+    T: int
+    H: int
+    F: int
+    E: int
+    top_k: int
+    padding_m: int
+    block_m: int
+    rsf: float = 1.0
+    zipf_s: Optional[float] = None
+    shared_F: int = 0
+
+    @property
+    def numel(self) -> int:
+        return self.T * self.top_k
+
+
+@dataclasses.dataclass(frozen=True)
+class QuantConfig:
+    """Fused SwiGLU + FP8 quantizer workload: x [M, 2F] bf16 ~N(0,1), gate|up halves."""
+    cid: int
+    name: str
+    M: int
+    F: int
+
+
+CONFIGS = {
+    "tiny": MoEConfig(0, "tiny", T=64, H=128, F=256, E=8, top_k=2, padding_m=64, block_m=64),
+    "qwen3_decode": MoEConfig(1, "qwen3_decode", T=512, H=2048, F=768, E=128, top_k=8,
+                              padding_m=128, block_m=128),
+    "qwen3_prefill": MoEConfig(2, "qwen3_prefill", T=4096, H=2048, F=768, E=128, top_k=8,
+                               padding_m=128, block_m=128),
+    "dsv3_prefill": MoEConfig(3, "dsv3_prefill", T=4096, H=7168, F=2048, E=256, top_k=8,
+                              padding_m=128, block_m=128, rsf=2.827, zipf_s=1.1, shared_F=2048),
+}
+QUANT_CONFIG = QuantConfig(4, "swiglu_quant_fp8", M=32768, F=2048)
+QUANT_EDGE_M = (0, 1, 127, 128, 129)
+
+
+def zipf_bias(cfg: MoEConfig) -> np.ndarray:
+    """Per-expert logit bias -s*ln(rank), rank a seeded permutation of 1..E (float32)."""
+    rng = np.random.Generator(np.random.PCG64(tensor_key(cfg.cid, TAG_BIAS)))
+    rank = rng.permutation(cfg.E) + 1
+    return (-cfg.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
+
+
+def hidden(cfg: MoEConfig, device="cpu", rows: Optional[slice] = None) -> torch.Tensor:
+    r0, r1 = (0, cfg.T) if rows is None else (rows.start, rows.stop)
+    return normal_bf16(tensor_key(cfg.cid, TAG_HIDDEN), (r1 - r0, cfg.H), 1.0, device,
+                       start=r0 * cfg.H)
+
+
+def router_logits(cfg: MoEConfig, device="cpu", rows: Optional[slice] = None) -> torch.Tensor:
+    r0, r1 = (0, cfg.T) if rows is None else (rows.start, rows.stop)
+    z = normal_f32(tensor_key(cfg.cid, TAG_LOGITS), (r1 - r0, cfg.E), 1.0, device,
+                   start=r0 * cfg.E)
+    if cfg.zipf_s is not None:
+        z = z + torch.from_numpy(zipf_bias(cfg)).to(device)
+    return z
+
+
+def w_gate_up(cfg: MoEConfig, device="cpu", experts: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """[E,2F,H] (or [len(experts),2F,H] for a subset), gate rows 0..F-1, up rows F..2F-1."""
+    per = 2 * cfg.F * cfg.H
+    key = tensor_key(cfg.cid, TAG_WGU)
+    sigma = 1.0 / math.sqrt(cfg.H)
+    if experts is None:
+        return normal_bf16(key, (cfg.E, 2 * cfg.F, cfg.H), sigma, device)
+    return torch.stack([normal_bf16(key, (2 * cfg.F, cfg.H), sigma, device, start=e * per)
+                        for e in experts]) if len(experts) else \
+        torch.empty(0, 2 * cfg.F, cfg.H, dtype=torch.bfloat16, device=device)
+
+
+def w_down(cfg: MoEConfig, device="cpu", experts: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """[E,H,F] (or a subset of experts)."""
+    per = cfg.H * cfg.F
+    key = tensor_key(cfg.cid, TAG_WD)
+    sigma = 1.0 / math.sqrt(cfg.F)
+    if experts is None:
+        return normal_bf16(key, (cfg.E, cfg.H, cfg.F), sigma, device)
+    return torch.stack([normal_bf16(key, (cfg.H, cfg.F), sigma, device, start=e * per)
+                        for e in experts]) if len(experts) else \
+        torch.empty(0, cfg.H, cfg.F, dtype=torch.bfloat16, device=device)
+
+
+def shared_w_gate_up(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    return normal_bf16(tensor_key(cfg.cid, TAG_SWGU), (2 * cfg.shared_F, cfg.H),
+                       1.0 / math.sqrt(cfg.H), device)
+
+
+def shared_w_down(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    return normal_bf16(tensor_key(cfg.cid, TAG_SWD), (cfg.H, cfg.shared_F),
+                       1.0 / math.sqrt(cfg.shared_F), device)
+
+
+def quant_input(M: int, F: int, device="cpu", rows: Optional[slice] = None,
+                cid: int = QUANT_CONFIG.cid) -> torch.Tensor:
+    """x [M, 2F] bf16 ~N(0,1): columns 0..F-1 are the gate half, F..2F-1 the up half."""
+    r0, r1 = (0, M) if rows is None else (rows.start, rows.stop)
+    return normal_bf16(tensor_key(cid, TAG_QUANT, M), (r1 - r0, 2 * F), 1.0, device,
+                       start=r0 * 2 * F)
