@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config dsv3_prefill]
+
+A step is one whole forward (routing, dispatch tables, permute, gate_up GEMM
+with fused SwiGLU, down GEMM, shared expert, unpermute) over one batch of
+seeded synthetic inputs that are resident in HBM before timing starts. The
+SwiGLU + FP8 quantizer is timed on its own workload (M=32768, F=2048) in the
+same run and reported under "kernels".
+
+Prints one JSON line. `value` is forward TFLOP/s (6*T*k*H*F routed plus
+6*T*H*Fs shared, per forward, over the timed steps); `ms_per_step` is ms per
+forward. `roofline` is for the dominant kernel (grouped_gemm_gate_up): its
+average duration comes from HIP events recorded on the launch stream around
+every launch inside the timed region; the algorithmic bytes and FLOPs per
+launch are counted from the realized routing (active experts' weights once,
+activations in and out once). `cpu_baseline` times the oracle on a bounded
+sample of tokens on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="dsv3_prefill",
+                   choices=["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=24, help="tokens in the oracle's timed sample")
+    p.add_argument("--unfused", action="store_true", help="gate_up GEMM then a separate SwiGLU kernel")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the multi-GPU (expert-parallel / tensor-parallel) path is "
+              "not built, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_synth
+    import mixture_experts_routed_moe_amd as mx
+
+    dev = torch.device("cuda", 0)
+    cfg = moe_synth.CONFIGS[args.config]
+    fuse = not args.unfused
+    t_gen = time.time()
+    hidden = moe_synth.hidden(cfg, dev)
+    logits = moe_synth.router_logits(cfg, dev)
+    wgu = moe_synth.w_gate_up(cfg, dev)
+    wd = moe_synth.w_down(cfg, dev)
+    swgu = moe_synth.shared_w_gate_up(cfg, dev) if cfg.shared_F else None
+    swd = moe_synth.shared_w_down(cfg, dev) if cfg.shared_F else None
+    shape = mx.MoEShape(cfg.T, cfg.H, cfg.F, cfg.E, cfg.top_k, cfg.padding_m, cfg.block_m, cfg.shared_F)
+    bufs = mx.MoEBuffers(shape, dev, fuse_swiglu=fuse)
+    qx = moe_synth.quant_input(moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F, dev)
+    qbufs = mx.swiglu_quant_fp8(qx)
+    torch.cuda.synchronize()
+    print(f"# inputs generated on the GPU in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    stages = ["topk_softmax", "align", "permute", "gate_up", "down", "shared_gate_up", "shared_down",
+              "unpermute"]
+    ev_log = {s: [] for s in stages}
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(record: bool):
+        def run(name, fn):
+            if record:
+                a = ev()
+                fn()
+                ev_log[name].append((a, ev()))
+            else:
+                fn()
+        tb = bufs.tables
+        run("topk_softmax", lambda: mx.moe_topk_softmax(logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights))
+        run("align", lambda: mx.moe_align(bufs.topk_ids, cfg.E, cfg.padding_m, cfg.block_m, tb))
+        run("permute", lambda: mx.moe_permute(hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm))
+        if fuse:
+            run("gate_up", lambda: mx.grouped_gemm_gate_up(bufs.x_perm, wgu, tb, cfg.padding_m, cfg.block_m,
+                                                           True, bufs.h))
+        else:
+            run("gate_up", lambda: (mx.grouped_gemm_gate_up(bufs.x_perm, wgu, tb, cfg.padding_m, cfg.block_m,
+                                                            False, bufs.gate_up), mx.swiglu(bufs.gate_up, bufs.h)))
+        run("down", lambda: mx.grouped_gemm_down(bufs.h, wd, tb, cfg.padding_m, cfg.block_m, bufs.y))
+        addend = None
+        if cfg.shared_F:
+            run("shared_gate_up", lambda: mx.grouped_gemm_gate_up(hidden, swgu, None, cfg.padding_m, cfg.block_m,
+                                                                  True, bufs.shared_h))
+            run("shared_down", lambda: mx.grouped_gemm_down(bufs.shared_h, swd, None, cfg.padding_m, cfg.block_m,
+                                                            bufs.shared_y))
+            addend = bufs.shared_y
+        run("unpermute", lambda: mx.moe_unpermute(bufs.y, tb["pair_to_row"], bufs.topk_weights, cfg.rsf, addend,
+                                                  bufs.out))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    stage_ms = {s: (sum(a.elapsed_time(b) for a, b in v) / len(v)) for s, v in ev_log.items() if v}
+
+    # realized routing (read after the timed region)
+    gs = bufs.tables["group_sizes"].cpu().numpy()
+    active = int((gs > 0).sum())
+    numel, H, F, E = cfg.numel, cfg.H, cfg.F, cfg.E
+    flop_gate_up = 4.0 * numel * H * F
+    flop_down = 2.0 * numel * H * F
+    flop_shared = 6.0 * cfg.T * H * cfg.shared_F
+    flop_fwd = flop_gate_up + flop_down + flop_shared
+    h_cols = F if fuse else 2 * F
+    bytes_gate_up = active * 2.0 * F * H * 2 + numel * H * 2 + numel * h_cols * 2
+    bytes_down = active * 1.0 * H * F * 2 + numel * F * 2 + numel * H * 2
+    bytes_permute = (cfg.T + numel) * H * 2 + 4 * numel
+    bytes_unpermute = numel * H * 2 + 8 * cfg.T * cfg.top_k + cfg.T * H * 2 * (2 if cfg.shared_F else 1)
+
+    def kern(name, flop, byts):
+        ms = stage_ms.get(name)
+        if not ms:
+            return None
+        s = ms * 1e-3
+        return {"ms": round(ms, 4), "tflops": round(flop / s / 1e12, 2) if flop else None,
+                "gbs": round(byts / s / 1e9, 1), "mfma_frac": round(flop / s / 1e12 / BF16_PEAK_TFLOPS, 4) if flop else None,
+                "hbm_frac": round(byts / s / 1e9 / HBM_PEAK_GBS, 4),
+                "roofline_frac": round(max(flop / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) / s, 4)}
+
+    kernels = {
+        "topk_softmax": kern("topk_softmax", 0, cfg.T * E * 4 + cfg.T * cfg.top_k * 8),
+        "align": kern("align", 0, numel * 4 * 3),
+        "permute": kern("permute", 0, bytes_permute),
+        "grouped_gemm_gate_up": kern("gate_up", flop_gate_up, bytes_gate_up),
+        "grouped_gemm_down": kern("down", flop_down, bytes_down),
+        "unpermute": kern("unpermute", 0, bytes_unpermute),
+    }
+    if cfg.shared_F:
+        Fs = cfg.shared_F
+        kernels["shared_gate_up"] = kern("shared_gate_up", 4.0 * cfg.T * H * Fs, 2.0 * Fs * H * 2 + cfg.T * H * 2 + cfg.T * Fs * 2)
+        kernels["shared_down"] = kern("shared_down", 2.0 * cfg.T * H * Fs, 1.0 * H * Fs * 2 + cfg.T * Fs * 2 + cfg.T * H * 2)
+
+    # fused SwiGLU + FP8 quantizer on its own workload, HIP events around each launch
+    qM, qF = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
+    for _ in range(5):
+        mx.swiglu_quant_fp8(qx, qbufs)
+    qev = []
+    for _ in range(max(20, args.steps)):
+        a = ev()
+        mx.swiglu_quant_fp8(qx, qbufs)
+        qev.append((a, ev()))
+    torch.cuda.synchronize()
+    q_ms = sum(a.elapsed_time(b) for a, b in qev) / len(qev)
+    qm_pad = -(-qM // 128) * 128
+    q_bytes = qM * 4 * qF + qM * qF + 4 * qM * qF // 128 + qF * qm_pad + 4 * (qF // 128) * (qm_pad // 128)
+    kernels["swiglu_quant_fp8"] = {"workload": f"M={qM},F={qF}", "ms": round(q_ms, 4),
+                                   "gbs": round(q_bytes / q_ms / 1e6, 1),
+                                   "hbm_frac": round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    gu = kernels["grouped_gemm_gate_up"]
+    gu_s = stage_ms["gate_up"] * 1e-3
+    roofline = {"kernel": "grouped_gemm_gate_up" + ("(+swiglu)" if fuse else ""),
+                "bound": "hbm" if bytes_gate_up / (HBM_PEAK_GBS * 1e9) >= flop_gate_up / (BF16_PEAK_TFLOPS * 1e12) else "mfma",
+                "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None,
+                "bytes_per_launch": bytes_gate_up, "flop_per_launch": flop_gate_up,
+                "launch_ms": round(stage_ms["gate_up"], 4), "mfma_frac": gu["mfma_frac"], "hbm_frac": gu["hbm_frac"]}
+    if roofline["bound"] == "hbm":
+        roofline.update(achieved=round(bytes_gate_up / gu_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        roofline.update(achieved=round(flop_gate_up / gu_s / 1e12, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, args.cpu_tokens)
+
+    value = flop_fwd / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": "routed-experts fwd ms + grouped-GEMM TFLOPS (% MFMA peak), T=4096",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded counter-based generator, N(0,1)-shaped inputs, random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": H, "F": F, "E": E, "top_k": cfg.top_k,
+                   "padding_m": cfg.padding_m, "block_m": cfg.block_m, "routed_scaling_factor": cfg.rsf,
+                   "zipf_bias_s": cfg.zipf_s, "shared_F": cfg.shared_F, "fused_swiglu": fuse,
+                   "active_experts": active, "max_rows_per_expert": int(gs.max()),
+                   "parallelism": "single GPU"},
+        "grouped_gemm_tflops": round((flop_gate_up + flop_down) / ((stage_ms["gate_up"] + stage_ms["down"]) * 1e-3) / 1e12, 2),
+        "grouped_gemm_mfma_frac": round((flop_gate_up + flop_down) / ((stage_ms["gate_up"] + stage_ms["down"]) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, n_tokens):
+    """The oracle, as it stands, on a bounded sample of tokens: TFLOP/s on the host cores."""
+    import torch
+    import moe_synth
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(1234)
+    tokens = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    tsel = torch.as_tensor(tokens, device=hidden.device)
+    hid = moe_synth.bits16(hidden[tsel])
+    lg = logits[tsel].cpu().numpy()
+    ids, _ = oracle.route(lg, cfg.top_k)
+    used = np.unique(ids)
+    sel = torch.as_tensor(used, device=wgu.device)
+    wgu_h = moe_synth.bits16(wgu[sel])
+    wd_h = moe_synth.bits16(wd[sel])
+    swgu_h = moe_synth.bits16(swgu) if swgu is not None else None
+    swd_h = moe_synth.bits16(swd) if swd is not None else None
+    remap = np.zeros(cfg.E, np.int64)
+    remap[used] = np.arange(used.size)
+    # the oracle's forward on the sampled tokens, restricted to the experts they reach
+    t0 = time.perf_counter()
+    ids2, w = oracle.route(lg, cfg.top_k)
+    ids_r = remap[ids2].astype(np.int32)
+    tab = oracle.dispatch_tables(ids_r, used.size, cfg.padding_m, cfg.block_m)
+    xp = oracle.permute(hid, tab["sorted_pair"], cfg.top_k)
+    gu = oracle.grouped_gemm(xp, wgu_h, tab["group_sizes"], tab["group_offsets"])
+    h = oracle.swiglu(gu, cfg.F)
+    y = oracle.grouped_gemm(h, wd_h, tab["group_sizes"], tab["group_offsets"])
+    shared = oracle.shared_expert(hid, swgu_h, swd_h) if swgu_h is not None else None
+    oracle.unpermute(y, tab["pair_to_row"], w, cfg.top_k, cfg.rsf, shared)
+    dt = time.perf_counter() - t0
+    flop = 6.0 * tokens.size * cfg.top_k * cfg.H * cfg.F + 6.0 * tokens.size * cfg.H * cfg.shared_F
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{tokens.size} of {cfg.T} tokens of {cfg.name} ({used.size} experts reached), "
+                      f"full forward incl. shared expert, float64 GEMMs; {dt:.1f}s",
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * moe_mi355x.h - C ABI of the MI355X (gfx950) routed-expert MoE forward and
+ * fused SwiGLU + FP8 activation quantizer (libmoe_mi355x.so).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are device memory owned by the caller, contiguous and
+ *     row-major; bf16 tensors are passed as uint16_t bit patterns. 16-byte
+ *     vectorised tensors (bf16 activations and weights, FP8 outputs) must be
+ *     16-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream). No entry point synchronises the stream or the device, copies
+ *     to or from the host, or allocates memory; scratch space, where needed,
+ *     is a caller-provided workspace.
+ *   - Return value: MOE_OK, or a negative code. On MOE_ERR_INVALID_ARG and
+ *     MOE_ERR_UNSUPPORTED nothing has been enqueued and outputs are untouched.
+ *     moe_last_error() gives a message for the calling thread's last failure.
+ *   - Empty work (T = 0 or M = 0) returns MOE_OK and enqueues nothing unless
+ *     the entry point says otherwise.
+ *   - Results are deterministic: the same inputs give the same bytes, run to
+ *     run (no atomics whose order reaches an output).
+ *
+ * Page citations name the five source pages by title:
+ *   TileOPs #778  "[Feat][MoE] SharedFusedMoE with native shared expert kernel and TP support"
+ *   TileOPs #1580 "[Perf][MoE] Grouped-GEMM TMA OOB zero-fill + unpermute out=: ..."
+ *   pypto-lib #809 "perf(dsv4/moe): predicate empty routed-expert stages"
+ *   TileLang tutorial Example 07 "MoE dispatch contract and quantized GEMM"
+ *   xtuner #2089 "[Feat] Fuse MoE activation FP8 quantization kernels"
+ */
+#ifndef MOE_MI355X_H_
+#define MOE_MI355X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, bad shape, misalignment */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid but outside what the kernels handle */
+#define MOE_ERR_HIP (-3)         /* a HIP launch reported an error */
+
+/* Message for the calling thread's most recent failure ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI revision of this header; bumps whenever a signature changes. */
+int moe_abi_version(void);
+
+/* Number of padded row blocks the grouped GEMMs iterate over, an upper bound
+ * that depends only on host-known sizes:
+ *     ceil(numel / block_m) + E * (padding_m / block_m).
+ * Tutorial Example 07, expected output: 18 pairs, 4 experts, 128-row blocks
+ * and padding give 5 = ceil(18/128) + 4. The page always has padding_m ==
+ * block_m; a larger multiple lets each expert's padding span that many
+ * blocks. Returns -1 for non-positive block_m / padding_m or padding_m not a
+ * multiple of block_m. Host-only, no device work. */
+int64_t moe_num_blocks(int64_t numel, int E, int block_m, int padding_m);
+
+/* Bytes of device workspace moe_align needs for numel = T*top_k pairs over E
+ * experts. */
+size_t moe_align_workspace_bytes(int64_t numel, int E);
+
+/* Top-k softmax routing.
+ * logits       [T, E] float32 router scores ("gating", TileOPs #778,
+ *              "Partial output contract").
+ * topk_ids     [T, top_k] int32 out: experts in descending-logit order; equal
+ *              logits go to the lower expert id.
+ * topk_weights [T, top_k] float32 out: softmax over all E renormalised over
+ *              the selected experts (equal to a softmax over the selected
+ *              logits), so each row sums to 1.
+ * Limits: 1 <= E <= 1024, 1 <= top_k <= min(E, 16). Non-finite logits are
+ * not supported. */
+int moe_topk_softmax(const float* logits, int64_t T, int E, int top_k, int32_t* topk_ids,
+                     float* topk_weights, hipStream_t stream);
+
+/* Dispatch tables of Tutorial Example 07 ("moe_dispatch_contract.py": the
+ * four host-side tables and the kernel-side row recovery), built on the
+ * device with wavefront ballots and prefix scans; no host synchronisation.
+ * topk_ids             [T, top_k] int32 in, each in [0, E).
+ * group_sizes          [E] out: pairs routed to each expert.
+ * group_offsets        [E] out: exclusive prefix sum of group_sizes (start of
+ *                      each expert's rows in the compact layout).
+ * group_padded_offsets [E] out: exclusive prefix sum of the sizes rounded up
+ *                      to padding_m (an empty expert pads to 0 rows).
+ * group_idx_for_bx     [moe_num_blocks(T*top_k, E, block_m, padding_m)] out:
+ *                      expert owning padded row block bx = the last expert
+ *                      whose padded offset is <= bx*block_m.
+ * sorted_pair          [T*top_k] out: pair index p = t*top_k + j of compact
+ *                      row r; rows of one expert keep ascending p.
+ * pair_to_row          [T*top_k] out: inverse permutation of sorted_pair.
+ * workspace            >= moe_align_workspace_bytes(T*top_k, E) bytes.
+ * Requires padding_m % block_m == 0, 1 <= E <= 1024, T*top_k < 2^31.
+ * With T = 0 the E-sized tables and group_idx_for_bx are still written. */
+int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_m, int block_m,
+              int32_t* group_sizes, int32_t* group_offsets, int32_t* group_padded_offsets,
+              int32_t* group_idx_for_bx, int32_t* sorted_pair, int32_t* pair_to_row,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Token permute into the compact expert-major layout (TileOPs "MoePermuteAlignOp":
+ * token routing for the grouped GEMM):
+ *     x_perm[r, :] = hidden[sorted_pair[r] / top_k, :]
+ * hidden [T, H] bf16, x_perm [T*top_k, H] bf16. H % 8 == 0. */
+int moe_permute(const uint16_t* hidden, const int32_t* sorted_pair, int64_t T, int top_k, int H,
+                uint16_t* x_perm, hipStream_t stream);
+
+/* Grouped GEMM for gate+up, C[e] = A[e] @ W[e]^T (TileOPs #1580, "Benchmark
+ * results" and "Grouped-GEMM kernel"): A is the compact [numel, H] layout;
+ * each expert's last, partial row block is masked inside the kernel (rows
+ * past the expert read as zero, stores limited to the valid rows) instead of
+ * padding A. Row blocks are decoded from the tables as in Tutorial Example 07:
+ *     m_start = bx*block_m - group_padded_offsets[g] + group_offsets[g].
+ * w_gate_up [E, 2F, H] bf16: rows 0..F-1 gate, rows F..2F-1 up.
+ * fuse_swiglu = 0: out [numel, 2F] bf16 = bf16(A @ W^T).
+ * fuse_swiglu = 1: out [numel, F] bf16 = bf16(silu(g) * u), g and u the bf16
+ *   roundings of the gate and up products: byte-identical to the unfused
+ *   GEMM followed by swiglu().
+ * Tables are the moe_align outputs for the same (numel, E, padding_m,
+ * block_m). Passing group_sizes = NULL (and the other three tables NULL)
+ * treats A as one dense group of numel rows with E = 1 (the shared expert,
+ * TileOPs #778 "SharedExpertMLPKernel").
+ * Limits: block_m in {64, 128}; H % 64 == 0; F % 64 == 0; numel < 2^31. */
+int grouped_gemm_gate_up(const uint16_t* x_perm, const uint16_t* w_gate_up,
+                         const int32_t* group_sizes, const int32_t* group_offsets,
+                         const int32_t* group_padded_offsets, const int32_t* group_idx_for_bx,
+                         int64_t numel, int E, int H, int F, int padding_m, int block_m,
+                         int fuse_swiglu, uint16_t* out, hipStream_t stream);
+
+/* SwiGLU on the gate|up halves: h[m, f] = bf16(silu(gate[m, f]) * up[m, f])
+ * with gate = gate_up[:, 0:F], up = gate_up[:, F:2F] (TileOPs #778 "SiLU-mul";
+ * xtuner #2089 native_swiglu). silu uses the library's fp32 exp sequence
+ * (moe_common.h). gate_up [M, 2F] bf16, h [M, F] bf16, F % 8 == 0. */
+int swiglu(const uint16_t* gate_up, int64_t M, int F, uint16_t* h, hipStream_t stream);
+
+/* Grouped GEMM for down, y[e] = h[e] @ W_down[e]^T, same masking and table
+ * contract as grouped_gemm_gate_up. h [numel, F] bf16, w_down [E, H, F] bf16,
+ * y [numel, H] bf16. NULL tables: one dense group (shared expert).
+ * Limits: block_m in {64, 128}; F % 64 == 0; H % 128 == 0. */
+int grouped_gemm_down(const uint16_t* h, const uint16_t* w_down, const int32_t* group_sizes,
+                      const int32_t* group_offsets, const int32_t* group_padded_offsets,
+                      const int32_t* group_idx_for_bx, int64_t numel, int E, int H, int F,
+                      int padding_m, int block_m, uint16_t* y, hipStream_t stream);
+
+/* Unpermute: weighted sum over each token's k expert outputs with
+ * routed_scaling_factor applied before the single cast and store (TileOPs
+ * #1580, "Unpermute"), plus an optional addend (the shared expert's output,
+ * TileOPs #778 "Partial output contract") joined before that rounding:
+ *     out[t] = bf16(rsf * sum_j topk_weights[t,j] * y[pair_to_row[t*k+j]] + addend[t])
+ * y [T*top_k, H] bf16, pair_to_row [T*top_k] int32, topk_weights [T, top_k]
+ * float32, addend [T, H] bf16 or NULL, out [T, H] bf16 (may not alias y).
+ * Sum in fp32, j ascending. H % 8 == 0, top_k <= 16. */
+int moe_unpermute(const uint16_t* y, const int32_t* pair_to_row, const float* topk_weights,
+                  int64_t T, int top_k, int H, float routed_scaling_factor,
+                  const uint16_t* addend, uint16_t* out, hipStream_t stream);
+
+/* Fused SwiGLU + FP8 quantizer (xtuner #2089, swiglu_per_tile_quant_with_
+ * trans_per_block): h = swiglu(gate_up) is formed in registers, never stored,
+ * and quantized to OCP e4m3 (max 448) in two layouts in one pass:
+ *   row layout  q_row [M, F] uint8, s_row [M, F/128] float32: per 1x128 tile
+ *               of a row, s = fl32(amax/448), code = e4m3(fl32(h/s));
+ *   transposed  q_t [F, M_pad] uint8, s_t [F/128, M_pad/128] float32 with
+ *               M_pad = ceil(M/128)*128: per 128x128 block (amax over real
+ *               rows), q_t[f, m] = e4m3(fl32(h[m, f]/s)); pad columns 0x00.
+ * Divisions are correctly rounded fp32, e4m3 rounding is nearest-even; a tile
+ * with amax 0 has scale 0 and codes 0x00. The bytes equal swiglu() followed
+ * by the two quantizers. gate_up [M, 2F] bf16; F % 128 == 0; M < 2^31. */
+int swiglu_quant_fp8(const uint16_t* gate_up, int64_t M, int F, uint8_t* q_row, float* s_row,
+                     uint8_t* q_t, float* s_t, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H_ */

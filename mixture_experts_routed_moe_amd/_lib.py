@@ -1,0 +1,228 @@
+"""ctypes binding of libmoe_mi355x.so: argument marshalling only.
+
+Each function takes torch tensors that live on the GPU, checks dtype, shape
+and contiguity, passes raw device pointers and the current HIP stream to the
+C entry point of the same name, and raises MoeError on a non-zero return.
+Every computation happens in the library's HIP kernels; there is no host or
+PyTorch fallback, and importing this module fails if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_HIP = -3
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m mixture_experts_routed_moe_amd.build` "
+            "(the MoE path has no fallback without its HIP library)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_abi_version": (I, []),
+        "moe_num_blocks": (I64, [I64, I, I, I]),
+        "moe_align_workspace_bytes": (SZ, [I64, I]),
+        "moe_topk_softmax": (I, [P, I64, I, I, P, P, P]),
+        "moe_align": (I, [P, I64, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
+        "moe_permute": (I, [P, P, I64, I, I, P, P]),
+        "grouped_gemm_gate_up": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
+        "swiglu": (I, [P, I64, I, P, P]),
+        "grouped_gemm_down": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, P, P]),
+        "moe_unpermute": (I, [P, P, P, I64, I, I, F, P, P, P]),
+        "swiglu_quant_fp8": (I, [P, I64, I, P, P, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_workspace_bytes",
+           "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up", "swiglu",
+           "grouped_gemm_down", "moe_unpermute", "swiglu_quant_fp8")
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    rc = getattr(_lib, name)(*args)
+    if rc != MOE_OK:
+        raise MoeError(name, rc, _lib.moe_last_error().decode(errors="replace"))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: torch.dtype, name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _out(out: Optional[torch.Tensor], shape, dtype, like: torch.Tensor, name: str) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name}: out shape {tuple(out.shape)} != {tuple(shape)}")
+    return out
+
+
+def num_blocks(numel: int, E: int, block_m: int, padding_m: int) -> int:
+    n = _lib.moe_num_blocks(numel, E, block_m, padding_m)
+    if n < 0:
+        raise ValueError("num_blocks: padding_m must be a positive multiple of block_m")
+    return int(n)
+
+
+def align_workspace_bytes(numel: int, E: int) -> int:
+    return int(_lib.moe_align_workspace_bytes(numel, E))
+
+
+# ----------------------------------------------------------------- entries --
+
+def moe_topk_softmax(logits: torch.Tensor, top_k: int, topk_ids=None, topk_weights=None):
+    T, E = logits.shape
+    ids = _out(topk_ids, (T, top_k), torch.int32, logits, "topk_ids")
+    w = _out(topk_weights, (T, top_k), torch.float32, logits, "topk_weights")
+    _call("moe_topk_softmax", _ptr(logits, torch.float32, "logits"), T, E, top_k,
+          _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_weights"), _stream(logits))
+    return ids, w
+
+
+def alloc_tables(numel: int, E: int, padding_m: int, block_m: int, device) -> Dict[str, torch.Tensor]:
+    mb = num_blocks(numel, E, block_m, padding_m)
+    i32 = dict(dtype=torch.int32, device=device)
+    return {
+        "group_sizes": torch.empty(E, **i32), "group_offsets": torch.empty(E, **i32),
+        "group_padded_offsets": torch.empty(E, **i32), "group_idx_for_bx": torch.empty(mb, **i32),
+        "sorted_pair": torch.empty(numel, **i32), "pair_to_row": torch.empty(numel, **i32),
+        "workspace": torch.empty(max(1, align_workspace_bytes(numel, E)), dtype=torch.uint8, device=device),
+    }
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, padding_m: int, block_m: int,
+              tables: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    T, k = topk_ids.shape
+    tb = tables if tables is not None else alloc_tables(T * k, E, padding_m, block_m, topk_ids.device)
+    i32 = torch.int32
+    ws = tb["workspace"]
+    _call("moe_align", _ptr(topk_ids, i32, "topk_ids"), T, k, E, padding_m, block_m,
+          _ptr(tb["group_sizes"], i32, "group_sizes"), _ptr(tb["group_offsets"], i32, "group_offsets"),
+          _ptr(tb["group_padded_offsets"], i32, "group_padded_offsets"),
+          _ptr(tb["group_idx_for_bx"], i32, "group_idx_for_bx"), _ptr(tb["sorted_pair"], i32, "sorted_pair"),
+          _ptr(tb["pair_to_row"], i32, "pair_to_row"), ws.data_ptr(), ws.numel(), _stream(topk_ids))
+    return tb
+
+
+def moe_permute(hidden: torch.Tensor, sorted_pair: torch.Tensor, top_k: int, out=None) -> torch.Tensor:
+    T, H = hidden.shape
+    x = _out(out, (T * top_k, H), torch.bfloat16, hidden, "x_perm")
+    _call("moe_permute", _ptr(hidden, torch.bfloat16, "hidden"), _ptr(sorted_pair, torch.int32, "sorted_pair"),
+          T, top_k, H, _ptr(x, torch.bfloat16, "x_perm"), _stream(hidden))
+    return x
+
+
+def _table_ptrs(tables):
+    if tables is None:
+        return None, None, None, None
+    i32 = torch.int32
+    return (_ptr(tables["group_sizes"], i32, "group_sizes"), _ptr(tables["group_offsets"], i32, "group_offsets"),
+            _ptr(tables["group_padded_offsets"], i32, "group_padded_offsets"),
+            _ptr(tables["group_idx_for_bx"], i32, "group_idx_for_bx"))
+
+
+def grouped_gemm_gate_up(x_perm: torch.Tensor, w_gate_up: torch.Tensor, tables: Optional[Dict[str, torch.Tensor]],
+                         padding_m: int, block_m: int, fuse_swiglu: bool = True, out=None) -> torch.Tensor:
+    """tables=None: dense single group (w_gate_up [2F, H] or [1, 2F, H])."""
+    if w_gate_up.dim() == 2:
+        w_gate_up = w_gate_up.unsqueeze(0)
+    E, twoF, H = w_gate_up.shape
+    F = twoF // 2
+    numel = x_perm.shape[0]
+    if x_perm.shape[1] != H:
+        raise ValueError("grouped_gemm_gate_up: x_perm width != H")
+    o = _out(out, (numel, F if fuse_swiglu else 2 * F), torch.bfloat16, x_perm, "out")
+    _call("grouped_gemm_gate_up", _ptr(x_perm, torch.bfloat16, "x_perm"), _ptr(w_gate_up, torch.bfloat16, "w_gate_up"),
+          *_table_ptrs(tables), numel, E, H, F, padding_m, block_m, int(bool(fuse_swiglu)),
+          _ptr(o, torch.bfloat16, "out"), _stream(x_perm))
+    return o
+
+
+def swiglu(gate_up: torch.Tensor, out=None) -> torch.Tensor:
+    M, twoF = gate_up.shape
+    h = _out(out, (M, twoF // 2), torch.bfloat16, gate_up, "h")
+    _call("swiglu", _ptr(gate_up, torch.bfloat16, "gate_up"), M, twoF // 2, _ptr(h, torch.bfloat16, "h"),
+          _stream(gate_up))
+    return h
+
+
+def grouped_gemm_down(h: torch.Tensor, w_down: torch.Tensor, tables: Optional[Dict[str, torch.Tensor]],
+                      padding_m: int, block_m: int, out=None) -> torch.Tensor:
+    if w_down.dim() == 2:
+        w_down = w_down.unsqueeze(0)
+    E, H, F = w_down.shape
+    numel = h.shape[0]
+    if h.shape[1] != F:
+        raise ValueError("grouped_gemm_down: h width != F")
+    y = _out(out, (numel, H), torch.bfloat16, h, "y")
+    _call("grouped_gemm_down", _ptr(h, torch.bfloat16, "h"), _ptr(w_down, torch.bfloat16, "w_down"),
+          *_table_ptrs(tables), numel, E, H, F, padding_m, block_m, _ptr(y, torch.bfloat16, "y"), _stream(h))
+    return y
+
+
+def moe_unpermute(y: torch.Tensor, pair_to_row: torch.Tensor, topk_weights: torch.Tensor,
+                  routed_scaling_factor: float = 1.0, addend: Optional[torch.Tensor] = None,
+                  out=None) -> torch.Tensor:
+    T, k = topk_weights.shape
+    H = y.shape[1]
+    o = _out(out, (T, H), torch.bfloat16, y, "out")
+    _call("moe_unpermute", _ptr(y, torch.bfloat16, "y"), _ptr(pair_to_row, torch.int32, "pair_to_row"),
+          _ptr(topk_weights, torch.float32, "topk_weights"), T, k, H, float(routed_scaling_factor),
+          _ptr(addend, torch.bfloat16, "addend"), _ptr(o, torch.bfloat16, "out"), _stream(y))
+    return o
+
+
+def swiglu_quant_fp8(gate_up: torch.Tensor, out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    M, twoF = gate_up.shape
+    F = twoF // 2
+    m_pad = -(-M // 128) * 128
+    o = out or {}
+    q_row = _out(o.get("q_row"), (M, F), torch.uint8, gate_up, "q_row")
+    s_row = _out(o.get("s_row"), (M, F // 128), torch.float32, gate_up, "s_row")
+    q_t = _out(o.get("q_t"), (F, m_pad), torch.uint8, gate_up, "q_t")
+    s_t = _out(o.get("s_t"), (F // 128, m_pad // 128), torch.float32, gate_up, "s_t")
+    _call("swiglu_quant_fp8", _ptr(gate_up, torch.bfloat16, "gate_up"), M, F, _ptr(q_row, torch.uint8, "q_row"),
+          _ptr(s_row, torch.float32, "s_row"), _ptr(q_t, torch.uint8, "q_t"), _ptr(s_t, torch.float32, "s_t"),
+          _stream(gate_up))
+    return {"q_row": q_row, "s_row": s_row, "q_t": q_t, "s_t": s_t}

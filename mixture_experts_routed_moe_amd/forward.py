@@ -1,0 +1,112 @@
+"""The routed-expert MoE forward as a sequence of library calls.
+
+Stage order follows the TileOPs routed pipeline (#1580, "Grouped-GEMM
+kernel" and "Unpermute"; #778, "Partial output contract" for the shared
+expert): routing, dispatch tables, permute, gate_up GEMM (+ SwiGLU), down
+GEMM, unpermute with the routing weights and routed_scaling_factor folded in
+before the store. The shared expert, when given, runs the same two GEMMs on
+all tokens as one dense group and joins the unpermute as its addend.
+
+`MoEBuffers` holds every intermediate for one problem size so a forward
+allocates nothing; all work is enqueued on the current stream without a host
+synchronisation.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+
+
+@dataclasses.dataclass
+class MoEShape:
+    T: int
+    H: int
+    F: int
+    E: int
+    top_k: int
+    padding_m: int = 128
+    block_m: int = 128
+    shared_F: int = 0
+
+    @property
+    def numel(self) -> int:
+        return self.T * self.top_k
+
+
+class MoEBuffers:
+    """Device buffers for every intermediate of one forward of `shape`."""
+
+    def __init__(self, shape: MoEShape, device, fuse_swiglu: bool = True):
+        s = shape
+        self.shape = s
+        self.fuse_swiglu = fuse_swiglu
+        bf16 = dict(dtype=torch.bfloat16, device=device)
+        self.topk_ids = torch.empty(s.T, s.top_k, dtype=torch.int32, device=device)
+        self.topk_weights = torch.empty(s.T, s.top_k, dtype=torch.float32, device=device)
+        self.tables = _lib.alloc_tables(s.numel, s.E, s.padding_m, s.block_m, device)
+        self.x_perm = torch.empty(s.numel, s.H, **bf16)
+        self.gate_up = None if fuse_swiglu else torch.empty(s.numel, 2 * s.F, **bf16)
+        self.h = torch.empty(s.numel, s.F, **bf16)
+        self.y = torch.empty(s.numel, s.H, **bf16)
+        self.out = torch.empty(s.T, s.H, **bf16)
+        if s.shared_F:
+            self.shared_gate_up = None if fuse_swiglu else torch.empty(s.T, 2 * s.shared_F, **bf16)
+            self.shared_h = torch.empty(s.T, s.shared_F, **bf16)
+            self.shared_y = torch.empty(s.T, s.H, **bf16)
+
+
+def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate_up: torch.Tensor,
+                       w_down: torch.Tensor, top_k: int, routed_scaling_factor: float = 1.0,
+                       padding_m: int = 128, block_m: int = 128,
+                       shared_w_gate_up: Optional[torch.Tensor] = None,
+                       shared_w_down: Optional[torch.Tensor] = None,
+                       fuse_swiglu: bool = True, buffers: Optional[MoEBuffers] = None) -> torch.Tensor:
+    """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden))."""
+    T, H = hidden.shape
+    E, twoF, H2 = w_gate_up.shape
+    F = twoF // 2
+    if H2 != H or tuple(w_down.shape) != (E, H, F) or tuple(router_logits.shape) != (T, E):
+        raise ValueError("routed_moe_forward: inconsistent shapes")
+    shared_F = 0 if shared_w_down is None else shared_w_down.shape[1]
+    shape = MoEShape(T, H, F, E, top_k, padding_m, block_m, shared_F)
+    b = buffers
+    if b is None:
+        b = MoEBuffers(shape, hidden.device, fuse_swiglu)
+    elif dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu:
+        raise ValueError("routed_moe_forward: buffers were made for another shape")
+
+    _lib.moe_topk_softmax(router_logits, top_k, b.topk_ids, b.topk_weights)
+    tb = _lib.moe_align(b.topk_ids, E, padding_m, block_m, b.tables)
+    _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm)
+    if fuse_swiglu:
+        _lib.grouped_gemm_gate_up(b.x_perm, w_gate_up, tb, padding_m, block_m, True, b.h)
+    else:
+        _lib.grouped_gemm_gate_up(b.x_perm, w_gate_up, tb, padding_m, block_m, False, b.gate_up)
+        _lib.swiglu(b.gate_up, b.h)
+    _lib.grouped_gemm_down(b.h, w_down, tb, padding_m, block_m, b.y)
+    addend = None
+    if shared_F:
+        if fuse_swiglu:
+            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, True, b.shared_h)
+        else:
+            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, False, b.shared_gate_up)
+            _lib.swiglu(b.shared_gate_up, b.shared_h)
+        _lib.grouped_gemm_down(b.shared_h, shared_w_down, None, padding_m, block_m, b.shared_y)
+        addend = b.shared_y
+    _lib.moe_unpermute(b.y, tb["pair_to_row"], b.topk_weights, routed_scaling_factor, addend, b.out)
+    return b.out
+
+
+def intermediates(b: MoEBuffers) -> Dict[str, torch.Tensor]:
+    d = {"topk_ids": b.topk_ids, "topk_weights": b.topk_weights, "x_perm": b.x_perm, "h": b.h, "y": b.y,
+         "out": b.out}
+    d.update({k: v for k, v in b.tables.items() if k != "workspace"})
+    if b.gate_up is not None:
+        d["gate_up"] = b.gate_up
+    if b.shape.shared_F:
+        d["shared"] = b.shared_y
+    return d

@@ -1,0 +1,347 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, stage by stage
+and end to end. Every stage is fed the same inputs on both sides; integer
+tables, permutations and FP8 bytes must match exactly, bf16 results within
+atol = rtol = 1e-2, routing weights within 2e-6 relative.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from oracle import numerics as nm
+from gpu_util import (assert_bf16_close, bits, dev, host, inputs, oracle_tokens, say)
+
+pytestmark = pytest.mark.gpu
+
+mx = pytest.importorskip("mixture_experts_routed_moe_amd")
+
+MID = moe_synth.MoEConfig(80, "mid", T=300, H=256, F=384, E=6, top_k=2, padding_m=128, block_m=128)
+MID64 = moe_synth.MoEConfig(81, "mid64", T=300, H=256, F=384, E=6, top_k=2, padding_m=128, block_m=64)
+
+
+def _t(a, d, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(d)
+
+
+def _bf16_dev(bits_np, d):
+    return torch.from_numpy(np.ascontiguousarray(bits_np).view(np.int16)).view(torch.bfloat16).to(d)
+
+
+# ---------------------------------------------------------------- inputs --
+
+def test_generator_same_bits_on_gpu():
+    d = dev()
+    key = moe_synth.tensor_key(3, 4)
+    a = moe_synth.normal_bf16(key, (5000,), 0.02, "cpu", start=123456)
+    b = moe_synth.normal_bf16(key, (5000,), 0.02, d, start=123456)
+    assert torch.equal(a, b.cpu())
+    cfg = moe_synth.CONFIGS["qwen3_decode"]
+    assert torch.equal(moe_synth.router_logits(cfg, "cpu", rows=slice(7, 11)),
+                       moe_synth.router_logits(cfg, d, rows=slice(7, 11)).cpu())
+
+
+# --------------------------------------------------------------- routing --
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"])
+def test_route(name):
+    d = dev()
+    cfg = moe_synth.CONFIGS[name]
+    say("route", name)
+    logits = moe_synth.router_logits(cfg, d)
+    ids, w = mx.moe_topk_softmax(logits, cfg.top_k)
+    rid, rw = oracle.route(host(logits), cfg.top_k)
+    assert np.array_equal(host(ids), rid)
+    np.testing.assert_allclose(host(w), rw, rtol=2e-6, atol=1e-7)
+
+
+def test_route_ties_and_small_shapes():
+    d = dev()
+    rng = np.random.default_rng(3)
+    for T, E, k in [(37, 8, 2), (5, 3, 3), (64, 1024, 16), (9, 65, 7), (1, 1, 1)]:
+        logits = rng.integers(-3, 3, size=(T, E)).astype(np.float32) * np.float32(0.5)
+        ids, w = mx.moe_topk_softmax(_t(logits, d), k)
+        rid, rw = oracle.route(logits, k)
+        assert np.array_equal(host(ids), rid), (T, E, k)
+        np.testing.assert_allclose(host(w), rw, rtol=2e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------ dispatch --
+
+def _align_cases(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "dispatch_worked_example.json")))
+    p = g["params"]
+    yield "worked", np.array(g["topk_ids"], np.int32), p["experts"], p["padding_m"], p["block_token"]
+    rng = np.random.default_rng(0)
+    yield "empty", np.zeros((0, 2), np.int32), 4, 64, 64
+    yield "one_expert", np.full((300, 1), 5, np.int32), 8, 128, 128
+    yield "exact_multiples", np.repeat(np.arange(4, dtype=np.int32), 64).reshape(-1, 2), 4, 64, 64
+    yield "pad128_block64", np.stack([rng.permutation(16)[:4] for _ in range(777)]).astype(np.int32), 16, 128, 64
+    yield "E1", np.zeros((50, 1), np.int32), 1, 16, 16
+    yield "E1000", np.stack([rng.permutation(1000)[:8] for _ in range(2100)]).astype(np.int32), 1000, 32, 32
+    for name in ("tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"):
+        cfg = moe_synth.CONFIGS[name]
+        ids, _ = oracle.route(moe_synth.router_logits(cfg).numpy(), cfg.top_k)
+        yield name, ids, cfg.E, cfg.padding_m, cfg.block_m
+
+
+def test_align_tables_bit_exact(golden_dir):
+    d = dev()
+    for name, ids, E, pm, bm in _align_cases(golden_dir):
+        say("align", name, ids.shape, E, pm, bm)
+        tb = mx.moe_align(_t(ids, d), E, pm, bm)
+        ref = oracle.dispatch_tables(ids, E, pm, bm)
+        for key in ("group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx",
+                    "sorted_pair", "pair_to_row"):
+            assert np.array_equal(host(tb[key]), ref[key]), (name, key)
+        assert tb["group_idx_for_bx"].numel() == ref["m_blocks"]
+
+
+def test_align_deterministic():
+    d = dev()
+    cfg = moe_synth.CONFIGS["dsv3_prefill"]
+    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k)
+    a = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
+    b = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
+    for key in ("sorted_pair", "pair_to_row", "group_idx_for_bx"):
+        assert torch.equal(a[key], b[key])
+
+
+# ------------------------------------------------------------- permute --
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_prefill", "dsv3_prefill"])
+def test_permute(name):
+    d = dev()
+    cfg = moe_synth.CONFIGS[name]
+    hid = moe_synth.hidden(cfg, d)
+    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k)
+    tb = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
+    xp = mx.moe_permute(hid, tb["sorted_pair"], cfg.top_k)
+    ref = oracle.permute(bits(hid), host(tb["sorted_pair"]), cfg.top_k)
+    assert np.array_equal(bits(xp), ref)
+
+
+# ---------------------------------------------------------------- GEMMs --
+
+def _gemm_setup(cfg, d):
+    hid = moe_synth.hidden(cfg, d)
+    ids, w = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k)
+    tb = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
+    xp = mx.moe_permute(hid, tb["sorted_pair"], cfg.top_k)
+    return xp, tb, ids, w
+
+
+@pytest.mark.parametrize("cfg", [moe_synth.CONFIGS["tiny"], MID, MID64], ids=["tiny", "mid", "mid64"])
+def test_grouped_gemm_gate_up_and_down(cfg):
+    d = dev()
+    say("gemm", cfg.name)
+    xp, tb, _, _ = _gemm_setup(cfg, d)
+    wgu = moe_synth.w_gate_up(cfg, d)
+    wd = moe_synth.w_down(cfg, d)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    assert (gs % cfg.block_m != 0).any()        # ragged tails exercised
+    gu = mx.grouped_gemm_gate_up(xp, wgu, tb, cfg.padding_m, cfg.block_m, fuse_swiglu=False)
+    ref_gu = oracle.grouped_gemm(bits(xp), bits(wgu), gs, go)
+    err = assert_bf16_close(bits(gu), ref_gu, "gate_up")
+    say("  gate_up max abs err", err)
+    # fused epilogue == unfused GEMM + SwiGLU, byte for byte, and == the oracle's SwiGLU of it
+    h = mx.grouped_gemm_gate_up(xp, wgu, tb, cfg.padding_m, cfg.block_m, fuse_swiglu=True)
+    assert torch.equal(h, mx.swiglu(gu))
+    assert np.array_equal(bits(h), oracle.swiglu(bits(gu), cfg.F))
+    y = mx.grouped_gemm_down(h, wd, tb, cfg.padding_m, cfg.block_m)
+    ref_y = oracle.grouped_gemm(bits(h), bits(wd), gs, go)
+    err = assert_bf16_close(bits(y), ref_y, "down")
+    say("  down max abs err", err)
+
+
+@pytest.mark.parametrize("numel,bm", [(1, 64), (200, 128), (333, 64), (4096, 128)])
+def test_dense_group_gemm(numel, bm):
+    d = dev()
+    H, F = 256, 192
+    key = moe_synth.tensor_key(70, numel)
+    x = moe_synth.normal_bf16(key, (numel, H), 1.0, d)
+    wgu = moe_synth.normal_bf16(key + 1, (2 * F, H), H ** -0.5, d)
+    wd = moe_synth.normal_bf16(key + 2, (H, F), F ** -0.5, d)
+    gu = mx.grouped_gemm_gate_up(x, wgu, None, bm, bm, fuse_swiglu=False)
+    one, zero = np.array([numel], np.int32), np.array([0], np.int32)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(wgu)[None], one, zero), "dense gate_up")
+    h = mx.grouped_gemm_gate_up(x, wgu, None, bm, bm, fuse_swiglu=True)
+    assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
+    y = mx.grouped_gemm_down(h, wd, None, bm, bm)
+    assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd)[None], one, zero), "dense down")
+
+
+# --------------------------------------------------------------- swiglu --
+
+def test_swiglu_bit_exact_including_extremes():
+    d = dev()
+    M, F = 257, 256
+    x = bits(moe_synth.normal_bf16(moe_synth.tensor_key(71), (M, 2 * F), 3.0, "cpu"))
+    specials = nm.to_bf16(np.array([0.0, -0.0, 1e-30, -1e-30, 20.0, -20.0, 90.0, -90.0, 1e30, -1e30,
+                                    1e-38, 2.0 ** -133, 87.0, -87.0, 0.5, -0.5]))
+    x[0, :len(specials)] = specials
+    x[1, F:F + len(specials)] = specials
+    x[2, :len(specials)] = specials[::-1]
+    x[2, F:F + len(specials)] = specials
+    h = mx.swiglu(_bf16_dev(x, d))
+    assert np.array_equal(bits(h), oracle.swiglu(x, F))
+
+
+# ------------------------------------------------------------- unpermute --
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_decode"])
+def test_unpermute_and_linearity(name):
+    d = dev()
+    cfg = moe_synth.CONFIGS[name]
+    T, k, H = cfg.T, cfg.top_k, cfg.H
+    y = moe_synth.normal_bf16(moe_synth.tensor_key(72, cfg.cid), (T * k, H), 0.5, d)
+    ids, w = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), k)
+    tb = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
+    add = moe_synth.normal_bf16(moe_synth.tensor_key(73, cfg.cid), (T, H), 0.5, d)
+    p2r = host(tb["pair_to_row"])
+    for rsf in (1.0, 2.827):
+        o = mx.moe_unpermute(y, tb["pair_to_row"], w, rsf)
+        assert_bf16_close(bits(o), oracle.unpermute(bits(y), p2r, host(w), k, rsf), f"unpermute rsf={rsf}")
+        o = mx.moe_unpermute(y, tb["pair_to_row"], w, rsf, addend=add)
+        assert_bf16_close(bits(o), oracle.unpermute(bits(y), p2r, host(w), k, rsf, bits(add)), "unpermute+addend")
+    o1 = nm.bf16_to_f64(bits(mx.moe_unpermute(y, tb["pair_to_row"], w, 1.0)))
+    for rsf in (2.0, 0.5):
+        o = nm.bf16_to_f64(bits(mx.moe_unpermute(y, tb["pair_to_row"], w, rsf)))
+        assert np.array_equal(o, rsf * o1)
+
+
+# -------------------------------------------------------------- quantizer --
+
+def _quant_compare(x_bits, F, q, rows=None):
+    ref = oracle.swiglu_quant_fp8(x_bits, F)
+    M = x_bits.shape[0]
+    if rows is None:
+        assert np.array_equal(host(q["q_row"]), ref["q_row"])
+        assert np.array_equal(host(q["s_row"]).view(np.uint32), ref["s_row"].view(np.uint32))
+        assert np.array_equal(host(q["q_t"]), ref["q_t"])
+        assert np.array_equal(host(q["s_t"]).view(np.uint32), ref["s_t"].view(np.uint32))
+    else:
+        r0, r1 = rows
+        mb = r0 // 128
+        assert np.array_equal(host(q["q_row"][r0:r1]), ref["q_row"])
+        assert np.array_equal(host(q["s_row"][r0:r1]).view(np.uint32), ref["s_row"].view(np.uint32))
+        assert np.array_equal(host(q["q_t"][:, r0:r0 + ref["q_t"].shape[1]]), ref["q_t"])
+        assert np.array_equal(host(q["s_t"][:, mb:mb + ref["s_t"].shape[1]]).view(np.uint32),
+                              ref["s_t"].view(np.uint32))
+    return M
+
+
+@pytest.mark.parametrize("M", moe_synth.QUANT_EDGE_M)
+def test_swiglu_quant_edge_sizes(M):
+    d = dev()
+    F = moe_synth.QUANT_CONFIG.F
+    x = moe_synth.quant_input(M, F, d)
+    q = mx.swiglu_quant_fp8(x)
+    assert q["q_t"].shape == (F, -(-M // 128) * 128)
+    if M:
+        _quant_compare(bits(x), F, q)
+
+
+def test_swiglu_quant_matches_unfused_pair():
+    d = dev()
+    M, F = 300, 512
+    x = moe_synth.quant_input(M, F, d)
+    q = mx.swiglu_quant_fp8(x)
+    h = bits(mx.swiglu(x))
+    ref = oracle.quant_fp8(h)
+    for key in ("q_row", "s_row", "q_t", "s_t"):
+        assert np.array_equal(host(q[key]).view(np.uint8), ref[key].view(np.uint8)), key
+
+
+def test_swiglu_quant_every_bf16_code():
+    """gate = 64 makes silu(gate) exactly 64, up = v/64 makes h = v for every bf16 v in [-448, 448];
+    448 in each row pins the row scale to 1, so the codes are the plain e4m3 encodings."""
+    d = dev()
+    f = nm.bf16_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    vals = f[np.isfinite(f) & (np.abs(f) <= 448.0) & ((np.abs(f) >= 2.0 ** -100) | (f == 0))]
+    per = 127
+    n_rows = -(-vals.size // per)
+    F = 128
+    h = np.zeros((n_rows, F), np.float64)
+    h[:, 0] = 448.0
+    flat = np.zeros(n_rows * per)
+    flat[:vals.size] = vals
+    h[:, 1:] = flat.reshape(n_rows, per)
+    gate = np.full((n_rows, F), 64.0)
+    x = np.concatenate([nm.to_bf16(gate), nm.to_bf16(h / 64.0)], axis=1)
+    assert np.array_equal(nm.bf16_to_f64(x[:, F:]) * 64.0, h)   # exact construction
+    q = mx.swiglu_quant_fp8(_bf16_dev(x, d))
+    assert np.all(host(q["s_row"]) == 1.0)
+    assert np.array_equal(host(q["q_row"]), nm.e4m3_encode(h))
+    _quant_compare(x, F, q)
+
+
+def test_swiglu_quant_full_size_sampled_blocks():
+    d = dev()
+    M, F = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
+    x = moe_synth.quant_input(M, F, d)
+    q = mx.swiglu_quant_fp8(x)
+    for r0 in (0, 128 * 97, M - 128):
+        _quant_compare(bits(x[r0:r0 + 128]), F, q, rows=(r0, r0 + 128))
+
+
+# ----------------------------------------------------------- end to end --
+
+def _gpu_forward(cfg, inp, fuse=True):
+    return mx.routed_moe_forward(inp["hidden"], inp["logits"], inp["w_gate_up"], inp["w_down"], cfg.top_k,
+                                 cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"),
+                                 inp.get("shared_w_down"), fuse_swiglu=fuse)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_decode"])
+def test_forward_full_oracle(name):
+    d = dev()
+    cfg = moe_synth.CONFIGS[name]
+    say("forward", name)
+    inp = inputs(cfg, d)
+    ref = oracle.forward(bits(inp["hidden"]), host(inp["logits"]), bits(inp["w_gate_up"]), bits(inp["w_down"]),
+                         cfg.top_k, cfg.rsf, cfg.padding_m, cfg.block_m)
+    for fuse in (True, False):
+        out = _gpu_forward(cfg, inp, fuse)
+        err = assert_bf16_close(bits(out), ref["out"], f"{name} out fuse={fuse}")
+        say("  out max abs err", err, "fuse", fuse)
+
+
+@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_prefill"])
+def test_forward_full_size_sampled_tokens(name):
+    d = dev()
+    cfg = moe_synth.CONFIGS[name]
+    say("forward", name, "generating inputs")
+    inp = inputs(cfg, d)
+    bufs = mx.MoEBuffers(mx.MoEShape(cfg.T, cfg.H, cfg.F, cfg.E, cfg.top_k, cfg.padding_m, cfg.block_m,
+                                     cfg.shared_F), d)
+    out = mx.routed_moe_forward(inp["hidden"], inp["logits"], inp["w_gate_up"], inp["w_down"], cfg.top_k,
+                                cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"),
+                                inp.get("shared_w_down"), buffers=bufs)
+    torch.cuda.synchronize()
+    # full-size tables against the oracle's
+    ids = host(bufs.topk_ids)
+    ref_ids, _ = oracle.route(host(inp["logits"]), cfg.top_k)
+    assert np.array_equal(ids, ref_ids)
+    ref_tab = oracle.dispatch_tables(ref_ids, cfg.E, cfg.padding_m, cfg.block_m)
+    for key in ("group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx", "sorted_pair",
+                "pair_to_row"):
+        assert np.array_equal(host(bufs.tables[key]), ref_tab[key]), key
+    say("  active experts", int((ref_tab["group_sizes"] > 0).sum()), "max rows", int(ref_tab["group_sizes"].max()))
+    tokens = np.unique(np.concatenate([[0, 1, cfg.T - 1], np.random.default_rng(cfg.cid).choice(cfg.T, 21)]))
+    ref = oracle_tokens(cfg, inp, tokens)
+    err = assert_bf16_close(bits(out[torch.as_tensor(tokens, device=d)]), ref["out"], f"{name} sampled out")
+    say("  sampled out max abs err", err)
+    if cfg.shared_F:
+        assert_bf16_close(bits(bufs.shared_y[torch.as_tensor(tokens, device=d)]), ref["shared"], "shared")
+    # determinism: a second forward gives the same bytes
+    out2 = mx.routed_moe_forward(inp["hidden"], inp["logits"], inp["w_gate_up"], inp["w_down"], cfg.top_k,
+                                 cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"),
+                                 inp.get("shared_w_down"))
+    assert torch.equal(out, out2)
