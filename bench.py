@@ -188,10 +188,11 @@ def main():
                                    "hbm_frac": round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBS, 4)}
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # a plain streaming kernel of known size: reads 1 GiB, writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -207,6 +208,7 @@ def main():
     else:
         roofline.update(achieved=round(flop_gate_up / gu_s / 1e12, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+    roofline["traffic"] = measured_traffic(cfg.name, fuse)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -230,6 +232,22 @@ def main():
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(workload, fused):
+    """HBM bytes per launch of the routed gate_up GEMM from the committed rocprofv3
+    FETCH_SIZE + WRITE_SIZE summary (scaled by the copy calibration), or None when
+    that summary is for another workload or another revision of the kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm_gate_up_{workload}.txt")
+    src = os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", "gemm.hip")
+    if not fused or not os.path.exists(path):
+        return None
+    kv = dict(line.split("=", 1) for line in open(path).read().splitlines() if "=" in line and not line.startswith("#"))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha256_16") != sha:
+        return None
+    return int(float(kv["traffic_bytes"]))
 
 
 def cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, n_tokens):

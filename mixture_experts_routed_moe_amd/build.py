@@ -38,7 +38,7 @@ def sources():
 
 
 def compile_flags():
-    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    return ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=fast-honor-pragmas",
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
