@@ -4,30 +4,31 @@
 // The row block is decoded from the dispatch tables (row recovery of the
 // tutorial's contract); blocks past an expert's rows, or past the last
 // expert, have no rows and return at once. A is the compact [numel, K]
-// layout: rows past the block's valid count are loaded as zero and never
-// stored, so an expert's last, partial tile needs no padding copy.
+// layout: rows past the block's valid count are never stored, so an expert's
+// last, partial tile needs no padding copy.
 //
-// Tile: BM x 128 outputs, K step 64, four wave64s in a 2x2 arrangement; each
-// wave accumulates (BM/2) x 64 with v_mfma_f32_32x32x16_bf16. A and W tiles
-// are K-contiguous in LDS, 128 bytes per row, with the eight 16-byte chunks
-// of row r stored at chunk position c ^ g(r) (see row_xor) so the
-// fragment reads are free of LDS bank conflicts. Global loads
-// of the next K step are issued into registers before the MFMAs of the
-// current step (LDS double buffer, one barrier per step).
+// Two kernels:
+//  * grouped_gemm_pipe_kernel, 128-row blocks (the production path): a
+//    128 x 256 tile fed by direct-to-LDS loads through a multi-stage ring, see
+//    the comment above it;
+//  * grouped_gemm_kernel, any block_m in {64, 128} and narrow outputs: a
+//    simpler register-staged double buffer, 128 x 128 tile, four wave64s in a
+//    2x2 arrangement each accumulating (BM/2) x 64 with
+//    v_mfma_f32_32x32x16_bf16. A and W tiles are K-contiguous in LDS, 128
+//    bytes per row, with the eight 16-byte chunks of row r stored at chunk
+//    position c ^ g(r) (see row_xor) so the fragment reads are free of LDS bank
+//    conflicts.
 //
-// Fused SwiGLU: the 128 W rows of a tile are 64 gate rows and the 64 up rows
-// F positions further; wave column wn holds gate columns wn*32..+32 and the
-// matching up columns in two accumulators, so the epilogue pairs them in
-// registers: h = bf16(silu(bf16(g)) * bf16(u)).
-#include <utility>
-
+// Fused SwiGLU: the W rows of a tile are gate rows and the matching up rows F
+// positions further; each wave holds gate columns and the matching up columns
+// in separate accumulators, so the epilogue pairs them in registers:
+// h = bf16(silu(bf16(g)) * bf16(u)).
 #include "moe_common.h"
 
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;
 constexpr int kBN = 128;
@@ -200,36 +201,39 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
 // Pipelined kernel for 128-row blocks: 128 x 256 tile (256 W rows: for the
 // fused gate_up, 128 gate rows and the matching 128 up rows, i.e. 128 output
 // columns), K step BK, a ring of STAGES LDS stages filled by direct-to-LDS
-// 16-byte loads (global_load_lds_dwordx4) issued STAGES-1 steps ahead, so no
-// VGPRs are spent staging the next tiles. One workgroup per CU (up to 144 KiB
-// of LDS), four waves in a 2x2 arrangement, each accumulating 64 x 128 in
-// AGPRs with v_mfma_f32_32x32x16_bf16 (8 accumulator tiles: 6 KiB of LDS
-// reads per 8 MFMAs).
+// 16-byte loads (global_load_lds_dwordx4), so no VGPRs are spent staging
+// tiles. Four waves in a 2x2 arrangement each accumulate 64 x 128 with
+// v_mfma_f32_32x32x16_bf16 (8 accumulator tiles: 6 fragment reads per 8
+// MFMAs). What bounds it is the rate at which bytes reach the CU, not the
+// MFMAs (without its global loads the same kernel runs above 2 PFLOP/s), so:
+//  * the loads of step kt+STAGES-1 are issued in pieces after each sub-step's
+//    MFMAs, never as one burst that would block MFMA issue;
+//  * fragments are double-buffered across the 16-wide sub-steps (the LDS
+//    reads of sub-step s+1 are in flight during sub-step s's MFMAs);
+//  * one barrier per K step, which both publishes the new stage and frees the
+//    slot read in the previous step.
 //
 // A direct-to-LDS load writes lane i's 16 bytes at (wave-uniform base + 16*i),
 // so the XOR swizzle is applied on the global side: the lane that fills LDS
 // chunk position p of row r fetches global chunk p ^ f(r), where f spreads
 // the rows read together by a ds_read_b128 over distinct banks
-// (see row_swz). Rows of A
-// past the block's valid count are fetched from the last valid row (in
-// bounds); they only feed output rows that are never stored.
+// (see row_swz). Rows of A past the block's valid count are fetched from the
+// last valid row (in bounds); they only feed output rows that are never
+// stored.
 //
 // Tile order: the hardware hands workgroup w to XCD w % 8. Logical tiles are
-// grouped GM row blocks x GN column tiles (about one tile per CU of an XCD)
-// and group g runs on XCD g % 8, so tiles that share A rows or W columns run
-// together behind one L2. Consecutive groups go to different XCDs, which
-// keeps the active (non-empty) blocks spread over all eight.
-#ifndef MOE_GEMM_KERNEL
-#define MOE_GEMM_KERNEL 1
-#endif
+// grouped GM row blocks x GN column tiles and group g runs on XCD g % 8, so
+// tiles that share A rows or W columns run together behind one L2.
+// Consecutive groups go to different XCDs, which keeps the active (non-empty)
+// blocks spread over all eight.
 #ifndef MOE_PIPE_BK
-#define MOE_PIPE_BK 32
+#define MOE_PIPE_BK 64
 #endif
 #ifndef MOE_PIPE_STAGES
 #define MOE_PIPE_STAGES 3
 #endif
 #ifndef MOE_PIPE_OCC
-#define MOE_PIPE_OCC 2
+#define MOE_PIPE_OCC 1
 #endif
 #ifndef MOE_PIPE_GROUP
 #define MOE_PIPE_GROUP 16
@@ -267,8 +271,6 @@ __device__ __forceinline__ void wait_dma_barrier_dyn(int stages_left) {
     else wait_dma_barrier_dyn<L, S - 1>(stages_left);
   }
 }
-
-__device__ __forceinline__ void release_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Chunk-position XOR for an LDS row of CPR 16-byte chunks: conflict-free
 // ds_read_b128 of 32 consecutive rows in 8- and in 16-lane phases.
@@ -384,6 +386,24 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue(s, 0, L);
+
+  // fragments of one 16-wide sub-step, double-buffered: the LDS reads of
+  // sub-step s+1 are issued before the MFMAs of sub-step s, so the MFMA pipe
+  // does not sit idle for an LDS round trip between sub-steps
+  bf16x8_t af[2][2], bfr[2][4];
+  auto read_frags = [&](const uint8_t* st, int ks, int buf) __attribute__((always_inline)) {
+    const int chunk = ks * 2 + khalf;
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int r = a_row[tm];
+      af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(st + r * ROWB + ((chunk ^ row_swz<CPR>(r)) << 4));
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int r = b_row[tn];
+      bfr[buf][tn] = *reinterpret_cast<const bf16x8_t*>(st + A_BYTES + r * ROWB + ((chunk ^ row_swz<CPR>(r)) << 4));
+    }
+  };
   for (int kt = 0; kt < nk; ++kt) {
     // steps kt+1 .. kt+STAGES-2 may still be in flight; step kt+STAGES-1 is
     // issued during this step's MFMAs into the slot freed by step kt-1
@@ -391,386 +411,20 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
     else wait_dma_barrier_dyn<L, STAGES - 3>(nk - 1 - kt);
     const bool ahead = kt + STAGES - 1 < nk;
     const uint8_t* st = smem + (kt % STAGES) * STAGE_BYTES;
+    read_frags(st, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
-      if (ahead) issue(kt + STAGES - 1, ks * PER, PER);
-      const int chunk = ks * 2 + khalf;
-      bf16x8_t af[2], bfr[4];
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm) {
-        const int r = a_row[tm];
-        af[tm] = *reinterpret_cast<const bf16x8_t*>(st + r * ROWB + ((chunk ^ row_swz<CPR>(r)) << 4));
-      }
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        const int r = b_row[tn];
-        bfr[tn] = *reinterpret_cast<const bf16x8_t*>(st + A_BYTES + r * ROWB + ((chunk ^ row_swz<CPR>(r)) << 4));
-      }
+      if (ks + 1 < NS) read_frags(st, ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
-    }
-  }
-
-  // epilogue (accumulator element r of lane l: row (r&3) + 4*(l>>5) + 8*(r>>2), column l&31)
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + tm * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-      if (row >= rows) continue;
-      uint16_t* crow = C + (m_start + row) * ldc;
-      const int col = lane & 31;
-      if (FUSED) {
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          const uint16_t gb = moe::f32_to_bf16(acc[tm][tn][r]);
-          const uint16_t ub = moe::f32_to_bf16(acc[tm][tn + 2][r]);
-          crow[nt * (kPipeBNW / 2) + wn * 64 + tn * 32 + col] = moe::swiglu_bf16(gb, ub);
-        }
-      } else {
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-          crow[nt * kPipeBNW + wn * 128 + tn * 32 + col] = moe::f32_to_bf16(acc[tm][tn][r]);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Weight-streaming kernel for 128-row blocks (same 128 x 256 tile and tile
-// order as above). Only the A tile, which all four waves read, goes through
-// LDS; each wave owns 64 of the 256 W rows (fused: 32 gate rows and the
-// matching 32 up rows) and streams them from global memory straight into
-// VGPRs. All global loads are plain VGPR loads issued D K-steps ahead into a
-// ring of D+1 register slots (the K loop is unrolled by D+1 so every slot
-// index is a compile-time constant); the A part of a slot is written to a
-// 2-deep LDS buffer one step before it is consumed. Keeping every load a
-// VGPR load lets the compiler count outstanding loads exactly (mixing in
-// direct-to-LDS loads makes it drain the whole queue). Each wave computes
-// 128 x 64 with 8 accumulator tiles: per 16-wide K sub-step, 4 LDS fragment
-// reads feed 8 MFMAs.
-//
-// K order inside a 64-wide step: MFMA lane half h (lanes 32h..32h+31) covers
-// K offsets [32h, 32h+32) over the four sub-steps, sub-step s taking
-// [32h + 8s, 32h + 8s + 8). A and B use the same order, so the products are
-// unchanged, and a lane's W data for a whole step is one contiguous 64-byte
-// piece of its row (four 16-byte loads; lanes l and l+32 cover the row's 128
-// bytes). The A tile keeps 128-byte rows; sub-step s of half h reads 16-byte
-// chunk 4h + s at LDS position (4h + s) ^ row_xor(r).
-#ifndef MOE_V2_DIST
-#define MOE_V2_DIST 3
-#endif
-
-template <bool FUSED, int D>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wstream_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int64_t numel, int m_blocks,
-    int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int gm, int gn) {
-  constexpr int SLOTS = D + 1;
-  constexpr int ROWB = kBK * 2;                    // 128-byte A rows in LDS
-  constexpr int A_STAGE = kPipeBM * ROWB;          // 16 KiB
-  constexpr int A_LOADS = kPipeBM * 8 / kThreads;  // 4 x 16 B per lane per step
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE];
-
-  const int w = blockIdx.x;
-  const int xcd = w & 7, j = w >> 3;
-  const int gsz = gm * gn;
-  const int jg = j / gsz;
-  const int t = j - jg * gsz;
-  const int group = jg * 8 + xcd;
-  const int super_cols = n_tiles / gn;
-  const int sr = group / super_cols;
-  const int sc = group - sr * super_cols;
-  const int tm_ = t % gm;
-  const int bx = sr * gm + tm_;
-  const int nt = sc * gn + (t - tm_) / gm;
-  if (bx >= m_blocks) return;
-  int g, rows;
-  int64_t m_start;
-  decode_block(tb, bx, kPipeBM, numel, g, m_start, rows);
-  if (rows == 0) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, bcol = lane & 31;
-
-  // A staging: chunk q = tid + 256 i covers row q >> 3, 16-byte chunk q & 7
-  const uint16_t* a_src[A_LOADS];
-  int a_dst[A_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = tid + kThreads * i, r = q >> 3, c = q & 7;
-    a_src[i] = A + (m_start + min(r, rows - 1)) * K + c * 8;
-    a_dst[i] = r * ROWB + ((c ^ row_xor(r)) << 4);
-  }
-  const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
-  const uint16_t* b_src[2];
-#pragma unroll
-  for (int tn = 0; tn < 2; ++tn) {
-    int64_t wrow;
-    if (FUSED)
-      wrow = (tn == 0 ? 0 : static_cast<int64_t>(up_row)) + static_cast<int64_t>(nt) * (kPipeBNW / 2) + wave * 32 + bcol;
-    else
-      wrow = static_cast<int64_t>(nt) * kPipeBNW + wave * 64 + tn * 32 + bcol;
-    b_src[tn] = Wb + wrow * K + h * 32;
-  }
-
-  u32x4 areg[SLOTS][A_LOADS];
-  u32x4 breg[SLOTS][2][4];
-
-  auto issue = [&](int kt, auto slot_c) __attribute__((always_inline)) {
-    constexpr int slot = decltype(slot_c)::value;
-    const int k0 = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) areg[slot][i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
-#pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) breg[slot][tn][q] = *reinterpret_cast<const u32x4*>(b_src[tn] + k0 + q * 8);
-  };
-  auto stash = [&](int kt, auto slot_c) __attribute__((always_inline)) {
-    constexpr int slot = decltype(slot_c)::value;
-    uint8_t* st = smem + (kt & 1) * A_STAGE;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<u32x4*>(st + a_dst[i]) = areg[slot][i];
-  };
-
-  floatx16 acc[4][2];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-  auto compute = [&](int kt, auto slot_c) __attribute__((always_inline)) {
-    constexpr int slot = decltype(slot_c)::value;
-    const uint8_t* st = smem + (kt & 1) * A_STAGE;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int chunk = 4 * h + s;
-      bf16x8_t af[4];
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm) {
-        const int r = tm * 32 + bcol;
-        af[tm] = *reinterpret_cast<const bf16x8_t*>(st + r * ROWB + ((chunk ^ row_xor(r)) << 4));
-      }
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af[tm], __builtin_bit_cast(bf16x8_t, breg[slot][tn][s]), acc[tm][tn], 0, 0, 0);
-    }
-  };
-
-  const int nk = K / kBK;
-  // prologue: steps 0..D-1 into slots 0..D-1 (the launcher ensures nk >= D),
-  // step 0's A tile into LDS buffer 0
-  [&]<int... S>(std::integer_sequence<int, S...>) {
-    (issue(S, std::integral_constant<int, S>{}), ...);
-  }(std::make_integer_sequence<int, D>{});
-  stash(0, std::integral_constant<int, 0>{});
-  release_barrier();
-
-  // step kt (slot U): issue step kt + D into slot (U + D) % SLOTS, compute
-  // step kt from LDS buffer kt & 1 and register slot U, then write step
-  // kt + 1's A tile (slot U + 1) into the other LDS buffer; one barrier.
-  auto step = [&](int kt, auto u_c, bool tail) __attribute__((always_inline)) {
-    constexpr int U = decltype(u_c)::value;
-    if (!tail || kt + D < nk) issue(kt + D, std::integral_constant<int, (U + D) % SLOTS>{});
-    compute(kt, u_c);
-    if (!tail || kt + 1 < nk) stash(kt + 1, std::integral_constant<int, (U + 1) % SLOTS>{});
-    release_barrier();
-  };
-  int kt0 = 0;
-  for (; kt0 + SLOTS - 1 + D < nk; kt0 += SLOTS) {
-    [&]<int... S>(std::integer_sequence<int, S...>) {
-      (step(kt0 + S, std::integral_constant<int, S>{}, false), ...);
-    }(std::make_integer_sequence<int, SLOTS>{});
-  }
-  // tail: fewer than SLOTS + D steps left; kt0 is a multiple of SLOTS
-  [&]<int... S>(std::integer_sequence<int, S...>) {
-    ((kt0 + S < nk ? step(kt0 + S, std::integral_constant<int, S % SLOTS>{}, true) : void()), ...);
-  }(std::make_integer_sequence<int, SLOTS - 1 + D>{});
-
-  // epilogue (accumulator element r of lane l: row (r&3) + 4*(l>>5) + 8*(r>>2), column l&31)
-#pragma unroll
-  for (int tm = 0; tm < 4; ++tm) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = tm * 32 + (r & 3) + 4 * h + 8 * (r >> 2);
-      if (row >= rows) continue;
-      uint16_t* crow = C + (m_start + row) * ldc;
-      if (FUSED) {
-        const uint16_t gb = moe::f32_to_bf16(acc[tm][0][r]);
-        const uint16_t ub = moe::f32_to_bf16(acc[tm][1][r]);
-        crow[nt * (kPipeBNW / 2) + wave * 32 + bcol] = moe::swiglu_bf16(gb, ub);
-      } else {
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn) crow[nt * kPipeBNW + wave * 64 + tn * 32 + bcol] = moe::f32_to_bf16(acc[tm][tn][r]);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Pair kernel: a workgroup covers two consecutive 128-row blocks of one
-// expert (256 rows) against 256 W rows, so each weight byte brought into the
-// CU feeds 512 FLOPs instead of 256 (the per-CU load path and HBM carry half
-// the weight traffic of the 128-row tile). The launch grid is the same as
-// for 128-row blocks: the block with an even index inside its expert leads
-// the pair, the odd one exits at once. Eight waves (two per SIMD, so one
-// wave's MFMAs cover the other's load and barrier stalls) in a 4 x 2
-// arrangement each accumulate 64 x 128 (8 tiles of 32 x 32); waves whose 64
-// rows are all past the expert's end skip their LDS reads and MFMAs, so an
-// expert's single last block costs what a 128-row tile costs. K step 32
-// (64-byte LDS rows, row_swz<4>), STAGES-deep direct-to-LDS ring with the
-// next step's loads spread over the MFMA sub-steps.
-#ifndef MOE_PAIR_STAGES
-#define MOE_PAIR_STAGES 3
-#endif
-constexpr int kPairThreads = 512;
-
-template <bool FUSED, int STAGES>
-__global__ __launch_bounds__(kPairThreads, 1) void grouped_gemm_pair_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int64_t numel, int m_blocks,
-    int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int gm, int gn) {
-  constexpr int BK = 32, CPR = 4, ROWB = 64, RPL = 16;   // 16 rows per wave-wide DMA load
-  constexpr int BM = 256;
-  constexpr int A_BYTES = BM * ROWB;                     // 16 KiB
-  constexpr int STAGE_BYTES = (BM + kPipeBNW) * ROWB;    // 32 KiB
-  constexpr int A_LOADS = BM / (8 * RPL);                // 2 per lane per step
-  constexpr int B_LOADS = kPipeBNW / (8 * RPL);          // 2
-  constexpr int L = A_LOADS + B_LOADS;
-  static_assert(STAGES >= 3 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE_BYTES];
-
-  const int w = blockIdx.x;
-  const int xcd = w & 7, j = w >> 3;
-  const int gsz = gm * gn;
-  const int jg = j / gsz;
-  const int t = j - jg * gsz;
-  const int group = jg * 8 + xcd;
-  const int super_cols = n_tiles / gn;
-  const int sr = group / super_cols;
-  const int sc = group - sr * super_cols;
-  const int tm_ = t % gm;
-  const int bx = sr * gm + tm_;
-  const int nt = sc * gn + (t - tm_) / gm;
-  if (bx >= m_blocks) return;
-  int g, rows;
-  int64_t m_start;
-  if (tb.gs == nullptr) {
-    if (bx & 1) return;
-    g = 0;
-    m_start = static_cast<int64_t>(bx) * kPipeBM;
-    const int64_t r = numel - m_start;
-    rows = r <= 0 ? 0 : (r >= BM ? BM : static_cast<int>(r));
-  } else {
-    g = tb.gidx[bx];
-    const int local = bx - tb.gpo[g] / kPipeBM;  // block index inside the expert
-    if (local & 1) return;
-    m_start = static_cast<int64_t>(bx) * kPipeBM - tb.gpo[g] + tb.go[g];
-    const int64_t r = static_cast<int64_t>(tb.go[g]) + tb.gs[g] - m_start;
-    rows = r <= 0 ? 0 : (r >= BM ? BM : static_cast<int>(r));
-  }
-  if (rows == 0) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const bool live = wm * 64 < rows;                      // this wave's rows hold data
-  const int lrow = lane / CPR, lpos = lane % CPR;
-
-  const uint16_t* a_src[A_LOADS];
-  int a_lds[A_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int rb = (wave * A_LOADS + i) * RPL;
-    const int r = rb + lrow;
-    a_src[i] = A + (m_start + min(r, rows - 1)) * K + (lpos ^ row_swz<CPR>(r)) * 8;
-    a_lds[i] = rb * ROWB;
-  }
-  const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
-  const uint16_t* b_src[B_LOADS];
-  int b_lds[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int rb = (wave * B_LOADS + i) * RPL;
-    const int r = rb + lrow;
-    int64_t wrow;
-    if (FUSED)
-      wrow = r < kPipeBNW / 2 ? static_cast<int64_t>(nt) * (kPipeBNW / 2) + r
-                              : static_cast<int64_t>(up_row) + static_cast<int64_t>(nt) * (kPipeBNW / 2) + (r - kPipeBNW / 2);
-    else
-      wrow = static_cast<int64_t>(nt) * kPipeBNW + r;
-    b_src[i] = Wb + wrow * K + (lpos ^ row_swz<CPR>(r)) * 8;
-    b_lds[i] = A_BYTES + rb * ROWB;
-  }
-  auto issue = [&](int kt, int first, int count) __attribute__((always_inline)) {
-    uint8_t* st = smem + (kt % STAGES) * STAGE_BYTES;
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      if (i < first || i >= first + count) continue;
-      if (i < A_LOADS) dma16(a_src[i] + k0, st + a_lds[i]);
-      else dma16(b_src[i - A_LOADS] + k0, st + b_lds[i - A_LOADS]);
-    }
-  };
-
-  floatx16 acc[2][4];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-  int a_row[2], b_row[4];
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm) a_row[tm] = wm * 64 + tm * 32 + (lane & 31);
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-    b_row[tn] = (FUSED ? (tn < 2 ? wn * 64 + tn * 32 : kPipeBNW / 2 + wn * 64 + (tn - 2) * 32)
-                       : wn * 128 + tn * 32) + (lane & 31);
-  const int khalf = lane >> 5;
-
-  constexpr int NS = BK / 16;  // 2 sub-steps
-  constexpr int PER = (L + NS - 1) / NS;
-  const int nk = K / BK;
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s, 0, L);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + STAGES - 2 < nk) wait_dma_barrier<(STAGES - 2) * L>();
-    else wait_dma_barrier_dyn<L, STAGES - 3>(nk - 1 - kt);
-    const bool ahead = kt + STAGES - 1 < nk;
-    const uint8_t* st = smem + (kt % STAGES) * STAGE_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < NS; ++ks) {
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][tm], bfr[ks & 1][tn], acc[tm][tn], 0, 0, 0);
+      // the loads set M0, which makes the compiler drain outstanding LDS
+      // reads: issue them after this sub-step's MFMAs are queued
       if (ahead) issue(kt + STAGES - 1, ks * PER, PER);
-      if (live) {
-        const int chunk = ks * 2 + khalf;
-        bf16x8_t af[2], bfr[4];
-#pragma unroll
-        for (int tm = 0; tm < 2; ++tm) {
-          const int r = a_row[tm];
-          af[tm] = *reinterpret_cast<const bf16x8_t*>(st + r * ROWB + ((chunk ^ row_swz<CPR>(r)) << 4));
-        }
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-          const int r = b_row[tn];
-          bfr[tn] = *reinterpret_cast<const bf16x8_t*>(st + A_BYTES + r * ROWB + ((chunk ^ row_swz<CPR>(r)) << 4));
-        }
-#pragma unroll
-        for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < 4; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
-      }
     }
   }
-  if (!live) return;
 
   // epilogue (accumulator element r of lane l: row (r&3) + 4*(l>>5) + 8*(r>>2), column l&31)
 #pragma unroll
@@ -817,20 +471,6 @@ int launch_pipe(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, 
   const int64_t groups = moe::ceil_div(m_blocks, gm) * (n_tiles / gn);
   const int64_t blocks = moe::ceil_div(groups, 8) * 8 * gm * gn;
   if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
-#if MOE_GEMM_KERNEL == 3
-  if (K % 32 == 0) {
-    grouped_gemm_pair_kernel<FUSED, MOE_PAIR_STAGES><<<static_cast<unsigned>(blocks), kPairThreads, 0, stream>>>(
-        A, W, tb, numel, static_cast<int>(m_blocks), n_tiles, K, w_stride, up_row, ldc, C, gm, gn);
-    return moe::check_launch(name);
-  }
-#endif
-#if MOE_GEMM_KERNEL == 2
-  if (K / kBK >= MOE_V2_DIST) {
-    grouped_gemm_wstream_kernel<FUSED, MOE_V2_DIST><<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
-        A, W, tb, numel, static_cast<int>(m_blocks), n_tiles, K, w_stride, up_row, ldc, C, gm, gn);
-    return moe::check_launch(name);
-  }
-#endif
   grouped_gemm_pipe_kernel<FUSED, MOE_PIPE_BK, MOE_PIPE_STAGES, MOE_PIPE_OCC><<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
       A, W, tb, numel, static_cast<int>(m_blocks), n_tiles, K, w_stride, up_row, ldc, C, gm, gn);
   return moe::check_launch(name);
