@@ -451,6 +451,292 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel for 128-row blocks: 256 x 256 tiles. A workgroup takes two
+// consecutive 128-row blocks of one expert (blocks 2q and 2q+1 of the
+// expert's padded range, i.e. its compact rows 256q .. 256q+255), so every
+// weight byte brought to the CU feeds 256 rows instead of 128: 128 FLOP per
+// staged byte against 85 for the 128 x 256 tile, which is what counts when
+// the CUs are fed at a fixed rate. The grid enumerates these 256-row tiles
+// directly (find_wide_tile), so no workgroup is launched for the odd blocks:
+// launching and retiring one per odd block lines the working workgroups up
+// with the hardware's workgroup-to-CU rotation and leaves half of the CUs
+// idle.
+//
+// Four waves in a 2x2 arrangement, each 128 rows x 128 weight rows
+// (16 accumulator tiles = 256 fp32 per lane, held in AGPRs), so one wave
+// reads 8 fragments per 16 MFMAs.
+//
+// An expert's last tile often has 128 rows or fewer (an odd block count).
+// Such a "half" tile loads only 128 A rows and splits K between the wave
+// rows: wave (wm, wn) computes rows 0..127 against weight rows of column half
+// wn over the 16-wide sub-steps ks with ks % 2 == wm, and the two partial
+// sums meet in LDS at the end. A half tile therefore costs about half a full
+// one, and the padding overhead stays that of 128-row blocks.
+//
+// Loads, fragments and barriers work as in grouped_gemm_pipe_kernel, over
+// the ring described at wide_ring_tile.
+constexpr int kWideRows = 256;
+constexpr int kWideW = 256;
+
+// The wide tile's K loop, K step 64 (whole 128-byte rows, so every L1 -> L2
+// request moves a full line): the A and the W part of a step are
+// separate 32 KiB "half stages", H(2kt) = A(kt) and H(2kt+1) = W(kt), kept in
+// a ring of five slots (H(i) in slot i % 5, 160 KiB). During step kt the
+// loads of W(kt+1) and A(kt+2) go into the two slots step kt-1 used, and the
+// wait at the top of step kt+1 leaves A(kt+2) in flight: between one and
+// three half stages are in flight at any time and the ring never drains.
+constexpr int kRingSlots = 5;
+constexpr int kRingSlotBytes = kWideRows * 128;
+
+template <bool FUSED, bool HALF>
+__device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __restrict__ A,
+                                               const uint16_t* __restrict__ Wb, int64_t m_start, int rows, int nt,
+                                               int K, int up_row, int ldc, uint16_t* __restrict__ C) {
+  constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
+  constexpr int AROWS = HALF ? kWideRows / 2 : kWideRows;
+  constexpr int A_LOADS = AROWS / (4 * RPL);         // per wave per half stage
+  constexpr int B_LOADS = kWideW / (4 * RPL);
+  constexpr int NS = BK / 16;
+  constexpr int MY_NS = HALF ? NS / 2 : NS;
+  constexpr int L = A_LOADS + B_LOADS;               // loads issued per step
+  constexpr int PER = (L + MY_NS - 1) / MY_NS;
+  static_assert(kRingSlotBytes == kWideW * ROWB, "slot holds one 256-row part");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = lane / CPR;
+  const int lpos = lane % CPR;
+
+  const uint16_t* a_src[A_LOADS];
+  int a_lds[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int rb = (wave * A_LOADS + i) * RPL;
+    const int r = rb + lrow;
+    const int rr = min(r, rows - 1);
+    a_src[i] = A + (m_start + rr) * K + (lpos ^ row_xor(r)) * 8;
+    a_lds[i] = rb * ROWB;
+  }
+  const uint16_t* b_src[B_LOADS];
+  int b_lds[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int rb = (wave * B_LOADS + i) * RPL;
+    const int r = rb + lrow;
+    int64_t wrow;
+    if (FUSED)
+      wrow = r < kWideW / 2 ? static_cast<int64_t>(nt) * (kWideW / 2) + r
+                            : static_cast<int64_t>(up_row) + static_cast<int64_t>(nt) * (kWideW / 2) + (r - kWideW / 2);
+    else
+      wrow = static_cast<int64_t>(nt) * kWideW + r;
+    b_src[i] = Wb + wrow * K + (lpos ^ row_xor(r)) * 8;
+    b_lds[i] = rb * ROWB;
+  }
+  auto slot = [&](int h) __attribute__((always_inline)) { return smem + (h % kRingSlots) * kRingSlotBytes; };
+  // loads [first, first+count) of the step-kt issue list: W(kt+1) then A(kt+2)
+  auto issue = [&](int kt, int first, int count, int nk) __attribute__((always_inline)) {
+    uint8_t* ws = slot(2 * (kt + 1) + 1);
+    uint8_t* as = slot(2 * (kt + 2));
+    const int kw = (kt + 1) * BK, ka = (kt + 2) * BK;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (i < first || i >= first + count) continue;
+      if (i < B_LOADS) {
+        if (kt + 1 < nk) dma16(b_src[i] + kw, ws + b_lds[i]);
+      } else {
+        if (kt + 2 < nk) dma16(a_src[i - B_LOADS] + ka, as + a_lds[i - B_LOADS]);
+      }
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  const int row0 = HALF ? 0 : wm * 128;
+  int a_row[4], b_row[4];
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm) a_row[tm] = row0 + tm * 32 + (lane & 31);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+    b_row[tn] = (FUSED ? (tn < 2 ? wn * 64 + tn * 32 : kWideW / 2 + wn * 64 + (tn - 2) * 32) : wn * 128 + tn * 32) +
+                (lane & 31);
+  const int khalf = lane >> 5;
+
+  const int nk = K / BK;
+  // prologue: A(0), W(0), A(1)
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) dma16(a_src[i], slot(0) + a_lds[i]);
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) dma16(b_src[i], slot(1) + b_lds[i]);
+  if (nk > 1) {
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) dma16(a_src[i] + BK, slot(2) + a_lds[i]);
+  }
+
+  bf16x8_t af[2][4], bfr[2][4];
+  auto read_frags = [&](const uint8_t* as, const uint8_t* bs, int ks, int buf) __attribute__((always_inline)) {
+    const int chunk = ks * 2 + khalf;
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+      const int r = a_row[tm];
+      af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(as + r * ROWB + ((chunk ^ row_xor(r)) << 4));
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int r = b_row[tn];
+      bfr[buf][tn] = *reinterpret_cast<const bf16x8_t*>(bs + r * ROWB + ((chunk ^ row_xor(r)) << 4));
+    }
+  };
+  auto my_ks = [&](int i) __attribute__((always_inline)) { return HALF ? 2 * i + wm : i; };
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // every load except A(kt+1) (the last issued) must have landed
+    if (kt + 1 < nk) wait_dma_barrier<A_LOADS>();
+    else wait_dma_barrier<0>();
+    const uint8_t* as = slot(2 * kt);
+    const uint8_t* bs = slot(2 * kt + 1);
+    read_frags(as, bs, my_ks(0), 0);
+#pragma unroll
+    for (int i = 0; i < MY_NS; ++i) {
+      if (i + 1 < MY_NS) read_frags(as, bs, my_ks(i + 1), (i + 1) & 1);
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i & 1][tm], bfr[i & 1][tn], acc[tm][tn], 0, 0, 0);
+      issue(kt, i * PER, PER, nk);
+    }
+  }
+
+  if constexpr (HALF) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    typedef float floatx4 __attribute__((ext_vector_type(4)));
+    floatx4* xch = reinterpret_cast<floatx4*>(smem + wn * (64 * 1024));
+    if (wm == 1) {
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            floatx4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2], acc[tm][tn][4 * q + 3]};
+            xch[((tm * 4 + tn) * 4 + q) * 64 + lane] = v;
+          }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wm == 1) return;
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const floatx4 v = xch[((tm * 4 + tn) * 4 + q) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[tm][tn][4 * q + e] += v[e];
+        }
+  }
+
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + tm * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+      if (row >= rows) continue;
+      uint16_t* crow = C + (m_start + row) * ldc;
+      const int col = lane & 31;
+      if (FUSED) {
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) {
+          const uint16_t gb = moe::f32_to_bf16(acc[tm][tn][r]);
+          const uint16_t ub = moe::f32_to_bf16(acc[tm][tn + 2][r]);
+          crow[nt * (kWideW / 2) + wn * 64 + tn * 32 + col] = moe::swiglu_bf16(gb, ub);
+        }
+      } else {
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+          crow[nt * kWideW + wn * 128 + tn * 32 + col] = moe::f32_to_bf16(acc[tm][tn][r]);
+      }
+    }
+  }
+}
+
+// Expert g and tile q inside it of the p-th 256-row tile, counting
+// ceil(gs[e] / 256) tiles per expert in expert order (a wave-wide scan over
+// the group sizes, 64 experts at a time). Returns false past the last tile.
+__device__ __forceinline__ bool find_wide_tile(const int32_t* __restrict__ gs, int E, int p, int& g, int& q) {
+  const int lane = threadIdx.x & 63;
+  int before = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int pc = e < E ? (gs[e] + (kWideRows - 1)) / kWideRows : 0;
+    int incl = pc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int total = __shfl(incl, 63);
+    if (p < before + total) {
+      const int j = __builtin_ctzll(__ballot(before + incl > p));
+      g = __builtin_amdgcn_readfirstlane(base + j);
+      q = __builtin_amdgcn_readfirstlane(p - before - (__shfl(incl, j) - __shfl(pc, j)));
+      return true;
+    }
+    before += total;
+  }
+  return false;
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel, int m_tiles,
+    int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int gm, int gn) {
+  constexpr int SMEM = kRingSlots * kRingSlotBytes;
+  static_assert(SMEM <= 160 * 1024, "LDS ring too large");
+  static_assert(SMEM >= 128 * 1024, "the half-tile exchange needs 128 KiB");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+
+  const int w = blockIdx.x;
+  const int xcd = w & 7, j = w >> 3;
+  const int gsz = gm * gn;
+  const int jg = j / gsz;
+  const int t = j - jg * gsz;
+  const int group = jg * 8 + xcd;
+  const int super_cols = n_tiles / gn;
+  const int sr = group / super_cols;
+  const int sc = group - sr * super_cols;
+  const int tm_ = t % gm;
+  const int p = sr * gm + tm_;                 // 256-row tile index
+  const int nt = sc * gn + (t - tm_) / gm;
+  if (p >= m_tiles) return;
+  int g;
+  int64_t m_start, r;
+  if (tb.gs == nullptr) {
+    g = 0;
+    m_start = static_cast<int64_t>(p) * kWideRows;
+    r = numel - m_start;
+  } else {
+    int q;
+    if (!find_wide_tile(tb.gs, E, p, g, q)) return;
+    m_start = static_cast<int64_t>(tb.go[g]) + static_cast<int64_t>(q) * kWideRows;
+    r = static_cast<int64_t>(tb.gs[g]) - static_cast<int64_t>(q) * kWideRows;
+  }
+  if (r <= 0) return;
+  const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
+  const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
+  if (rows <= kWideRows / 2)
+    wide_ring_tile<FUSED, true>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
+  else
+    wide_ring_tile<FUSED, false>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
+}
+
 // Group shape for the tile order: GN column tiles (a divisor of n_tiles, at
 // most MOE_PIPE_GN_MAX) by GM row blocks, about MOE_PIPE_GROUP tiles.
 void pipe_groups(int n_tiles, int& gm, int& gn) {
@@ -476,6 +762,30 @@ int launch_pipe(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, 
   return moe::check_launch(name);
 }
 
+#ifndef MOE_WIDE_GROUP
+#define MOE_WIDE_GROUP 16
+#endif
+
+template <bool FUSED>
+int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int n_tiles, int K,
+                int64_t w_stride, int up_row, int ldc, uint16_t* C, hipStream_t stream, const char* name) {
+  // every non-empty expert ends in at most one partial tile
+  const int64_t m_tiles = moe::ceil_div(numel, kWideRows) + (tb.gs ? E : 0);
+  int gn = 1;
+  for (int d = MOE_PIPE_GN_MAX; d >= 1; --d)
+    if (n_tiles % d == 0) {
+      gn = d;
+      break;
+    }
+  const int gm = MOE_WIDE_GROUP / gn > 0 ? MOE_WIDE_GROUP / gn : 1;
+  const int64_t groups = moe::ceil_div(m_tiles, gm) * (n_tiles / gn);
+  const int64_t blocks = moe::ceil_div(groups, 8) * 8 * gm * gn;
+  if (blocks > 0x7FFFFFFF || m_tiles > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
+  grouped_gemm_wide_kernel<FUSED><<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
+      A, W, tb, E, numel, static_cast<int>(m_tiles), n_tiles, K, w_stride, up_row, ldc, C, gm, gn);
+  return moe::check_launch(name);
+}
+
 template <bool FUSED>
 int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E, int block_m, int padding_m,
            int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* C, hipStream_t stream,
@@ -485,6 +795,11 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
   // ldc is the output width: F for the fused gate_up, 2F or H otherwise
   const int pipe_cols = FUSED ? kPipeBNW / 2 : kPipeBNW;
+  // 256-row tiles pay off once experts average a full 128-row block (at
+  // fewer rows per expert nearly every tile is a half tile and the 128-row
+  // kernel, with less fixed cost per tile, is faster)
+  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && numel >= static_cast<int64_t>(kPipeBM) * E)
+    return launch_wide<FUSED>(A, W, tb, E, numel, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
   if (block_m == kPipeBM && ldc % pipe_cols == 0)
     return launch_pipe<FUSED>(A, W, tb, numel, m_blocks, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);

@@ -177,6 +177,59 @@ def test_dense_group_gemm(numel, bm):
     assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd)[None], one, zero), "dense down")
 
 
+# Expert sizes around the 128-row block and the 256-row pair of blocks: an
+# empty expert, single rows, partial and exact blocks, odd and even block
+# counts (the last block of an odd count is computed on its own).
+EDGE_SIZES = [0, 1, 127, 128, 129, 255, 256, 257, 383, 384, 385, 700]
+
+
+@pytest.mark.parametrize("H,F,extra_empty", [(256, 256, 0), (512, 384, 0), (256, 256, 20)])
+def test_grouped_gemm_expert_size_edges(H, F, extra_empty):
+    """extra_empty appends empty experts; with 20 of them the rows per expert
+    average under one 128-row block, which selects the 128-row tile kernel
+    instead of the 256-row one."""
+    d = dev()
+    say("gemm edges", H, F, extra_empty)
+    sizes = EDGE_SIZES + [0] * extra_empty
+    E = len(sizes)
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    ids_np = ids_np[np.random.default_rng(7).permutation(ids_np.size)][:, None]
+    T = ids_np.shape[0]
+    ids = _t(ids_np, d)
+    tb = mx.moe_align(ids, E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    assert list(gs) == sizes
+    key = moe_synth.tensor_key(71, H)
+    xp = moe_synth.normal_bf16(key, (T, H), 1.0, d)
+    wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, H), H ** -0.5, d)
+    wd = moe_synth.normal_bf16(key + 2, (E, H, F), F ** -0.5, d)
+    gu = mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, fuse_swiglu=False)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(xp), bits(wgu), gs, go), "gate_up")
+    h = mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, fuse_swiglu=True)
+    assert torch.equal(h, mx.swiglu(gu))
+    y = mx.grouped_gemm_down(h, wd, tb, 128, 128)
+    assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd), gs, go), "down")
+    # same inputs again: bitwise repeatable
+    assert torch.equal(mx.grouped_gemm_down(h, wd, tb, 128, 128), y)
+
+
+@pytest.mark.parametrize("numel", [1, 129, 300, 4224])
+def test_dense_gemm_wide_shapes(numel):
+    d = dev()
+    H, F = 256, 256
+    key = moe_synth.tensor_key(72, numel)
+    x = moe_synth.normal_bf16(key, (numel, H), 1.0, d)
+    wgu = moe_synth.normal_bf16(key + 1, (2 * F, H), H ** -0.5, d)
+    wd = moe_synth.normal_bf16(key + 2, (H, F), F ** -0.5, d)
+    one, zero = np.array([numel], np.int32), np.array([0], np.int32)
+    gu = mx.grouped_gemm_gate_up(x, wgu, None, 128, 128, fuse_swiglu=False)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(wgu)[None], one, zero), "dense gate_up")
+    h = mx.grouped_gemm_gate_up(x, wgu, None, 128, 128, fuse_swiglu=True)
+    assert torch.equal(h, mx.swiglu(gu))
+    y = mx.grouped_gemm_down(h, wd, None, 128, 128)
+    assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd)[None], one, zero), "dense down")
+
+
 # --------------------------------------------------------------- swiglu --
 
 def test_swiglu_bit_exact_including_extremes():
