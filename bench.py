@@ -68,6 +68,7 @@ def main():
     t_gen = time.time()
     hidden = moe_synth.hidden(cfg, dev)
     logits = moe_synth.router_logits(cfg, dev)
+    bias = moe_synth.expert_bias(cfg, dev)
     wgu = moe_synth.w_gate_up(cfg, dev)
     wd = moe_synth.w_down(cfg, dev)
     swgu = moe_synth.shared_w_gate_up(cfg, dev) if cfg.shared_F else None
@@ -98,7 +99,7 @@ def main():
             else:
                 fn()
         tb = bufs.tables
-        run("topk_softmax", lambda: mx.moe_topk_softmax(logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights))
+        run("topk_softmax", lambda: mx.moe_topk_softmax(logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bias))
         run("align", lambda: mx.moe_align(bufs.topk_ids, cfg.E, cfg.padding_m, cfg.block_m, tb))
         run("permute", lambda: mx.moe_permute(hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm))
         if fuse:
@@ -123,15 +124,20 @@ def main():
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    step_ev = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
+        a = ev()
         step(True)
+        step_ev.append((a, ev()))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     stage_ms = {s: (sum(a.elapsed_time(b) for a, b in v) / len(v)) for s, v in ev_log.items() if v}
+    stage_pct = {s: pct([a.elapsed_time(b) for a, b in v]) for s, v in ev_log.items() if v}
+    step_pct = pct([a.elapsed_time(b) for a, b in step_ev])
 
     # realized routing (read after the timed region)
     gs = bufs.tables["group_sizes"].cpu().numpy()
@@ -152,7 +158,7 @@ def main():
         if not ms:
             return None
         s = ms * 1e-3
-        return {"ms": round(ms, 4), "tflops": round(flop / s / 1e12, 2) if flop else None,
+        return {"ms": round(ms, 4), **stage_pct[name], "tflops": round(flop / s / 1e12, 2) if flop else None,
                 "gbs": round(byts / s / 1e9, 1), "mfma_frac": round(flop / s / 1e12 / BF16_PEAK_TFLOPS, 4) if flop else None,
                 "hbm_frac": round(byts / s / 1e9 / HBM_PEAK_GBS, 4),
                 "roofline_frac": round(max(flop / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) / s, 4)}
@@ -174,16 +180,23 @@ def main():
     qM, qF = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
     for _ in range(5):
         mx.swiglu_quant_fp8(qx, qbufs)
+    # its working set (about 0.4 GB) is under twice the 256 MiB MALL: a 512 MiB
+    # write outside the events evicts it between launches
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     qev = []
-    for _ in range(max(20, args.steps)):
+    for i in range(max(20, args.steps)):
+        flush.fill_(i & 0xFF)
         a = ev()
         mx.swiglu_quant_fp8(qx, qbufs)
         qev.append((a, ev()))
     torch.cuda.synchronize()
-    q_ms = sum(a.elapsed_time(b) for a, b in qev) / len(qev)
+    del flush
+    q_list = [a.elapsed_time(b) for a, b in qev]
+    q_ms = sum(q_list) / len(q_list)
     qm_pad = -(-qM // 128) * 128
     q_bytes = qM * 4 * qF + qM * qF + 4 * qM * qF // 128 + qF * qm_pad + 4 * (qF // 128) * (qm_pad // 128)
-    kernels["swiglu_quant_fp8"] = {"workload": f"M={qM},F={qF}", "ms": round(q_ms, 4),
+    kernels["swiglu_quant_fp8"] = {"workload": f"M={qM},F={qF}", "ms": round(q_ms, 4), **pct(q_list),
+                                   "mall_flushed": True,
                                    "gbs": round(q_bytes / q_ms / 1e6, 1),
                                    "hbm_frac": round(q_bytes / q_ms / 1e6 / HBM_PEAK_GBS, 4)}
 
@@ -212,13 +225,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, args.cpu_tokens)
+        cpu = cpu_baseline(cfg, hidden, logits, bias, wgu, wd, swgu, swd, args.cpu_tokens)
 
     value = flop_fwd / (ms_per_step * 1e-3) / 1e12
     line = {
         "metric": "routed-experts fwd ms + grouped-GEMM TFLOPS (% MFMA peak), T=4096",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms_per_step, 4), "step_ms_p50": step_pct["ms_p50"], "step_ms_min": step_pct["ms_min"],
+        "step_ms_p90": step_pct["ms_p90"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded counter-based generator, N(0,1)-shaped inputs, random-init weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": H, "F": F, "E": E, "top_k": cfg.top_k,
                    "padding_m": cfg.padding_m, "block_m": cfg.block_m, "routed_scaling_factor": cfg.rsf,
@@ -250,7 +264,24 @@ def measured_traffic(workload, fused):
     return int(float(kv["traffic_bytes"]))
 
 
-def cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, n_tokens):
+def pct(ms_list):
+    v = np.sort(np.asarray(ms_list, dtype=np.float64))
+    return {"ms_p50": round(float(np.percentile(v, 50)), 4), "ms_min": round(float(v[0]), 4),
+            "ms_p90": round(float(np.percentile(v, 90)), 4)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, hidden, logits, bias, wgu, wd, swgu, swd, n_tokens):
     """The oracle, as it stands, on a bounded sample of tokens: TFLOP/s on the host cores."""
     import torch
     import moe_synth
@@ -266,7 +297,8 @@ def cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, n_tokens):
     tsel = torch.as_tensor(tokens, device=hidden.device)
     hid = moe_synth.bits16(hidden[tsel])
     lg = logits[tsel].cpu().numpy()
-    ids, _ = oracle.route(lg, cfg.top_k)
+    bias_h = None if bias is None else bias.cpu().numpy()
+    ids, _ = oracle.route(lg, cfg.top_k, bias_h)
     used = np.unique(ids)
     sel = torch.as_tensor(used, device=wgu.device)
     wgu_h = moe_synth.bits16(wgu[sel])
@@ -277,7 +309,7 @@ def cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, n_tokens):
     remap[used] = np.arange(used.size)
     # the oracle's forward on the sampled tokens, restricted to the experts they reach
     t0 = time.perf_counter()
-    ids2, w = oracle.route(lg, cfg.top_k)
+    ids2, w = oracle.route(lg, cfg.top_k, bias_h)
     ids_r = remap[ids2].astype(np.int32)
     tab = oracle.dispatch_tables(ids_r, used.size, cfg.padding_m, cfg.block_m)
     xp = oracle.permute(hid, tab["sorted_pair"], cfg.top_k)
@@ -291,7 +323,8 @@ def cpu_baseline(cfg, hidden, logits, wgu, wd, swgu, swd, n_tokens):
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{tokens.size} of {cfg.T} tokens of {cfg.name} ({used.size} experts reached), "
                       f"full forward incl. shared expert, float64 GEMMs; {dt:.1f}s",
-            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":

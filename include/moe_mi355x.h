@@ -63,18 +63,29 @@ int64_t moe_num_blocks(int64_t numel, int E, int block_m, int padding_m);
  * experts. */
 size_t moe_align_workspace_bytes(int64_t numel, int E);
 
-/* Top-k softmax routing.
+/* Scoring functions of moe_topk_softmax. */
+#define MOE_SCORING_SOFTMAX 0 /* softmax over all E experts (the workloads of TileOPs #1580) */
+#define MOE_SCORING_SIGMOID 1 /* logistic sigmoid per expert ("sigmoid routing", the Kimi-K2
+                                 benchmark of TileOPs #778) */
+
+/* Top-k routing.
  * logits       [T, E] float32 router scores ("gating", TileOPs #778,
  *              "Partial output contract").
- * topk_ids     [T, top_k] int32 out: experts in descending-logit order; equal
- *              logits go to the lower expert id.
- * topk_weights [T, top_k] float32 out: softmax over all E renormalised over
- *              the selected experts (equal to a softmax over the selected
- *              logits), so each row sums to 1.
+ * expert_bias  [E] float32 or NULL: added to every row of logits (one fp32
+ *              addition) before selection and scoring.
+ * scoring      MOE_SCORING_SOFTMAX or MOE_SCORING_SIGMOID.
+ * renormalize  1: weights are the selected experts' scores divided by their
+ *              sum (for softmax: a softmax over the selected logits), so each
+ *              row sums to 1; 0: the scores themselves (softmax probability
+ *              over all E, or the sigmoid).
+ * topk_ids     [T, top_k] int32 out: experts in descending order of
+ *              logit + bias; equal values go to the lower expert id.
+ * topk_weights [T, top_k] float32 out, slot order as topk_ids.
  * Limits: 1 <= E <= 1024, 1 <= top_k <= min(E, 16). Non-finite logits are
- * not supported. */
-int moe_topk_softmax(const float* logits, int64_t T, int E, int top_k, int32_t* topk_ids,
-                     float* topk_weights, hipStream_t stream);
+ * not supported. Returns MOE_ERR_INVALID_ARG for another scoring or
+ * renormalize value. */
+int moe_topk_softmax(const float* logits, const float* expert_bias, int64_t T, int E, int top_k, int scoring,
+                     int renormalize, int32_t* topk_ids, float* topk_weights, hipStream_t stream);
 
 /* Dispatch tables of Tutorial Example 07 ("moe_dispatch_contract.py": the
  * four host-side tables and the kernel-side row recovery), built on the

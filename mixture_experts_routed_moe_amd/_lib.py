@@ -4,7 +4,9 @@ Each function takes torch tensors that live on the GPU, checks dtype, shape
 and contiguity, passes raw device pointers and the current HIP stream to the
 C entry point of the same name, and raises MoeError on a non-zero return.
 Every computation happens in the library's HIP kernels; there is no host or
-PyTorch fallback, and importing this module fails if the library is missing.
+PyTorch fallback: the first call raises ImportError if the library is missing
+or was built for another ABI revision (the import itself does not load it, so
+the build step can run from a fresh checkout).
 """
 from __future__ import annotations
 
@@ -29,6 +31,10 @@ class MoeError(RuntimeError):
         self.code = code
 
 
+ABI_VERSION = 2
+SCORING = {"softmax": 0, "sigmoid": 1}
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -41,7 +47,7 @@ def _load() -> ctypes.CDLL:
         "moe_abi_version": (I, []),
         "moe_num_blocks": (I64, [I64, I, I, I]),
         "moe_align_workspace_bytes": (SZ, [I64, I]),
-        "moe_topk_softmax": (I, [P, I64, I, I, P, P, P]),
+        "moe_topk_softmax": (I, [P, P, I64, I, I, I, I, P, P, P]),
         "moe_align": (I, [P, I64, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
         "moe_permute": (I, [P, P, I64, I, I, P, P]),
         "grouped_gemm_gate_up": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
@@ -54,10 +60,13 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI {lib.moe_abi_version()}, this binding needs {ABI_VERSION}: rebuild it "
+                          "with `python -m mixture_experts_routed_moe_amd.build`")
     return lib
 
 
-_lib = _load()
+_lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_workspace_bytes",
            "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up", "swiglu",
@@ -65,13 +74,19 @@ EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_wor
 
 
 def lib() -> ctypes.CDLL:
+    """The loaded library; loads it on first use and raises ImportError when
+    it is missing or was built for another ABI revision (there is no
+    fallback path)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
     return _lib
 
 
 def _call(name: str, *args) -> None:
-    rc = getattr(_lib, name)(*args)
+    rc = getattr(lib(), name)(*args)
     if rc != MOE_OK:
-        raise MoeError(name, rc, _lib.moe_last_error().decode(errors="replace"))
+        raise MoeError(name, rc, lib().moe_last_error().decode(errors="replace"))
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -99,24 +114,34 @@ def _out(out: Optional[torch.Tensor], shape, dtype, like: torch.Tensor, name: st
 
 
 def num_blocks(numel: int, E: int, block_m: int, padding_m: int) -> int:
-    n = _lib.moe_num_blocks(numel, E, block_m, padding_m)
+    n = lib().moe_num_blocks(numel, E, block_m, padding_m)
     if n < 0:
         raise ValueError("num_blocks: padding_m must be a positive multiple of block_m")
     return int(n)
 
 
 def align_workspace_bytes(numel: int, E: int) -> int:
-    return int(_lib.moe_align_workspace_bytes(numel, E))
+    return int(lib().moe_align_workspace_bytes(numel, E))
 
 
 # ----------------------------------------------------------------- entries --
 
-def moe_topk_softmax(logits: torch.Tensor, top_k: int, topk_ids=None, topk_weights=None):
+def moe_topk_softmax(logits: torch.Tensor, top_k: int, topk_ids=None, topk_weights=None,
+                     expert_bias: Optional[torch.Tensor] = None, scoring: str = "softmax",
+                     renormalize: bool = True):
     T, E = logits.shape
+    if scoring not in SCORING:
+        raise ValueError(f"moe_topk_softmax: scoring must be one of {sorted(SCORING)}")
     ids = _out(topk_ids, (T, top_k), torch.int32, logits, "topk_ids")
     w = _out(topk_weights, (T, top_k), torch.float32, logits, "topk_weights")
-    _call("moe_topk_softmax", _ptr(logits, torch.float32, "logits"), T, E, top_k,
-          _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_weights"), _stream(logits))
+    bias = None
+    if expert_bias is not None:
+        if tuple(expert_bias.shape) != (E,):
+            raise ValueError("moe_topk_softmax: expert_bias must be [E]")
+        bias = _ptr(expert_bias, torch.float32, "expert_bias")
+    _call("moe_topk_softmax", _ptr(logits, torch.float32, "logits"), bias, T, E, top_k, SCORING[scoring],
+          int(bool(renormalize)), _ptr(ids, torch.int32, "topk_ids"), _ptr(w, torch.float32, "topk_weights"),
+          _stream(logits))
     return ids, w
 
 

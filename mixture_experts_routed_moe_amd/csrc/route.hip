@@ -1,10 +1,12 @@
-// Top-k softmax routing: one wavefront per token.
+// Top-k routing: one wavefront per token.
 //
-// Each lane holds ceil(E/64) logits in registers. k rounds of a wave-wide
-// argmax (value, then lower expert id) pick the experts in descending order;
-// the selected logits stay in the lane that equals their slot, and the
-// renormalised weights are a softmax over those k logits, which equals the
-// full softmax divided by its top-k mass.
+// Each lane holds ceil(E/64) routing logits (router score plus the optional
+// per-expert bias) in registers. k rounds of a wave-wide argmax (value, then
+// lower expert id) pick the experts in descending order; the selected logits
+// stay in the lane that equals their slot. Scores: softmax over all E (the
+// sum over every lane's logits), or the logistic sigmoid of each logit;
+// renormalised weights divide by the selected experts' score sum, which for
+// softmax equals a softmax over the k selected logits.
 #include "moe_common.h"
 
 namespace {
@@ -18,10 +20,16 @@ __device__ __forceinline__ void better(float& bv, int& be, float ov, int oe) {
   }
 }
 
+__device__ __forceinline__ float wave_sum(float s) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
 template <int VPT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_softmax_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ weights) {
+    const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E, int k, int sigmoid,
+    int renormalize, int32_t* __restrict__ ids, float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
@@ -31,7 +39,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_softmax_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -INFINITY;
+    v[i] = e < E ? (bias ? row[e] + bias[e] : row[e]) : -INFINITY;
   }
   uint32_t taken = 0;
   float my_v = -INFINITY;
@@ -58,41 +66,63 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_softmax_kernel(
     }
     if (j == 0) top_v = bv;
   }
-  // softmax over the k selected logits (max is the first one)
-  const float ex = lane < k ? expf(my_v - top_v) : 0.0f;
-  float s = ex;
+  float score, denom;
+  if (sigmoid) {
+    score = lane < k ? 1.0f / (1.0f + expf(-my_v)) : 0.0f;
+    denom = renormalize ? wave_sum(score) : 1.0f;
+  } else {
+    // the first selected logit is the maximum over all E
+    score = lane < k ? expf(my_v - top_v) : 0.0f;
+    if (renormalize) {
+      denom = wave_sum(score);
+    } else {
+      float s = 0.0f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      for (int i = 0; i < VPT; ++i)
+        if (lane + 64 * i < E) s += expf(v[i] - top_v);
+      denom = wave_sum(s);
+    }
+  }
   if (lane < k) {
     ids[t * k + lane] = my_e;
-    weights[t * k + lane] = ex / s;
+    weights[t * k + lane] = score / denom;
   }
 }
 
 }  // namespace
 
-extern "C" int moe_topk_softmax(const float* logits, int64_t T, int E, int top_k, int32_t* topk_ids,
-                                float* topk_weights, hipStream_t stream) {
+extern "C" int moe_topk_softmax(const float* logits, const float* expert_bias, int64_t T, int E, int top_k,
+                                int scoring, int renormalize, int32_t* topk_ids, float* topk_weights,
+                                hipStream_t stream) {
   using namespace moe;
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_topk_softmax: T < 0");
   if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_topk_softmax: E=%d not in [1,1024]", E);
   if (top_k < 1 || top_k > 16 || top_k > E)
     return fail(MOE_ERR_UNSUPPORTED, "moe_topk_softmax: top_k=%d not in [1,min(E,16)]", top_k);
+  if (scoring != MOE_SCORING_SOFTMAX && scoring != MOE_SCORING_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "moe_topk_softmax: scoring=%d", scoring);
+  if (renormalize != 0 && renormalize != 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_topk_softmax: renormalize=%d not 0 or 1", renormalize);
   if (T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_weights) return fail(MOE_ERR_INVALID_ARG, "moe_topk_softmax: null pointer");
   const int64_t blocks = ceil_div(T, kWavesPerBlock);
   if (blocks > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "moe_topk_softmax: T too large");
   const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kWavesPerBlock);
   const int vpt = (E + 63) / 64;
+  const int sig = scoring == MOE_SCORING_SIGMOID;
+#define MOE_ROUTE_LAUNCH(V)                                                                                   \
+  topk_softmax_kernel<V><<<grid, block, 0, stream>>>(logits, expert_bias, T, E, top_k, sig, renormalize, topk_ids, \
+                                                     topk_weights)
   if (vpt <= 1)
-    topk_softmax_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, top_k, topk_ids, topk_weights);
+    MOE_ROUTE_LAUNCH(1);
   else if (vpt <= 2)
-    topk_softmax_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, top_k, topk_ids, topk_weights);
+    MOE_ROUTE_LAUNCH(2);
   else if (vpt <= 4)
-    topk_softmax_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, top_k, topk_ids, topk_weights);
+    MOE_ROUTE_LAUNCH(4);
   else if (vpt <= 8)
-    topk_softmax_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, top_k, topk_ids, topk_weights);
+    MOE_ROUTE_LAUNCH(8);
   else
-    topk_softmax_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, top_k, topk_ids, topk_weights);
+    MOE_ROUTE_LAUNCH(16);
+#undef MOE_ROUTE_LAUNCH
   return check_launch("moe_topk_softmax");
 }

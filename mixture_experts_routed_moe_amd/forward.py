@@ -64,8 +64,18 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
                        padding_m: int = 128, block_m: int = 128,
                        shared_w_gate_up: Optional[torch.Tensor] = None,
                        shared_w_down: Optional[torch.Tensor] = None,
-                       fuse_swiglu: bool = True, buffers: Optional[MoEBuffers] = None) -> torch.Tensor:
-    """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden))."""
+                       fuse_swiglu: bool = True, buffers: Optional[MoEBuffers] = None,
+                       expert_bias: Optional[torch.Tensor] = None, scoring: str = "softmax",
+                       renormalize: bool = True, return_parts: bool = False):
+    """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden)).
+
+    With return_parts=True returns (shared_out, routed_out) instead, the split
+    of TileOPs #778 "Partial output contract": shared_out [T, H] bf16 (None
+    without a shared expert) and routed_out the routed sum alone; the caller
+    adds them (after its all-reduce of shared_out when the shared expert is
+    tensor-parallel). Otherwise the shared output is added inside the
+    unpermute before its single rounding.
+    """
     T, H = hidden.shape
     E, twoF, H2 = w_gate_up.shape
     F = twoF // 2
@@ -79,7 +89,7 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     elif dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu:
         raise ValueError("routed_moe_forward: buffers were made for another shape")
 
-    _lib.moe_topk_softmax(router_logits, top_k, b.topk_ids, b.topk_weights)
+    _lib.moe_topk_softmax(router_logits, top_k, b.topk_ids, b.topk_weights, expert_bias, scoring, renormalize)
     tb = _lib.moe_align(b.topk_ids, E, padding_m, block_m, b.tables)
     _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm)
     if fuse_swiglu:
@@ -97,6 +107,9 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
             _lib.swiglu(b.shared_gate_up, b.shared_h)
         _lib.grouped_gemm_down(b.shared_h, shared_w_down, None, padding_m, block_m, b.shared_y)
         addend = b.shared_y
+    if return_parts:
+        _lib.moe_unpermute(b.y, tb["pair_to_row"], b.topk_weights, routed_scaling_factor, None, b.out)
+        return addend, b.out
     _lib.moe_unpermute(b.y, tb["pair_to_row"], b.topk_weights, routed_scaling_factor, addend, b.out)
     return b.out
 

@@ -131,8 +131,8 @@ TAG_HIDDEN, TAG_LOGITS, TAG_BIAS, TAG_WGU, TAG_WD, TAG_SWGU, TAG_SWD, TAG_QUANT 
 class MoEConfig:
     """One routed-expert forward workload.
 
-    hidden [T,H] bf16 ~N(0,1); router logits [T,E] fp32 ~N(0,1) (+ a per-expert
-    Zipf bias when `zipf_s` is set); w_gate_up [E,2F,H] bf16 ~N(0,1/H) with the
+    hidden [T,H] bf16 ~N(0,1); router logits [T,E] fp32 ~N(0,1), plus a per-expert
+    Zipf bias [E] (expert_bias) when `zipf_s` is set; w_gate_up [E,2F,H] bf16 ~N(0,1/H) with the
     gate rows first; w_down [E,H,F] bf16 ~N(0,1/F); optional shared expert
     w_gate_up [2Fs,H] ~N(0,1/H), w_down [H,Fs] ~N(0,1/Fs).
     """
@@ -191,11 +191,14 @@ def hidden(cfg: MoEConfig, device="cpu", rows: Optional[slice] = None) -> torch.
 
 def router_logits(cfg: MoEConfig, device="cpu", rows: Optional[slice] = None) -> torch.Tensor:
     r0, r1 = (0, cfg.T) if rows is None else (rows.start, rows.stop)
-    z = normal_f32(tensor_key(cfg.cid, TAG_LOGITS), (r1 - r0, cfg.E), 1.0, device,
-                   start=r0 * cfg.E)
-    if cfg.zipf_s is not None:
-        z = z + torch.from_numpy(zipf_bias(cfg)).to(device)
-    return z
+    return normal_f32(tensor_key(cfg.cid, TAG_LOGITS), (r1 - r0, cfg.E), 1.0, device, start=r0 * cfg.E)
+
+
+def expert_bias(cfg: MoEConfig, device="cpu") -> Optional[torch.Tensor]:
+    """The per-expert Zipf bias [E] float32 of a skewed workload (None without one)."""
+    if cfg.zipf_s is None:
+        return None
+    return torch.from_numpy(zipf_bias(cfg)).to(device)
 
 
 def w_gate_up(cfg: MoEConfig, device="cpu", experts: Optional[Sequence[int]] = None) -> torch.Tensor:

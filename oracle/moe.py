@@ -3,7 +3,8 @@
 Test infrastructure only (see oracle/__init__.py). Each function restates one
 step as the pages define it, in the order they give:
 
-  route             softmax over the router logits, top-k, weights renormalised
+  route             router logits (+ bias) scored by softmax or sigmoid, top-k, weights
+                    renormalised or not
   dispatch_tables   group_sizes / group_offsets / group_padded_offsets /
                     group_idx_for_bx and the expert-major permutation
   block_decode      the kernel-side row recovery of one row block
@@ -32,32 +33,45 @@ from .numerics import bf16_to_f32, bf16_to_f64, silu32, to_bf16
 
 # ------------------------------------------------------------------ route --
 
-def route(logits: np.ndarray, top_k: int):
-    """Top-k softmax routing with renormalised weights.
+def route(logits: np.ndarray, top_k: int, bias: Optional[np.ndarray] = None, scoring: str = "softmax",
+          renormalize: bool = True):
+    """Top-k routing.
 
     The op's routing input is a [T, E] score tensor ("gating" in the call of
     TileOPs #778, "Partial output contract"); the tutorial's example routes
     every token to top_k experts ("Example 07 ... expected output"). The
-    workload description fixes softmax -> top-k -> renormalise.
+    workload description fixes softmax -> top-k -> renormalise; TileOPs #778's
+    Kimi-K2 benchmark names sigmoid routing.
 
-    Selection: experts ordered by descending fp32 logit, ties to the lower
-    expert id; slot j holds the j-th expert of that order. Weights: the full
-    softmax p over all E experts in float64, then p_sel / sum(p_sel), stored
-    as float32.
+    Routing logit v = logits + bias, one float32 addition (bias is the
+    per-expert skew of the DeepSeek-V3-shaped workload; the pages give no
+    formula, so it enters selection and scoring alike). Selection: experts
+    ordered by descending v, ties to the lower expert id; slot j holds the
+    j-th expert of that order. Scores, in float64: softmax of v over all E,
+    or the logistic sigmoid of each v. Weights: the selected scores divided by
+    their sum (renormalize) or the scores themselves; stored as float32.
     """
     v = np.asarray(logits, dtype=np.float32)
     T, E = v.shape
     if not (1 <= top_k <= E):
         raise ValueError("top_k out of range")
+    if bias is not None:
+        v = (v + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
     # stable argsort of -v: equal logits keep ascending expert id
     order = np.argsort(-v, axis=1, kind="stable")
     ids = order[:, :top_k].astype(np.int32)
     v64 = v.astype(np.float64)
-    ex = np.exp(v64 - v64.max(axis=1, keepdims=True))
-    p = ex / ex.sum(axis=1, keepdims=True)
+    if scoring == "softmax":
+        ex = np.exp(v64 - v64.max(axis=1, keepdims=True))
+        p = ex / ex.sum(axis=1, keepdims=True)
+    elif scoring == "sigmoid":
+        p = 1.0 / (1.0 + np.exp(-v64))
+    else:
+        raise ValueError("scoring must be 'softmax' or 'sigmoid'")
     p_sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    w = (p_sel / p_sel.sum(axis=1, keepdims=True)).astype(np.float32)
-    return ids, w
+    if renormalize:
+        p_sel = p_sel / p_sel.sum(axis=1, keepdims=True)
+    return ids, p_sel.astype(np.float32)
 
 
 # -------------------------------------------------------- dispatch tables --
@@ -258,7 +272,8 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, w_gate_up_bits: np.ndar
             w_down_bits: np.ndarray, top_k: int, routed_scaling_factor: float = 1.0,
             padding_m: int = 128, block_m: int = 128,
             shared_w_gate_up_bits: Optional[np.ndarray] = None,
-            shared_w_down_bits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+            shared_w_down_bits: Optional[np.ndarray] = None, bias: Optional[np.ndarray] = None,
+            scoring: str = "softmax", renormalize: bool = True) -> Dict[str, np.ndarray]:
     """The whole routed (+ shared) forward; returns every intermediate.
 
     Order as the TileOPs pipeline runs it (#1580 "Grouped-GEMM kernel" and
@@ -268,7 +283,7 @@ def forward(hidden_bits: np.ndarray, logits: np.ndarray, w_gate_up_bits: np.ndar
     """
     E, twoF, H = w_gate_up_bits.shape
     F = twoF // 2
-    ids, w = route(logits, top_k)
+    ids, w = route(logits, top_k, bias, scoring, renormalize)
     tab = dispatch_tables(ids, E, padding_m, block_m)
     x_perm = permute(hidden_bits, tab["sorted_pair"], top_k)
     gu = grouped_gemm(x_perm, w_gate_up_bits, tab["group_sizes"], tab["group_offsets"])

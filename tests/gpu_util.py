@@ -50,6 +50,8 @@ def inputs(cfg, device):
         "w_gate_up": moe_synth.w_gate_up(cfg, device),
         "w_down": moe_synth.w_down(cfg, device),
     }
+    if cfg.zipf_s is not None:
+        d["bias"] = moe_synth.expert_bias(cfg, device)
     if cfg.shared_F:
         d["shared_w_gate_up"] = moe_synth.shared_w_gate_up(cfg, device)
         d["shared_w_down"] = moe_synth.shared_w_down(cfg, device)
@@ -66,7 +68,7 @@ def oracle_tokens(cfg, inp, tokens):
     tokens = np.asarray(tokens)
     hid = bits(inp["hidden"][torch.as_tensor(tokens, device=inp["hidden"].device)])
     logits = host(inp["logits"][torch.as_tensor(tokens, device=inp["logits"].device)])
-    ids, w = oracle.route(logits, cfg.top_k)
+    ids, w = oracle.route(logits, cfg.top_k, host(inp["bias"]) if "bias" in inp else None)
     used = np.unique(ids)
     remap = {int(e): i for i, e in enumerate(used)}
     ids_r = np.vectorize(lambda e: remap[int(e)])(ids).astype(np.int32)
@@ -82,4 +84,5 @@ def oracle_tokens(cfg, inp, tokens):
     if cfg.shared_F:
         shared = oracle.shared_expert(hid, bits(inp["shared_w_gate_up"]), bits(inp["shared_w_down"]))
     out = oracle.unpermute(y, tab["pair_to_row"], w, cfg.top_k, cfg.rsf, shared)
-    return {"topk_ids": ids, "topk_weights": w, "out": out, "shared": shared}
+    routed = oracle.unpermute(y, tab["pair_to_row"], w, cfg.top_k, cfg.rsf, None)
+    return {"topk_ids": ids, "topk_weights": w, "out": out, "shared": shared, "routed": routed}

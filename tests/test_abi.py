@@ -61,7 +61,7 @@ def test_num_blocks_matches_worked_example(lib):
     assert lib.moe_num_blocks(100, 3, 64, 128) == 2 + 6
     assert lib.moe_num_blocks(10, 3, 64, 96) == -1
     assert lib.moe_num_blocks(0, 8, 64, 64) == 8
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_workspace_size(lib):
@@ -90,9 +90,13 @@ def test_argument_errors_return_before_launch(lib):
     assert lib.swiglu_quant_fp8(None, 4, 100, None, None, None, None, None) == -1
     assert lib.swiglu_quant_fp8(None, 0, 256, None, None, None, None, None) == 0
     # routing limits
-    lib.moe_topk_softmax.argtypes = [P, c.c_int64, c.c_int, c.c_int, P, P, P]
-    assert lib.moe_topk_softmax(None, 4, 2048, 8, None, None, None) == -2
-    assert lib.moe_topk_softmax(None, 4, 8, 9, None, None, None) == -2
+    lib.moe_topk_softmax.argtypes = [P, P, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int, P, P, P]
+    assert lib.moe_topk_softmax(None, None, 4, 2048, 8, 0, 1, None, None, None) == -2
+    assert lib.moe_topk_softmax(None, None, 4, 8, 9, 0, 1, None, None, None) == -2
+    assert lib.moe_topk_softmax(None, None, 4, 8, 2, 2, 1, None, None, None) == -1   # unknown scoring
+    assert lib.moe_topk_softmax(None, None, 4, 8, 2, 1, 3, None, None, None) == -1   # renormalize not 0/1
+    assert lib.moe_topk_softmax(None, None, 0, 8, 2, 1, 0, None, None, None) == 0    # T = 0: nothing to do
+    assert lib.moe_topk_softmax(None, None, 4, 8, 2, 0, 1, None, None, None) == -1   # null pointers
     # unpermute aliasing and null pointers
     lib.moe_unpermute.argtypes = [P, P, P, c.c_int64, c.c_int, c.c_int, c.c_float, P, P, P]
     assert lib.moe_unpermute(None, None, None, 4, 2, 16, 1.0, None, None, None) == -1

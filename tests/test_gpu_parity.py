@@ -55,8 +55,9 @@ def test_route(name):
     cfg = moe_synth.CONFIGS[name]
     say("route", name)
     logits = moe_synth.router_logits(cfg, d)
-    ids, w = mx.moe_topk_softmax(logits, cfg.top_k)
-    rid, rw = oracle.route(host(logits), cfg.top_k)
+    bias = moe_synth.expert_bias(cfg, d)
+    ids, w = mx.moe_topk_softmax(logits, cfg.top_k, expert_bias=bias)
+    rid, rw = oracle.route(host(logits), cfg.top_k, None if bias is None else host(bias))
     assert np.array_equal(host(ids), rid)
     np.testing.assert_allclose(host(w), rw, rtol=2e-6, atol=1e-7)
 
@@ -70,6 +71,21 @@ def test_route_ties_and_small_shapes():
         rid, rw = oracle.route(logits, k)
         assert np.array_equal(host(ids), rid), (T, E, k)
         np.testing.assert_allclose(host(w), rw, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_route_scoring_bias_renormalize(scoring, renormalize):
+    d = dev()
+    rng = np.random.default_rng(11)
+    for T, E, k in [(300, 384, 8), (77, 64, 6), (5, 1000, 16)]:
+        logits = (rng.standard_normal((T, E)) * 1.5).astype(np.float32)
+        for bias in (None, (rng.standard_normal(E) * 2).astype(np.float32)):
+            ids, w = mx.moe_topk_softmax(_t(logits, d), k, expert_bias=None if bias is None else _t(bias, d),
+                                         scoring=scoring, renormalize=renormalize)
+            rid, rw = oracle.route(logits, k, bias, scoring, renormalize)
+            assert np.array_equal(host(ids), rid), (T, E, k, bias is None)
+            np.testing.assert_allclose(host(w), rw, rtol=2e-6, atol=1e-7)
 
 
 # ------------------------------------------------------------ dispatch --
@@ -87,7 +103,8 @@ def _align_cases(golden_dir):
     yield "E1000", np.stack([rng.permutation(1000)[:8] for _ in range(2100)]).astype(np.int32), 1000, 32, 32
     for name in ("tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"):
         cfg = moe_synth.CONFIGS[name]
-        ids, _ = oracle.route(moe_synth.router_logits(cfg).numpy(), cfg.top_k)
+        bias = moe_synth.expert_bias(cfg)
+        ids, _ = oracle.route(moe_synth.router_logits(cfg).numpy(), cfg.top_k, None if bias is None else bias.numpy())
         yield name, ids, cfg.E, cfg.padding_m, cfg.block_m
 
 
@@ -106,7 +123,8 @@ def test_align_tables_bit_exact(golden_dir):
 def test_align_deterministic():
     d = dev()
     cfg = moe_synth.CONFIGS["dsv3_prefill"]
-    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k)
+    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k,
+                                 expert_bias=moe_synth.expert_bias(cfg, d))
     a = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
     b = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
     for key in ("sorted_pair", "pair_to_row", "group_idx_for_bx"):
@@ -120,7 +138,8 @@ def test_permute(name):
     d = dev()
     cfg = moe_synth.CONFIGS[name]
     hid = moe_synth.hidden(cfg, d)
-    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k)
+    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k,
+                                 expert_bias=moe_synth.expert_bias(cfg, d))
     tb = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
     xp = mx.moe_permute(hid, tb["sorted_pair"], cfg.top_k)
     ref = oracle.permute(bits(hid), host(tb["sorted_pair"]), cfg.top_k)
@@ -346,10 +365,10 @@ def test_swiglu_quant_full_size_sampled_blocks():
 
 # ----------------------------------------------------------- end to end --
 
-def _gpu_forward(cfg, inp, fuse=True):
+def _gpu_forward(cfg, inp, fuse=True, **kw):
     return mx.routed_moe_forward(inp["hidden"], inp["logits"], inp["w_gate_up"], inp["w_down"], cfg.top_k,
                                  cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"),
-                                 inp.get("shared_w_down"), fuse_swiglu=fuse)
+                                 inp.get("shared_w_down"), fuse_swiglu=fuse, expert_bias=inp.get("bias"), **kw)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3_decode"])
@@ -360,6 +379,7 @@ def test_forward_full_oracle(name):
     inp = inputs(cfg, d)
     ref = oracle.forward(bits(inp["hidden"]), host(inp["logits"]), bits(inp["w_gate_up"]), bits(inp["w_down"]),
                          cfg.top_k, cfg.rsf, cfg.padding_m, cfg.block_m)
+    assert "bias" not in inp
     for fuse in (True, False):
         out = _gpu_forward(cfg, inp, fuse)
         err = assert_bf16_close(bits(out), ref["out"], f"{name} out fuse={fuse}")
@@ -374,13 +394,11 @@ def test_forward_full_size_sampled_tokens(name):
     inp = inputs(cfg, d)
     bufs = mx.MoEBuffers(mx.MoEShape(cfg.T, cfg.H, cfg.F, cfg.E, cfg.top_k, cfg.padding_m, cfg.block_m,
                                      cfg.shared_F), d)
-    out = mx.routed_moe_forward(inp["hidden"], inp["logits"], inp["w_gate_up"], inp["w_down"], cfg.top_k,
-                                cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"),
-                                inp.get("shared_w_down"), buffers=bufs)
+    out = _gpu_forward(cfg, inp, buffers=bufs)
     torch.cuda.synchronize()
     # full-size tables against the oracle's
     ids = host(bufs.topk_ids)
-    ref_ids, _ = oracle.route(host(inp["logits"]), cfg.top_k)
+    ref_ids, _ = oracle.route(host(inp["logits"]), cfg.top_k, host(inp["bias"]) if "bias" in inp else None)
     assert np.array_equal(ids, ref_ids)
     ref_tab = oracle.dispatch_tables(ref_ids, cfg.E, cfg.padding_m, cfg.block_m)
     for key in ("group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx", "sorted_pair",
@@ -394,7 +412,11 @@ def test_forward_full_size_sampled_tokens(name):
     if cfg.shared_F:
         assert_bf16_close(bits(bufs.shared_y[torch.as_tensor(tokens, device=d)]), ref["shared"], "shared")
     # determinism: a second forward gives the same bytes
-    out2 = mx.routed_moe_forward(inp["hidden"], inp["logits"], inp["w_gate_up"], inp["w_down"], cfg.top_k,
-                                 cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"),
-                                 inp.get("shared_w_down"))
+    out2 = _gpu_forward(cfg, inp)
     assert torch.equal(out, out2)
+    if cfg.shared_F:
+        # the split of the partial-output contract: shared part and routed part, added by the caller
+        shared, routed = _gpu_forward(cfg, inp, return_parts=True)
+        assert torch.equal(shared, bufs.shared_y)
+        sel = torch.as_tensor(tokens, device=d)
+        assert_bf16_close(bits(routed[sel]), ref["routed"], f"{name} routed part")

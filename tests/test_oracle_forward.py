@@ -77,9 +77,9 @@ def test_swiglu_closed_forms():
     np.testing.assert_allclose(h3, gf / (1 + np.exp(-gf)) * uf, rtol=2 ** -8, atol=1e-30)
 
 
-def _per_token_forward(hid, logits, wgu, wd, k, rsf, shared=None):
+def _per_token_forward(hid, logits, wgu, wd, k, rsf, shared=None, bias=None):
     """Token by token: no tables, no permutation, same rounding points."""
-    ids, w = oracle.route(logits, k)
+    ids, w = oracle.route(logits, k, bias)
     T, H = hid.shape
     F = wd.shape[2]
     out = np.zeros((T, H), np.uint16)
@@ -119,10 +119,11 @@ def test_forward_with_shared_expert_and_skew():
     cfg = moe_synth.MoEConfig(90, "tiny_shared", T=24, H=64, F=128, E=16, top_k=4, padding_m=32,
                               block_m=16, rsf=2.827, zipf_s=1.1, shared_F=128)
     hid, logits, wgu, wd = _tiny_inputs(cfg)
+    bias = moe_synth.expert_bias(cfg).numpy()
     swgu = moe_synth.bits16(moe_synth.shared_w_gate_up(cfg))
     swd = moe_synth.bits16(moe_synth.shared_w_down(cfg))
     res = oracle.forward(hid, logits, wgu, wd, cfg.top_k, cfg.rsf, cfg.padding_m, cfg.block_m,
-                         swgu, swd)
+                         swgu, swd, bias=bias)
     # shared expert per token, by the same no-table route
     x = nm.bf16_to_f64(hid)
     shared = np.zeros_like(hid)
@@ -132,7 +133,7 @@ def test_forward_with_shared_expert_and_skew():
                         nm.bf16_to_f32(gu[cfg.shared_F:])).astype(np.float32))
         shared[t] = nm.to_bf16(nm.bf16_to_f64(swd) @ nm.bf16_to_f64(h))
     assert np.array_equal(res["shared"], shared)
-    ref = _per_token_forward(hid, logits, wgu, wd, cfg.top_k, cfg.rsf, shared)
+    ref = _per_token_forward(hid, logits, wgu, wd, cfg.top_k, cfg.rsf, shared, bias)
     assert np.array_equal(res["out"], ref)
     assert (res["group_sizes"] == 0).any()          # the skew leaves some experts empty
 

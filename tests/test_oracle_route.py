@@ -54,3 +54,46 @@ def test_renormalisation_drops_other_experts():
         assert ids.tolist() == [[0, 1]]
         np.testing.assert_allclose(w, w0, rtol=1e-7)
     np.testing.assert_allclose(w0[0, 0], 1 / (1 + math.exp(-2.0)), rtol=1e-7)
+
+
+def test_unnormalised_softmax_is_the_full_softmax():
+    # scipy's softmax over all E experts, read at the selected slots
+    from scipy.special import softmax
+    rng = np.random.default_rng(21)
+    logits = (rng.standard_normal((11, 40)) * 3).astype(np.float32)
+    ids, w = oracle.route(logits, 5, renormalize=False)
+    full = softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(full, ids.astype(np.int64), axis=1), rtol=2e-7)
+    assert (w.sum(axis=1) < 1).all()
+
+
+def test_sigmoid_scores_brute_force():
+    rng = np.random.default_rng(22)
+    logits = (rng.standard_normal((9, 24)) * 2).astype(np.float32)
+    for renorm in (False, True):
+        ids, w = oracle.route(logits, 4, scoring="sigmoid", renormalize=renorm)
+        for t in range(logits.shape[0]):
+            order, _ = _brute(logits[t], 4)
+            assert ids[t].tolist() == order
+            s = [1.0 / (1.0 + math.exp(-float(logits[t, e]))) for e in order]
+            ref = [x / math.fsum(s) for x in s] if renorm else s
+            np.testing.assert_allclose(w[t], ref, rtol=2e-7)
+
+
+def test_bias_shifts_selection_and_scores():
+    # the bias is one float32 addition to the logits; a large bias forces its
+    # expert into slot 0 and a very negative one keeps it out
+    rng = np.random.default_rng(23)
+    logits = rng.standard_normal((6, 10)).astype(np.float32)
+    bias = np.zeros(10, np.float32)
+    bias[7], bias[2] = 50.0, -50.0
+    ids, w = oracle.route(logits, 3, bias)
+    assert (ids[:, 0] == 7).all() and not (ids == 2).any()
+    for t in range(6):
+        v = [float(np.float32(logits[t, e]) + np.float32(bias[e])) for e in range(10)]
+        order, ww = _brute(np.array(v, np.float32), 3)
+        assert ids[t].tolist() == order
+        np.testing.assert_allclose(w[t], ww, rtol=2e-7)
+    # float32 rounding of the sum decides ties: 1 + 2^-24 rounds to 1, so experts 0 and 1 tie
+    ids, _ = oracle.route(np.array([[1.0, 1.0]], np.float32), 1, np.array([0.0, 2.0 ** -24], np.float32))
+    assert ids.tolist() == [[0]]
