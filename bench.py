@@ -180,12 +180,13 @@ def main():
     qM, qF = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
     for _ in range(5):
         mx.swiglu_quant_fp8(qx, qbufs)
-    # its working set (about 0.4 GB) is under twice the 256 MiB MALL: a 512 MiB
-    # write outside the events evicts it between launches
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # its working set (about 0.4 GB) is under twice the 256 MiB MALL: reading a
+    # 512 MiB buffer outside the events evicts it between launches (a read, so
+    # the timed launch does not also pay for writing dirty flush lines back)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
     qev = []
     for i in range(max(20, args.steps)):
-        flush.fill_(i & 0xFF)
+        flush.sum()
         a = ev()
         mx.swiglu_quant_fp8(qx, qbufs)
         qev.append((a, ev()))

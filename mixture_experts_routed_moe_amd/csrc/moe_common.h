@@ -83,4 +83,54 @@ __device__ __forceinline__ uint16_t swiglu_bf16(uint16_t gate, uint16_t up) {
   return f32_to_bf16(s * bf16_to_f32(up));
 }
 
+// ------------------------------------------------ SiLU lookup in LDS --
+// The gate input of every SwiGLU is bf16, so silu_spec(g) has 2^16 possible
+// arguments. A table of the 2 * 32 * 128 = 8192 values with |g| in
+// [2^-25, 128) (bf16 exponent field 102..133, both signs), plus 128 values for
+// the mantissas of g in [-256, -128), gives silu_spec(g) for every finite g:
+//   |g| < 2^-25: exp(-g) rounds to exactly 1, so silu = g / 2;
+//   g >= 128:    1 + exp(-g) rounds to 1, so silu = g;
+//   g <= -128:   the exponent argument saturates at 88, silu = g / D for one
+//                constant D, which scales exactly with powers of two of g
+//                (the results stay normal), so the [-256, -128) entry times
+//                2^(exponent - 134) is exact.
+// Every entry is computed with silu_spec itself, so a lookup returns the same
+// bits as the direct evaluation.
+constexpr int kSiluTabE0 = 102;                          // bf16 exponent field of 2^-25
+constexpr int kSiluTabMid = 2 * 32 * 128;
+constexpr int kSiluTabSize = kSiluTabMid + 128;
+
+// Entry i of the table.
+__device__ __forceinline__ float silu_table_entry(int i) {
+  uint32_t b;
+  if (i < kSiluTabMid)
+    b = (static_cast<uint32_t>(i >> 12) << 15) | (static_cast<uint32_t>(((i >> 7) & 31) + kSiluTabE0) << 7) |
+        static_cast<uint32_t>(i & 127);
+  else
+    b = 0x8000u | (134u << 7) | static_cast<uint32_t>(i - kSiluTabMid);
+  return silu_spec(bf16_to_f32(static_cast<uint16_t>(b)));
+}
+
+// silu_spec of a bf16 gate (bits in the low 16 bits of gb), from the table.
+// Written with bit masks rather than branches: every lane takes the same
+// instructions, and no per-element condition has to stay live.
+__device__ __forceinline__ float silu_lookup(const float* tab, uint32_t gb) {
+  const uint32_t e = (gb >> 7) & 0xFFu;
+  const uint32_t k = e - kSiluTabE0;                                  // wraps for e < kSiluTabE0
+  const uint32_t mid = 0u - static_cast<uint32_t>(k < 32u);           // all ones inside the table range
+  const uint32_t idx_mid = ((gb >> 3) & 0x1000u) | ((k & 31u) << 7) | (gb & 127u);
+  const uint32_t idx = (idx_mid & mid) | ((kSiluTabMid + (gb & 127u)) & ~mid);
+  const float t = tab[idx];
+  const float g = __uint_as_float(gb << 16);
+  const float big = (gb & 0x8000u) ? __builtin_ldexpf(t, static_cast<int>(e) - 134) : g;  // |g| >= 128
+  const float out = e < static_cast<uint32_t>(kSiluTabE0) ? g * 0.5f : big;
+  return __uint_as_float((__float_as_uint(t) & mid) | (__float_as_uint(out) & ~mid));
+}
+
+// bf16(silu(gate) * up), the same bits as swiglu_bf16, with the SiLU from the table.
+__device__ __forceinline__ uint16_t swiglu_bf16_tab(const float* tab, uint32_t gate, uint32_t up) {
+#pragma clang fp contract(off)
+  return f32_to_bf16(silu_lookup(tab, gate) * __uint_as_float(up << 16));
+}
+
 }  // namespace moe

@@ -1,17 +1,32 @@
 // SwiGLU and the fused SwiGLU + FP8 (OCP e4m3) activation quantizer.
 //
-// swiglu_quant_fp8: one workgroup per 128x128 block of h = SiLU(gate) * up.
-// Thread (rg, cg) of 16x16 owns rows rg*8..rg*8+7 and columns cg*8..cg*8+7
-// of the block, so
+// Both take every SiLU from a lookup table in LDS (a lookup and a few selects
+// instead of an exp polynomial and a divide), which moves them from ALU-bound
+// towards the HBM bound. Each call first runs silu_table_kernel, which writes
+// the 8320 exact silu_spec values of moe_common.h's table into the
+// file-scope array g_silu_tab; the kernels that follow on the same stream copy
+// it into LDS. The array holds constants: a call on another stream that
+// rewrites it concurrently writes the same bits, so no ordering between
+// streams is needed.
+//
+// swiglu_quant_fp8: one 512-thread workgroup per 128x128 block of
+// h = SiLU(gate) * up. Thread (rg, cg) of 32x16 owns rows rg*4..rg*4+3 and
+// columns cg*8..cg*8+7 of the block, so
 //   * gate/up loads are 16-byte vectors and a row's 16 threads read 256
 //     contiguous bytes of each half;
-//   * the 1x128 row amax is a reduction over the 16 lanes of a row (xor 1..8);
+//   * the 1x128 row amax is a reduction over the 16 lanes of a row (xor 1..8),
+//     on the bf16 magnitude bits with packed 16-bit max;
 //   * the 128x128 block amax adds a reduction over row groups and one LDS
-//     exchange between the four waves;
+//     exchange between the eight waves;
 //   * the row-layout store is 8 bytes per thread (a row's 128 bytes come
-//     from 16 consecutive lanes) and the transposed store is also 8 bytes
-//     per thread: a thread's 8 consecutive rows of one column are 8
-//     consecutive bytes of q_t, no LDS transpose needed.
+//     from 16 consecutive lanes); the transposed codes are gathered in LDS
+//     (in the table's space, free once the SiLUs are done) and written as
+//     16-byte pieces, eight lanes per 128-byte line of q_t;
+//   * codes are packed with the converter's half-word select, four per word
+//     without masks or shifts.
+// Measured: the block-per-workgroup shape with many workgroups in flight
+// beats persistent or multi-block workgroups that load the table once (their
+// lockstep phases leave HBM idle while they compute).
 // h never leaves registers. code = e4m3(RN32(h / s)): the quotient is taken
 // as RN32(h * RN64(1/s)) in fp64. That is the correctly rounded fp32
 // quotient: the fp64 product is within 2^-52 (relative) of h/s, while h/s
@@ -26,131 +41,256 @@ namespace {
 
 constexpr int kTile = 128;
 
-__device__ __forceinline__ float wave_max_xor(float v, int first, int last) {
-  for (int off = first; off <= last; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+__device__ __forceinline__ uint32_t wave_umax_xor(uint32_t v, int first, int last) {
+  for (int off = first; off <= last; off <<= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off)));
   return v;
 }
 
-// Two fp32 values -> two e4m3 bytes in the low half of the result.
-__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+// Two fp32 values -> two e4m3 bytes written into half `hi` of `old` (the
+// other half is kept).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2(float a, float b, uint32_t old) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), HI));
 }
 
-// Correctly rounded fp32 quotient h / s from a per-tile RN64(1/s).
-__device__ __forceinline__ float quotient(float h, double inv_s) {
-  return static_cast<float>(static_cast<double>(h) * inv_s);
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+
+// Two fp32 products rounded to bf16 (nearest even), packed low | high << 16.
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return static_cast<uint32_t>(moe::f32_to_bf16(lo)) | (static_cast<uint32_t>(moe::f32_to_bf16(hi)) << 16);
 }
+
+__device__ float g_silu_tab[moe::kSiluTabSize];
+
+__global__ __launch_bounds__(256) void silu_table_kernel() {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= moe::kSiluTabSize) return;
+  g_silu_tab[i] = moe::silu_table_entry(i);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kSiluTabPieces = moe::kSiluTabSize / 4;                   // 16-byte pieces
+constexpr int kSiluTabLds = (kSiluTabPieces + 63) / 64 * 64 * 4;        // floats: whole 64-piece loads
+static_assert(moe::kSiluTabSize % 4 == 0, "16-byte pieces");
+
+// Starts copying g_silu_tab into tab[kSiluTabLds] with direct-to-LDS loads
+// (no VGPRs); thread t of n, n a multiple of 64. A wave-wide load fills 64
+// consecutive pieces; in the last one, lanes past the table re-read its last
+// piece into the padding. The caller waits for the loads and barriers.
+__device__ __forceinline__ void load_silu_table(float* tab, int t, int n) {
+  const int lane = t & 63;
+  for (int c = (t >> 6) * 64; c < kSiluTabPieces; c += n) {
+    const int src = min(c + lane, kSiluTabPieces - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const float4*>(g_silu_tab) + src,
+                                     (lds_void_t*)(reinterpret_cast<float4*>(tab) + c), 16, 0, 0);
+  }
+}
+
+constexpr int kSwigluChunks = 4;   // 16-byte chunks per thread
 
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint4* __restrict__ gu, uint32_t total, uint32_t f8,
                                                      uint4* __restrict__ h) {
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
+  __shared__ __attribute__((aligned(16))) float tab[kSiluTabLds];
+  load_silu_table(tab, threadIdx.x, 256);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const uint32_t base = blockIdx.x * (256u * kSwigluChunks) + threadIdx.x;
+  uint4 g[kSwigluChunks], u[kSwigluChunks];
+#pragma unroll
+  for (int q = 0; q < kSwigluChunks; ++q) {
+    const uint32_t i = min(base + q * 256u, total - 1u);
     const uint32_t m = i / f8, c = i - m * f8;
-    const uint4 g = gu[static_cast<uint64_t>(m) * 2 * f8 + c];
-    const uint4 u = gu[static_cast<uint64_t>(m) * 2 * f8 + f8 + c];
-    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+    g[q] = gu[static_cast<uint64_t>(m) * 2 * f8 + c];
+    u[q] = gu[static_cast<uint64_t>(m) * 2 * f8 + f8 + c];
+  }
+#pragma unroll
+  for (int q = 0; q < kSwigluChunks; ++q) {
+    const uint32_t i = base + q * 256u;
+    if (i >= total) break;
+    const uint32_t gw[4] = {g[q].x, g[q].y, g[q].z, g[q].w};
+    const uint32_t uw[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
     uint32_t o[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint16_t lo = moe::swiglu_bf16(static_cast<uint16_t>(gw[k] & 0xFFFFu), static_cast<uint16_t>(uw[k] & 0xFFFFu));
-      const uint16_t hi = moe::swiglu_bf16(static_cast<uint16_t>(gw[k] >> 16), static_cast<uint16_t>(uw[k] >> 16));
-      o[k] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+      const uint32_t lo = moe::swiglu_bf16_tab(tab, gw[k] & 0xFFFFu, uw[k] & 0xFFFFu);
+      const uint32_t hi = moe::swiglu_bf16_tab(tab, gw[k] >> 16, uw[k] >> 16);
+      o[k] = lo | (hi << 16);
     }
     h[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
-__global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __restrict__ x, int M, int F,
-                                                           int m_pad, int n_fb, uint8_t* __restrict__ q_row,
-                                                           float* __restrict__ s_row, uint8_t* __restrict__ q_t,
-                                                           float* __restrict__ s_t) {
-  __shared__ float s_wmax[4];
-  const int fb = blockIdx.x % n_fb;
-  const int mb = blockIdx.x / n_fb;
+constexpr int kQuantThreads = 512;   // per 128x128 block: 32 row groups of 4 x 16 column groups of 8
+
+__global__ __launch_bounds__(kQuantThreads) void swiglu_quant_kernel(const uint16_t* __restrict__ x, int M, int F,
+                                                                     int m_pad, int n_fb, uint8_t* __restrict__ q_row,
+                                                                     float* __restrict__ s_row,
+                                                                     uint8_t* __restrict__ q_t,
+                                                                     float* __restrict__ s_t) {
+  // the SiLU table, and once the SiLUs are done the transposed codes of the block
+  __shared__ __attribute__((aligned(16))) float tab[kSiluTabLds];
+  __shared__ uint32_t s_wmax[kQuantThreads / 64];
+  static_assert(kSiluTabLds * 4 >= kTile * kTile, "the transposed block fits in the table's space");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = tid & 15, rg = tid >> 4;
+  const int fb = blockIdx.x % n_fb;
+  const int mb = blockIdx.x / n_fb;
   const int col0 = fb * kTile + cg * 8;
-  const int row0 = mb * kTile + rg * 8;
+  const int row0 = mb * kTile + rg * 4;
 
-  float h[8][8];
+  // all 8 loads first, rows past M read row M-1 (in bounds) and are masked
+  uint4 g[4], u[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = row0 + i;
-    if (m < M) {
-      const uint16_t* rp = x + static_cast<int64_t>(m) * 2 * F;
-      const uint4 g = *reinterpret_cast<const uint4*>(rp + col0);
-      const uint4 u = *reinterpret_cast<const uint4*>(rp + F + col0);
-      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-      const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+  for (int i = 0; i < 4; ++i) {
+    const int m = min(row0 + i, M - 1);
+    const uint16_t* rp = x + static_cast<int64_t>(m) * 2 * F;
+    g[i] = *reinterpret_cast<const uint4*>(rp + col0);
+    u[i] = *reinterpret_cast<const uint4*>(rp + F + col0);
+  }
+  load_silu_table(tab, tid, kQuantThreads);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // SwiGLU. Fast path: every gate of the wave is in the table's range (bf16
+  // magnitude bits in [0x3300, 0x4300), checked two at a time with packed
+  // 16-bit subtract and max), so a SiLU is one lookup at
+  // sign * 4096 + (magnitude - 0x3300). Otherwise the wave takes the general
+  // lookup (closed forms outside the range).
+  u16x2 worst = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) worst = __builtin_elementwise_max(worst, as_u16x2(gw[k] & 0x7FFF7FFFu) - u16x2{0x3300, 0x3300});
+  }
+  const bool fast = __ballot(max(worst.x, worst.y) >= 0x1000) == 0;
+
+  uint32_t hp[4][4];  // h as bf16 pairs: hp[i][k] holds columns 2k, 2k+1 of row i
+  if (fast) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+      const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        h[i][2 * k] = moe::bf16_to_f32(moe::swiglu_bf16(static_cast<uint16_t>(gw[k] & 0xFFFFu),
-                                                        static_cast<uint16_t>(uw[k] & 0xFFFFu)));
-        h[i][2 * k + 1] = moe::bf16_to_f32(moe::swiglu_bf16(static_cast<uint16_t>(gw[k] >> 16),
-                                                            static_cast<uint16_t>(uw[k] >> 16)));
+        const float s_lo = tab[((gw[k] >> 3) & 0x1000u) | ((gw[k] & 0x7FFFu) - 0x3300u)];
+        const float s_hi = tab[((gw[k] >> 19) & 0x1000u) | (((gw[k] >> 16) & 0x7FFFu) - 0x3300u)];
+        hp[i][k] = bf16_pair(s_lo * __uint_as_float(uw[k] << 16), s_hi * __uint_as_float(uw[k] & 0xFFFF0000u));
       }
-    } else {
+    }
+  } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[i][j] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+      const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        hp[i][k] = bf16_pair(moe::silu_lookup(tab, gw[k] & 0xFFFFu) * __uint_as_float(uw[k] << 16),
+                             moe::silu_lookup(tab, gw[k] >> 16) * __uint_as_float(uw[k] & 0xFFFF0000u));
     }
   }
-
-  // 1x128 row amax (16 lanes per row) and the 128x128 block amax
-  float amax_row[8];
-  float blk = 0.0f;
+  if ((mb + 1) * kTile > M) {
+    // rows past M (the last row block only) are zero
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float a = 0.0f;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(h[i][j]));
-    a = wave_max_xor(a, 1, 8);
-    amax_row[i] = a;
-    blk = fmaxf(blk, a);
+      for (int k = 0; k < 4; ++k) hp[i][k] = row0 + i < M ? hp[i][k] : 0u;
   }
-  blk = wave_max_xor(blk, 16, 32);
-  if (lane == 0) s_wmax[wave] = blk;
-  __syncthreads();
-  blk = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+  auto hv = [&](int i, int j) __attribute__((always_inline)) {
+    return __uint_as_float((j & 1) ? (hp[i][j >> 1] & 0xFFFF0000u) : (hp[i][j >> 1] << 16));
+  };
+
+  // 1x128 row amax (16 lanes per row) and the 128x128 block amax, on the
+  // bf16 magnitude bits (their integer order is the order of |h|)
+  float amax_row[4];
+  uint32_t blk_bits = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, as_u16x2(hp[i][k] & 0x7FFF7FFFu));
+    const uint32_t a = wave_umax_xor(max(static_cast<uint32_t>(m2.x), static_cast<uint32_t>(m2.y)), 1, 8);
+    amax_row[i] = __uint_as_float(a << 16);
+    blk_bits = max(blk_bits, a);
+  }
+  blk_bits = wave_umax_xor(blk_bits, 16, 32);
+  if (lane == 0) s_wmax[wave] = blk_bits;
+  __syncthreads();  // also: every SiLU lookup is done, the table's space is free
+  uint32_t bb = s_wmax[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; ++w) bb = max(bb, s_wmax[w]);
+  const float blk = __uint_as_float(bb << 16);
 
   // block (transposed) scale
   const float sb = blk / 448.0f;
   const double inv_sb = sb > 0.0f ? 1.0 / static_cast<double>(sb) : 0.0;
   if (tid == 0) s_t[static_cast<int64_t>(fb) * (m_pad / kTile) + mb] = sb;
 
-  // row layout: codes and scales
-  uint32_t qt[8][2];  // transposed codes: [column j][rows 0-3 | rows 4-7]
+  // codes: two rows at a time; each h is widened to fp64 once and divided
+  // by both scales. Row codes pack four per word; a column's four transposed
+  // codes (rows 0-3) fill its word, rows (0,1) in the low half, (2,3) high.
+  uint32_t qt[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) qt[j][0] = qt[j][1] = 0u;
+  for (int i = 0; i < 4; i += 2) {
+    float sr[2];
+    double inv_r[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = row0 + i;
-    const float s = amax_row[i] / 448.0f;
-    const double inv_s = s > 0.0f ? 1.0 / static_cast<double>(s) : 0.0;
-    uint32_t w0 = 0u, w1 = 0u;
-    if (s > 0.0f) {
-      w0 = e4m3x2(quotient(h[i][0], inv_s), quotient(h[i][1], inv_s)) |
-           (e4m3x2(quotient(h[i][2], inv_s), quotient(h[i][3], inv_s)) << 16);
-      w1 = e4m3x2(quotient(h[i][4], inv_s), quotient(h[i][5], inv_s)) |
-           (e4m3x2(quotient(h[i][6], inv_s), quotient(h[i][7], inv_s)) << 16);
+    for (int r = 0; r < 2; ++r) {
+      sr[r] = amax_row[i + r] / 448.0f;
+      inv_r[r] = sr[r] > 0.0f ? 1.0 / static_cast<double>(sr[r]) : 0.0;
     }
-    if (m < M) {
-      *reinterpret_cast<uint2*>(q_row + static_cast<int64_t>(m) * F + col0) = make_uint2(w0, w1);
-      if (cg == 0) s_row[static_cast<int64_t>(m) * n_fb + fb] = s;
-    }
-    if (sb > 0.0f) {
+    float qr[2][8];
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const uint32_t pr = e4m3x2(quotient(h[i][j], inv_sb), quotient(h[i][j + 1], inv_sb));
-        const int sh = (i & 3) * 8;
-        qt[j][i >> 2] |= (pr & 0xFFu) << sh;
-        qt[j + 1][i >> 2] |= (pr >> 8) << sh;
+    for (int j = 0; j < 8; ++j) {
+      const double d0 = static_cast<double>(hv(i, j)), d1 = static_cast<double>(hv(i + 1, j));
+      qr[0][j] = static_cast<float>(d0 * inv_r[0]);
+      qr[1][j] = static_cast<float>(d1 * inv_r[1]);
+      const float b0 = static_cast<float>(d0 * inv_sb), b1 = static_cast<float>(d1 * inv_sb);
+      if (i == 0)
+        qt[j] = fp8x2<false>(b0, b1, 0u);
+      else
+        qt[j] = fp8x2<true>(b0, b1, qt[j]);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int m = row0 + i + r;
+      uint32_t w0 = fp8x2<true>(qr[r][2], qr[r][3], fp8x2<false>(qr[r][0], qr[r][1], 0u));
+      uint32_t w1 = fp8x2<true>(qr[r][6], qr[r][7], fp8x2<false>(qr[r][4], qr[r][5], 0u));
+      // an all-zero row has scale 0 and codes 0 (a -0.0 would otherwise encode as 0x80)
+      w0 = sr[r] > 0.0f ? w0 : 0u;
+      w1 = sr[r] > 0.0f ? w1 : 0u;
+      if (m < M) {
+        *reinterpret_cast<uint2*>(q_row + static_cast<int64_t>(m) * F + col0) = make_uint2(w0, w1);
+        if (cg == 0) s_row[static_cast<int64_t>(m) * n_fb + fb] = sr[r];
       }
     }
   }
-  // transposed layout: column f = col0 + j, rows row0..row0+7 are 8 bytes
+  if (!(sb > 0.0f)) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<uint2*>(q_t + static_cast<int64_t>(col0 + j) * m_pad + row0) = make_uint2(qt[j][0], qt[j][1]);
+    for (int j = 0; j < 8; ++j) qt[j] = 0u;
+  }
+  // transposed layout through LDS: the block's column c is 128 bytes (its
+  // rows) of q_t row fb*128 + c; this thread's 4 rows of a column are 4 of
+  // them. Rows past M hold code 0, which is the required padding.
+  uint8_t* tq = reinterpret_cast<uint8_t*>(tab);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(tq + (cg * 8 + j) * kTile + rg * 4) = qt[j];
+  __syncthreads();
+  // then 16-byte pieces, eight lanes per q_t row: whole 128-byte lines
+#pragma unroll
+  for (int r = 0; r < (kTile * kTile / 16) / kQuantThreads; ++r) {
+    const int piece = tid + kQuantThreads * r;
+    const int c = piece >> 3, part = piece & 7;
+    *reinterpret_cast<uint4*>(q_t + static_cast<int64_t>(fb * kTile + c) * m_pad + mb * kTile + part * 16) =
+        *reinterpret_cast<const uint4*>(tq + c * kTile + part * 16);
+  }
+}
+
+int launch_silu_table(hipStream_t stream) {
+  silu_table_kernel<<<(moe::kSiluTabSize + 255) / 256, 256, 0, stream>>>();
+  return moe::check_launch("silu_table_kernel");
 }
 
 }  // namespace
@@ -161,10 +301,12 @@ extern "C" int swiglu(const uint16_t* gate_up, int64_t M, int F, uint16_t* h, hi
     return fail(MOE_ERR_INVALID_ARG, "swiglu: M=%lld F=%d (F must be a positive multiple of 8)", (long long)M, F);
   if (M == 0) return MOE_OK;
   const int64_t total = M * (F / 8);
-  if (total >= (int64_t(1) << 32)) return fail(MOE_ERR_UNSUPPORTED, "swiglu: M*F too large");
+  if (total >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "swiglu: M*F too large");
   if (!gate_up || !h) return fail(MOE_ERR_INVALID_ARG, "swiglu: null pointer");
   if (!aligned16(gate_up) || !aligned16(h)) return fail(MOE_ERR_INVALID_ARG, "swiglu: pointers not 16-byte aligned");
-  const int64_t blocks = std::min<int64_t>(ceil_div(total, 256), 256 * 64);
+  int rc = launch_silu_table(stream);
+  if (rc) return rc;
+  const int64_t blocks = ceil_div(total, 256 * kSwigluChunks);
   swiglu_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(reinterpret_cast<const uint4*>(gate_up),
                                                                    static_cast<uint32_t>(total),
                                                                    static_cast<uint32_t>(F / 8),
@@ -188,7 +330,9 @@ extern "C" int swiglu_quant_fp8(const uint16_t* gate_up, int64_t M, int F, uint8
   const int n_fb = F / kTile;
   const int64_t blocks = (m_pad / kTile) * n_fb;
   if (blocks > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "swiglu_quant_fp8: too many blocks");
-  swiglu_quant_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+  int rc = launch_silu_table(stream);
+  if (rc) return rc;
+  swiglu_quant_kernel<<<static_cast<unsigned>(blocks), kQuantThreads, 0, stream>>>(
       gate_up, static_cast<int>(M), F, static_cast<int>(m_pad), n_fb, q_row, s_row, q_t, s_t);
   return check_launch("swiglu_quant_fp8");
 }

@@ -111,3 +111,29 @@ def test_silu32_against_float64():
     assert nm.silu32(np.array([20.0, 64.0], np.float32)).tolist() == [20.0, 64.0]
     g = np.linspace(-6, 6, 1001).astype(np.float32)
     np.testing.assert_allclose(nm.silu32(-g), nm.silu32(g) - g, atol=2e-6)
+
+
+def test_silu_closed_forms_outside_the_middle_range():
+    """The SiLU specification reduces to closed forms outside |g| in [2^-25, 128):
+    exp(-g) rounds to exactly 1 below (silu = g/2), 1 + exp(-g) rounds to 1 for
+    g >= 128 (silu = g), and for g <= -128 the exponent argument saturates at 88,
+    so silu(g) = g / D for one constant D and scales exactly with powers of two
+    of g. Checked over every finite bf16 value (kernels that tabulate only the
+    middle range rely on these)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    e = (bits.astype(np.uint32) >> 7) & 0xFF
+    finite = e != 0xFF
+    g = nm.bf16_to_f32(bits)
+    s = nm.silu32(g)
+    tiny = finite & (e < 102)
+    assert np.array_equal(s[tiny].view(np.uint32), (g[tiny] * np.float32(0.5)).view(np.uint32))
+    pos_big = finite & (e >= 134) & (bits < 0x8000)
+    assert np.array_equal(s[pos_big].view(np.uint32), g[pos_big].view(np.uint32))
+    neg_big = finite & (e >= 134) & (bits >= 0x8000)
+    base = (bits[neg_big].astype(np.uint32) & 0x807F) | (134 << 7)        # same sign and mantissa, exponent of [128, 256)
+    s_base = nm.silu32(nm.bf16_to_f32(base.astype(np.uint16)))
+    scaled = np.ldexp(s_base, (e[neg_big].astype(np.int32) - 134)).astype(np.float32)
+    assert np.array_equal(s[neg_big].view(np.uint32), scaled.view(np.uint32))
+    # and the middle range is exactly what a table of 2 * 32 * 128 entries must hold
+    mid = finite & (e >= 102) & (e < 134)
+    assert mid.sum() == 2 * 32 * 128
