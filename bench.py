@@ -101,7 +101,7 @@ def main():
         tb = bufs.tables
         run("topk_softmax", lambda: mx.moe_topk_softmax(logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bias))
         run("align", lambda: mx.moe_align(bufs.topk_ids, cfg.E, cfg.padding_m, cfg.block_m, tb))
-        run("permute", lambda: mx.moe_permute(hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm))
+        run("permute", lambda: mx.moe_permute(hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm, tb["pair_to_row"]))
         if fuse:
             run("gate_up", lambda: mx.grouped_gemm_gate_up(bufs.x_perm, wgu, tb, cfg.padding_m, cfg.block_m,
                                                            True, bufs.h))

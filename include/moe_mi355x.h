@@ -113,9 +113,14 @@ int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_
 /* Token permute into the compact expert-major layout (TileOPs "MoePermuteAlignOp":
  * token routing for the grouped GEMM):
  *     x_perm[r, :] = hidden[sorted_pair[r] / top_k, :]
- * hidden [T, H] bf16, x_perm [T*top_k, H] bf16. H % 8 == 0. */
-int moe_permute(const uint16_t* hidden, const int32_t* sorted_pair, int64_t T, int top_k, int H,
-                uint16_t* x_perm, hipStream_t stream);
+ * equivalently x_perm[pair_to_row[p], :] = hidden[p / top_k, :].
+ * hidden [T, H] bf16, x_perm [T*top_k, H] bf16. H % 8 == 0.
+ * sorted_pair, pair_to_row: the two permutation tables of moe_align; either
+ * may be NULL (not both). With pair_to_row (and top_k <= 16) the copy runs
+ * token by token, reading each hidden row once; otherwise it gathers by
+ * sorted_pair. Both give the same bytes. */
+int moe_permute(const uint16_t* hidden, const int32_t* sorted_pair, const int32_t* pair_to_row, int64_t T,
+                int top_k, int H, uint16_t* x_perm, hipStream_t stream);
 
 /* Grouped GEMM for gate+up, C[e] = A[e] @ W[e]^T (TileOPs #1580, "Benchmark
  * results" and "Grouped-GEMM kernel"): A is the compact [numel, H] layout;

@@ -31,7 +31,7 @@ class MoeError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 SCORING = {"softmax": 0, "sigmoid": 1}
 
 
@@ -49,7 +49,7 @@ def _load() -> ctypes.CDLL:
         "moe_align_workspace_bytes": (SZ, [I64, I]),
         "moe_topk_softmax": (I, [P, P, I64, I, I, I, I, P, P, P]),
         "moe_align": (I, [P, I64, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
-        "moe_permute": (I, [P, P, I64, I, I, P, P]),
+        "moe_permute": (I, [P, P, P, I64, I, I, P, P]),
         "grouped_gemm_gate_up": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
         "swiglu": (I, [P, I64, I, P, P]),
         "grouped_gemm_down": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, P, P]),
@@ -170,11 +170,13 @@ def moe_align(topk_ids: torch.Tensor, E: int, padding_m: int, block_m: int,
     return tb
 
 
-def moe_permute(hidden: torch.Tensor, sorted_pair: torch.Tensor, top_k: int, out=None) -> torch.Tensor:
+def moe_permute(hidden: torch.Tensor, sorted_pair: Optional[torch.Tensor], top_k: int, out=None,
+                pair_to_row: Optional[torch.Tensor] = None) -> torch.Tensor:
     T, H = hidden.shape
     x = _out(out, (T * top_k, H), torch.bfloat16, hidden, "x_perm")
     _call("moe_permute", _ptr(hidden, torch.bfloat16, "hidden"), _ptr(sorted_pair, torch.int32, "sorted_pair"),
-          T, top_k, H, _ptr(x, torch.bfloat16, "x_perm"), _stream(hidden))
+          _ptr(pair_to_row, torch.int32, "pair_to_row"), T, top_k, H, _ptr(x, torch.bfloat16, "x_perm"),
+          _stream(hidden))
     return x
 
 

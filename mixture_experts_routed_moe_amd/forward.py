@@ -91,7 +91,7 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
 
     _lib.moe_topk_softmax(router_logits, top_k, b.topk_ids, b.topk_weights, expert_bias, scoring, renormalize)
     tb = _lib.moe_align(b.topk_ids, E, padding_m, block_m, b.tables)
-    _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm)
+    _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm, tb["pair_to_row"])
     if fuse_swiglu:
         _lib.grouped_gemm_gate_up(b.x_perm, w_gate_up, tb, padding_m, block_m, True, b.h)
     else:

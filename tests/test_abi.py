@@ -61,7 +61,7 @@ def test_num_blocks_matches_worked_example(lib):
     assert lib.moe_num_blocks(100, 3, 64, 128) == 2 + 6
     assert lib.moe_num_blocks(10, 3, 64, 96) == -1
     assert lib.moe_num_blocks(0, 8, 64, 64) == 8
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_workspace_size(lib):
@@ -78,9 +78,10 @@ def test_argument_errors_return_before_launch(lib):
     rc = lib.moe_align(None, 4, 2, 8, 96, 64, *([None] * 7), 0, None)
     assert rc == -1 and b"multiple" in lib.moe_last_error()
     # moe_permute: H not a multiple of 8; T = 0 is a no-op
-    lib.moe_permute.argtypes = [P, P, c.c_int64, c.c_int, c.c_int, P, P]
-    assert lib.moe_permute(None, None, 4, 2, 12, None, None) == -1
-    assert lib.moe_permute(None, None, 0, 2, 16, None, None) == 0
+    lib.moe_permute.argtypes = [P, P, P, c.c_int64, c.c_int, c.c_int, P, P]
+    assert lib.moe_permute(None, None, None, 4, 2, 12, None, None) == -1
+    assert lib.moe_permute(None, None, None, 0, 2, 16, None, None) == 0
+    assert lib.moe_permute(None, None, None, 4, 2, 16, None, None) == -1   # neither permutation table
     # grouped GEMM: unsupported block_m, mixed NULL tables
     lib.grouped_gemm_gate_up.argtypes = [P] * 6 + [c.c_int64] + [c.c_int] * 6 + [P, P]
     assert lib.grouped_gemm_gate_up(None, None, None, None, None, None, 8, 1, 128, 128, 128, 96, 1, None, None) == -2

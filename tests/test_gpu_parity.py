@@ -141,9 +141,25 @@ def test_permute(name):
     ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k,
                                  expert_bias=moe_synth.expert_bias(cfg, d))
     tb = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
-    xp = mx.moe_permute(hid, tb["sorted_pair"], cfg.top_k)
     ref = oracle.permute(bits(hid), host(tb["sorted_pair"]), cfg.top_k)
-    assert np.array_equal(bits(xp), ref)
+    # gather by sorted_pair, scatter by pair_to_row, and both given (scatter)
+    for sp, p2r in ((tb["sorted_pair"], None), (None, tb["pair_to_row"]), (tb["sorted_pair"], tb["pair_to_row"])):
+        xp = mx.moe_permute(hid, sp, cfg.top_k, pair_to_row=p2r)
+        assert np.array_equal(bits(xp), ref), (sp is None, p2r is None)
+
+
+@pytest.mark.parametrize("T,k,H,E", [(7, 3, 200, 5), (37, 16, 64, 40), (5, 2, 16392, 4), (300, 1, 2056, 3)])
+def test_permute_ragged_shapes(T, k, H, E):
+    """Row counts that are not multiples of the rows per workgroup, rows that
+    are not multiples of the 256-chunk pass, rows wider than one pass."""
+    d = dev()
+    rng = np.random.default_rng(T * 1000 + H)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    tb = mx.moe_align(_t(ids, d), E, 16, 16)
+    hid = moe_synth.normal_bf16(moe_synth.tensor_key(74, H), (T, H), 1.0, d)
+    ref = oracle.permute(bits(hid), host(tb["sorted_pair"]), k)
+    for sp, p2r in ((tb["sorted_pair"], None), (None, tb["pair_to_row"])):
+        assert np.array_equal(bits(mx.moe_permute(hid, sp, k, pair_to_row=p2r)), ref)
 
 
 # ---------------------------------------------------------------- GEMMs --
