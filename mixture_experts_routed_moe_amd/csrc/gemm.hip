@@ -463,14 +463,17 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
 // with the hardware's workgroup-to-CU rotation and leaves half of the CUs
 // idle.
 //
-// Four waves in a 2x2 arrangement, each 128 rows x 128 weight rows
-// (16 accumulator tiles = 256 fp32 per lane, held in AGPRs), so one wave
-// reads 8 fragments per 16 MFMAs.
+// Eight waves (two per SIMD) in a 4x2 arrangement, each 64 rows x 128 weight
+// rows (8 accumulator tiles), so while one wave of a SIMD waits on a load
+// issue, a barrier or an LDS read, the other keeps the matrix core busy
+// (measured on the DeepSeek-V3-shaped routed gate_up: 2.83 ms against 3.02
+// ms with four 128 x 128 waves). A wave whose rows are all past the tile's
+// valid rows skips its MFMAs.
 //
 // An expert's last tile often has 128 rows or fewer (an odd block count).
 // Such a "half" tile loads only 128 A rows and splits K between the wave
-// rows: wave (wm, wn) computes rows 0..127 against weight rows of column half
-// wn over the 16-wide sub-steps ks with ks % 2 == wm, and the two partial
+// rows: wave rows wm and wm + 2 cover the same 64 rows, the first over the
+// even 16-wide sub-steps, the second over the odd ones, and the two partial
 // sums meet in LDS at the end. A half tile therefore costs about half a full
 // one, and the padding overhead stays that of 128-row blocks.
 //
@@ -489,14 +492,16 @@ constexpr int kWideW = 256;
 constexpr int kRingSlots = 5;
 constexpr int kRingSlotBytes = kWideRows * 128;
 
-template <bool FUSED, bool HALF>
+template <bool FUSED, bool HALF, int NW>
 __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ Wb, int64_t m_start, int rows, int nt,
                                                int K, int up_row, int ldc, uint16_t* __restrict__ C) {
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
   constexpr int AROWS = HALF ? kWideRows / 2 : kWideRows;
-  constexpr int A_LOADS = AROWS / (4 * RPL);         // per wave per half stage
-  constexpr int B_LOADS = kWideW / (4 * RPL);
+  constexpr int WM = NW / 2;                         // wave rows (two wave columns)
+  constexpr int TM = kWideRows / WM / 32;            // 32-row MFMA tiles per wave
+  constexpr int A_LOADS = AROWS / (NW * RPL);        // per wave per half stage
+  constexpr int B_LOADS = kWideW / (NW * RPL);
   constexpr int NS = BK / 16;
   constexpr int MY_NS = HALF ? NS / 2 : NS;
   constexpr int L = A_LOADS + B_LOADS;               // loads issued per step
@@ -550,18 +555,24 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     }
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[TM][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  const int row0 = HALF ? 0 : wm * 128;
-  int a_row[4], b_row[4];
+  // half tiles: wave rows wm and wm + WM/2 cover the same rows, the first
+  // the even sub-steps, the second the odd ones
+  const int kpar = HALF ? (wm >= WM / 2) : 0;
+  const int row0 = (HALF ? wm % (WM / 2) : wm) * TM * 32;
+  // 32-row MFMA tiles of this wave that hold valid rows (the others are
+  // skipped: with two waves per SIMD the partner wave gets the matrix core)
+  const int live_tm = __builtin_amdgcn_readfirstlane(min(TM, max(0, (rows - row0 + 31) / 32)));
+  int a_row[TM], b_row[4];
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm) a_row[tm] = row0 + tm * 32 + (lane & 31);
+  for (int tm = 0; tm < TM; ++tm) a_row[tm] = row0 + tm * 32 + (lane & 31);
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn)
     b_row[tn] = (FUSED ? (tn < 2 ? wn * 64 + tn * 32 : kWideW / 2 + wn * 64 + (tn - 2) * 32) : wn * 128 + tn * 32) +
@@ -579,11 +590,11 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     for (int i = 0; i < A_LOADS; ++i) dma16(a_src[i] + BK, slot(2) + a_lds[i]);
   }
 
-  bf16x8_t af[2][4], bfr[2][4];
+  bf16x8_t af[2][TM], bfr[2][4];
   auto read_frags = [&](const uint8_t* as, const uint8_t* bs, int ks, int buf) __attribute__((always_inline)) {
     const int chunk = ks * 2 + khalf;
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
+    for (int tm = 0; tm < TM; ++tm) {
       const int r = a_row[tm];
       af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(as + r * ROWB + ((chunk ^ row_xor(r)) << 4));
     }
@@ -593,7 +604,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
       bfr[buf][tn] = *reinterpret_cast<const bf16x8_t*>(bs + r * ROWB + ((chunk ^ row_xor(r)) << 4));
     }
   };
-  auto my_ks = [&](int i) __attribute__((always_inline)) { return HALF ? 2 * i + wm : i; };
+  auto my_ks = [&](int i) __attribute__((always_inline)) { return HALF ? 2 * i + kpar : i; };
 
   for (int kt = 0; kt < nk; ++kt) {
     // every load except A(kt+1) (the last issued) must have landed
@@ -606,21 +617,27 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     for (int i = 0; i < MY_NS; ++i) {
       if (i + 1 < MY_NS) read_frags(as, bs, my_ks(i + 1), (i + 1) & 1);
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
+      for (int tm = 0; tm < TM; ++tm) {
+        if (tm >= live_tm) break;  // wave-uniform: this and later row tiles hold no valid rows
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i & 1][tm], bfr[i & 1][tn], acc[tm][tn], 0, 0, 0);
+      }
       issue(kt, i * PER, PER, nk);
     }
   }
 
   if constexpr (HALF) {
+    // the two K halves meet in LDS (the ring is idle: every load has landed
+    // at the last step's wait): the odd-sub-step waves hand over their sums
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     typedef float floatx4 __attribute__((ext_vector_type(4)));
-    floatx4* xch = reinterpret_cast<floatx4*>(smem + wn * (64 * 1024));
-    if (wm == 1) {
+    constexpr int XCH = TM * 4 * 4 * 64;                 // floatx4 per wave
+    static_assert(NW / 2 * XCH * 16 <= kRingSlots * kRingSlotBytes, "exchange fits the ring");
+    floatx4* xch = reinterpret_cast<floatx4*>(smem) + ((wm % (WM / 2)) * 2 + wn) * XCH;
+    if (kpar) {
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
+      for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
@@ -630,9 +647,9 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
           }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (wm == 1) return;
+    if (kpar) return;
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
@@ -644,7 +661,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   }
 
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm) {
+  for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = row0 + tm * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
@@ -694,8 +711,8 @@ __device__ __forceinline__ bool find_wide_tile(const int32_t* __restrict__ gs, i
   return false;
 }
 
-template <bool FUSED>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(
+template <bool FUSED, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel, int m_tiles,
     int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int gm, int gn) {
   constexpr int SMEM = kRingSlots * kRingSlotBytes;
@@ -713,7 +730,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(
   const int sr = group / super_cols;
   const int sc = group - sr * super_cols;
   const int tm_ = t % gm;
-  const int p = sr * gm + tm_;                 // 256-row tile index
+  const int p = sr * gm + tm_;  // 256-row tile index
   const int nt = sc * gn + (t - tm_) / gm;
   if (p >= m_tiles) return;
   int g;
@@ -732,9 +749,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_wide_kernel(
   const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
   if (rows <= kWideRows / 2)
-    wide_ring_tile<FUSED, true>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
+    wide_ring_tile<FUSED, true, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
   else
-    wide_ring_tile<FUSED, false>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
+    wide_ring_tile<FUSED, false, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
 }
 
 // Group shape for the tile order: GN column tiles (a divisor of n_tiles, at
@@ -765,6 +782,9 @@ int launch_pipe(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, 
 #ifndef MOE_WIDE_GROUP
 #define MOE_WIDE_GROUP 16
 #endif
+#ifndef MOE_WIDE_WAVES
+#define MOE_WIDE_WAVES 8
+#endif
 
 template <bool FUSED>
 int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int n_tiles, int K,
@@ -781,7 +801,7 @@ int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
   const int64_t groups = moe::ceil_div(m_tiles, gm) * (n_tiles / gn);
   const int64_t blocks = moe::ceil_div(groups, 8) * 8 * gm * gn;
   if (blocks > 0x7FFFFFFF || m_tiles > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
-  grouped_gemm_wide_kernel<FUSED><<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
+  grouped_gemm_wide_kernel<FUSED, MOE_WIDE_WAVES><<<static_cast<unsigned>(blocks), 64 * MOE_WIDE_WAVES, 0, stream>>>(
       A, W, tb, E, numel, static_cast<int>(m_tiles), n_tiles, K, w_stride, up_row, ldc, C, gm, gn);
   return moe::check_launch(name);
 }
@@ -798,7 +818,10 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   // 256-row tiles pay off once experts average a full 128-row block (at
   // fewer rows per expert nearly every tile is a half tile and the 128-row
   // kernel, with less fixed cost per tile, is faster)
-  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && numel >= static_cast<int64_t>(kPipeBM) * E)
+#ifndef MOE_WIDE_MIN_ROWS
+#define MOE_WIDE_MIN_ROWS 128
+#endif
+  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && numel >= static_cast<int64_t>(MOE_WIDE_MIN_ROWS) * E)
     return launch_wide<FUSED>(A, W, tb, E, numel, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
   if (block_m == kPipeBM && ldc % pipe_cols == 0)
     return launch_pipe<FUSED>(A, W, tb, numel, m_blocks, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
