@@ -16,7 +16,10 @@ average duration comes from HIP events recorded on the launch stream around
 every launch inside the timed region; the algorithmic bytes and FLOPs per
 launch are counted from the realized routing (active experts' weights once,
 activations in and out once). `cpu_baseline` times the oracle on a bounded
-sample of tokens on the host cores.
+sample of tokens on the host cores. `other_workloads` repeats the timed loop
+(same steps and warmup) on the other forward shapes of the family (the Qwen3
+prefill and decode shapes when the DeepSeek-V3 prefill is the primary one) and
+reports each one's ms per forward, TFLOP/s and per-kernel figures.
 """
 from __future__ import annotations
 
@@ -44,11 +47,142 @@ def parse():
     p.add_argument("--config", default="dsv3_prefill",
                    choices=["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only-primary", action="store_true", help="skip the other forward workloads")
     p.add_argument("--cpu-tokens", type=int, default=24, help="tokens in the oracle's timed sample")
     p.add_argument("--unfused", action="store_true", help="gate_up GEMM then a separate SwiGLU kernel")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     return p.parse_args()
+
+
+OTHER_WORKLOADS = ("qwen3_prefill", "qwen3_decode", "dsv3_prefill")
+STAGES = ("topk_softmax", "align", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "unpermute")
+
+
+class Workload:
+    """One forward configuration: seeded inputs and weights resident on the GPU,
+    the buffers of the forward, and a timed loop over whole forwards."""
+
+    def __init__(self, cfg, dev, fuse):
+        import moe_synth
+        import mixture_experts_routed_moe_amd as mx
+        self.cfg, self.fuse, self.mx = cfg, fuse, mx
+        self.hidden = moe_synth.hidden(cfg, dev)
+        self.logits = moe_synth.router_logits(cfg, dev)
+        self.bias = moe_synth.expert_bias(cfg, dev)
+        self.wgu = moe_synth.w_gate_up(cfg, dev)
+        self.wd = moe_synth.w_down(cfg, dev)
+        self.swgu = moe_synth.shared_w_gate_up(cfg, dev) if cfg.shared_F else None
+        self.swd = moe_synth.shared_w_down(cfg, dev) if cfg.shared_F else None
+        shape = mx.MoEShape(cfg.T, cfg.H, cfg.F, cfg.E, cfg.top_k, cfg.padding_m, cfg.block_m, cfg.shared_F)
+        self.bufs = mx.MoEBuffers(shape, dev, fuse_swiglu=fuse)
+
+    def step(self, run):
+        cfg, mx, bufs, fuse = self.cfg, self.mx, self.bufs, self.fuse
+        tb = bufs.tables
+        run("topk_softmax", lambda: mx.moe_topk_softmax(self.logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights,
+                                                        self.bias))
+        run("align", lambda: mx.moe_align(bufs.topk_ids, cfg.E, cfg.padding_m, cfg.block_m, tb))
+        run("permute", lambda: mx.moe_permute(self.hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm,
+                                              tb["pair_to_row"]))
+        if fuse:
+            run("gate_up", lambda: mx.grouped_gemm_gate_up(bufs.x_perm, self.wgu, tb, cfg.padding_m, cfg.block_m,
+                                                           True, bufs.h))
+        else:
+            run("gate_up", lambda: (mx.grouped_gemm_gate_up(bufs.x_perm, self.wgu, tb, cfg.padding_m, cfg.block_m,
+                                                            False, bufs.gate_up), mx.swiglu(bufs.gate_up, bufs.h)))
+        run("down", lambda: mx.grouped_gemm_down(bufs.h, self.wd, tb, cfg.padding_m, cfg.block_m, bufs.y))
+        addend = None
+        if cfg.shared_F:
+            run("shared_gate_up", lambda: mx.grouped_gemm_gate_up(self.hidden, self.swgu, None, cfg.padding_m,
+                                                                  cfg.block_m, True, bufs.shared_h))
+            run("shared_down", lambda: mx.grouped_gemm_down(bufs.shared_h, self.swd, None, cfg.padding_m,
+                                                            cfg.block_m, bufs.shared_y))
+            addend = bufs.shared_y
+        run("unpermute", lambda: mx.moe_unpermute(bufs.y, tb["pair_to_row"], bufs.topk_weights, cfg.rsf, addend,
+                                                  bufs.out))
+
+    def run(self, steps, warmup, ev):
+        import torch
+        cfg, fuse = self.cfg, self.fuse
+        ev_log = {s: [] for s in STAGES}
+
+        def timed(name, fn):
+            a = ev()
+            fn()
+            ev_log[name].append((a, ev()))
+
+        for _ in range(warmup):
+            self.step(lambda name, fn: fn())
+        torch.cuda.synchronize()
+        print(f"# {cfg.name}: warmup done ({warmup} steps)", file=sys.stderr, flush=True)
+        step_ev = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            a = ev()
+            self.step(timed)
+            step_ev.append((a, ev()))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / steps
+        print(f"# {cfg.name}: timed {steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+        stage_ms = {s: (sum(a.elapsed_time(b) for a, b in v) / len(v)) for s, v in ev_log.items() if v}
+        stage_pct = {s: pct([a.elapsed_time(b) for a, b in v]) for s, v in ev_log.items() if v}
+        step_pct = pct([a.elapsed_time(b) for a, b in step_ev])
+
+        # realized routing (read after the timed region)
+        gs = self.bufs.tables["group_sizes"].cpu().numpy()
+        active = int((gs > 0).sum())
+        numel, H, F, E = cfg.numel, cfg.H, cfg.F, cfg.E
+        flop_gate_up = 4.0 * numel * H * F
+        flop_down = 2.0 * numel * H * F
+        flop_shared = 6.0 * cfg.T * H * cfg.shared_F
+        flop_fwd = flop_gate_up + flop_down + flop_shared
+        h_cols = F if fuse else 2 * F
+        bytes_gate_up = active * 2.0 * F * H * 2 + numel * H * 2 + numel * h_cols * 2
+        bytes_down = active * 1.0 * H * F * 2 + numel * F * 2 + numel * H * 2
+        bytes_permute = (cfg.T + numel) * H * 2 + 4 * numel
+        bytes_unpermute = numel * H * 2 + 8 * cfg.T * cfg.top_k + cfg.T * H * 2 * (2 if cfg.shared_F else 1)
+
+        def kern(name, flop, byts):
+            ms = stage_ms.get(name)
+            if not ms:
+                return None
+            s = ms * 1e-3
+            return {"ms": round(ms, 4), **stage_pct[name], "tflops": round(flop / s / 1e12, 2) if flop else None,
+                    "gbs": round(byts / s / 1e9, 1),
+                    "mfma_frac": round(flop / s / 1e12 / BF16_PEAK_TFLOPS, 4) if flop else None,
+                    "hbm_frac": round(byts / s / 1e9 / HBM_PEAK_GBS, 4),
+                    "roofline_frac": round(max(flop / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) / s, 4)}
+
+        kernels = {
+            "topk_softmax": kern("topk_softmax", 0, cfg.T * E * 4 + cfg.T * cfg.top_k * 8),
+            "align": kern("align", 0, numel * 4 * 3),
+            "permute": kern("permute", 0, bytes_permute),
+            "grouped_gemm_gate_up": kern("gate_up", flop_gate_up, bytes_gate_up),
+            "grouped_gemm_down": kern("down", flop_down, bytes_down),
+            "unpermute": kern("unpermute", 0, bytes_unpermute),
+        }
+        if cfg.shared_F:
+            Fs = cfg.shared_F
+            kernels["shared_gate_up"] = kern("shared_gate_up", 4.0 * cfg.T * H * Fs,
+                                             2.0 * Fs * H * 2 + cfg.T * H * 2 + cfg.T * Fs * 2)
+            kernels["shared_down"] = kern("shared_down", 2.0 * cfg.T * H * Fs,
+                                          1.0 * H * Fs * 2 + cfg.T * Fs * 2 + cfg.T * H * 2)
+        gemm_s = (stage_ms["gate_up"] + stage_ms["down"]) * 1e-3
+        summary = {
+            "ms_per_forward": round(ms_per_step, 4), **{"step_" + k: v for k, v in step_pct.items()},
+            "tflops": round(flop_fwd / (ms_per_step * 1e-3) / 1e12, 2),
+            "grouped_gemm_tflops": round((flop_gate_up + flop_down) / gemm_s / 1e12, 2),
+            "grouped_gemm_mfma_frac": round((flop_gate_up + flop_down) / gemm_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "config": {"T": cfg.T, "H": H, "F": F, "E": E, "top_k": cfg.top_k, "padding_m": cfg.padding_m,
+                       "shared_F": cfg.shared_F, "active_experts": active, "max_rows_per_expert": int(gs.max())},
+            "kernels": kernels,
+        }
+        return {"ms_per_step": ms_per_step, "step_pct": step_pct, "stage_ms": stage_ms, "kernels": kernels,
+                "flop_gate_up": flop_gate_up, "flop_down": flop_down, "flop_fwd": flop_fwd,
+                "bytes_gate_up": bytes_gate_up, "group_sizes": gs, "summary": summary}
 
 
 def main():
@@ -66,115 +200,39 @@ def main():
     cfg = moe_synth.CONFIGS[args.config]
     fuse = not args.unfused
     t_gen = time.time()
-    hidden = moe_synth.hidden(cfg, dev)
-    logits = moe_synth.router_logits(cfg, dev)
-    bias = moe_synth.expert_bias(cfg, dev)
-    wgu = moe_synth.w_gate_up(cfg, dev)
-    wd = moe_synth.w_down(cfg, dev)
-    swgu = moe_synth.shared_w_gate_up(cfg, dev) if cfg.shared_F else None
-    swd = moe_synth.shared_w_down(cfg, dev) if cfg.shared_F else None
-    shape = mx.MoEShape(cfg.T, cfg.H, cfg.F, cfg.E, cfg.top_k, cfg.padding_m, cfg.block_m, cfg.shared_F)
-    bufs = mx.MoEBuffers(shape, dev, fuse_swiglu=fuse)
+    wl = Workload(cfg, dev, fuse)
     qx = moe_synth.quant_input(moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F, dev)
     qbufs = mx.swiglu_quant_fp8(qx)
     torch.cuda.synchronize()
     print(f"# inputs generated on the GPU in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
-    stages = ["topk_softmax", "align", "permute", "gate_up", "down", "shared_gate_up", "shared_down",
-              "unpermute"]
-    ev_log = {s: [] for s in stages}
 
     def ev():
         e = torch.cuda.Event(enable_timing=True)
         e.record(stream)
         return e
 
-    def step(record: bool):
-        def run(name, fn):
-            if record:
-                a = ev()
-                fn()
-                ev_log[name].append((a, ev()))
-            else:
-                fn()
-        tb = bufs.tables
-        run("topk_softmax", lambda: mx.moe_topk_softmax(logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bias))
-        run("align", lambda: mx.moe_align(bufs.topk_ids, cfg.E, cfg.padding_m, cfg.block_m, tb))
-        run("permute", lambda: mx.moe_permute(hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm, tb["pair_to_row"]))
-        if fuse:
-            run("gate_up", lambda: mx.grouped_gemm_gate_up(bufs.x_perm, wgu, tb, cfg.padding_m, cfg.block_m,
-                                                           True, bufs.h))
-        else:
-            run("gate_up", lambda: (mx.grouped_gemm_gate_up(bufs.x_perm, wgu, tb, cfg.padding_m, cfg.block_m,
-                                                            False, bufs.gate_up), mx.swiglu(bufs.gate_up, bufs.h)))
-        run("down", lambda: mx.grouped_gemm_down(bufs.h, wd, tb, cfg.padding_m, cfg.block_m, bufs.y))
-        addend = None
-        if cfg.shared_F:
-            run("shared_gate_up", lambda: mx.grouped_gemm_gate_up(hidden, swgu, None, cfg.padding_m, cfg.block_m,
-                                                                  True, bufs.shared_h))
-            run("shared_down", lambda: mx.grouped_gemm_down(bufs.shared_h, swd, None, cfg.padding_m, cfg.block_m,
-                                                            bufs.shared_y))
-            addend = bufs.shared_y
-        run("unpermute", lambda: mx.moe_unpermute(bufs.y, tb["pair_to_row"], bufs.topk_weights, cfg.rsf, addend,
-                                                  bufs.out))
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    step_ev = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        a = ev()
-        step(True)
-        step_ev.append((a, ev()))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
-
-    stage_ms = {s: (sum(a.elapsed_time(b) for a, b in v) / len(v)) for s, v in ev_log.items() if v}
-    stage_pct = {s: pct([a.elapsed_time(b) for a, b in v]) for s, v in ev_log.items() if v}
-    step_pct = pct([a.elapsed_time(b) for a, b in step_ev])
-
-    # realized routing (read after the timed region)
-    gs = bufs.tables["group_sizes"].cpu().numpy()
+    res = wl.run(args.steps, args.warmup, ev)
+    ms_per_step = res["ms_per_step"]
+    stage_ms, kernels = res["stage_ms"], res["kernels"]
+    flop_gate_up, bytes_gate_up, flop_down = res["flop_gate_up"], res["bytes_gate_up"], res["flop_down"]
+    gs = res["group_sizes"]
     active = int((gs > 0).sum())
-    numel, H, F, E = cfg.numel, cfg.H, cfg.F, cfg.E
-    flop_gate_up = 4.0 * numel * H * F
-    flop_down = 2.0 * numel * H * F
-    flop_shared = 6.0 * cfg.T * H * cfg.shared_F
-    flop_fwd = flop_gate_up + flop_down + flop_shared
-    h_cols = F if fuse else 2 * F
-    bytes_gate_up = active * 2.0 * F * H * 2 + numel * H * 2 + numel * h_cols * 2
-    bytes_down = active * 1.0 * H * F * 2 + numel * F * 2 + numel * H * 2
-    bytes_permute = (cfg.T + numel) * H * 2 + 4 * numel
-    bytes_unpermute = numel * H * 2 + 8 * cfg.T * cfg.top_k + cfg.T * H * 2 * (2 if cfg.shared_F else 1)
+    H, F, E = cfg.H, cfg.F, cfg.E
+    hidden, logits, bias, wgu, wd, swgu, swd = (wl.hidden, wl.logits, wl.bias, wl.wgu, wl.wd, wl.swgu, wl.swd)
 
-    def kern(name, flop, byts):
-        ms = stage_ms.get(name)
-        if not ms:
-            return None
-        s = ms * 1e-3
-        return {"ms": round(ms, 4), **stage_pct[name], "tflops": round(flop / s / 1e12, 2) if flop else None,
-                "gbs": round(byts / s / 1e9, 1), "mfma_frac": round(flop / s / 1e12 / BF16_PEAK_TFLOPS, 4) if flop else None,
-                "hbm_frac": round(byts / s / 1e9 / HBM_PEAK_GBS, 4),
-                "roofline_frac": round(max(flop / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) / s, 4)}
-
-    kernels = {
-        "topk_softmax": kern("topk_softmax", 0, cfg.T * E * 4 + cfg.T * cfg.top_k * 8),
-        "align": kern("align", 0, numel * 4 * 3),
-        "permute": kern("permute", 0, bytes_permute),
-        "grouped_gemm_gate_up": kern("gate_up", flop_gate_up, bytes_gate_up),
-        "grouped_gemm_down": kern("down", flop_down, bytes_down),
-        "unpermute": kern("unpermute", 0, bytes_unpermute),
-    }
-    if cfg.shared_F:
-        Fs = cfg.shared_F
-        kernels["shared_gate_up"] = kern("shared_gate_up", 4.0 * cfg.T * H * Fs, 2.0 * Fs * H * 2 + cfg.T * H * 2 + cfg.T * Fs * 2)
-        kernels["shared_down"] = kern("shared_down", 2.0 * cfg.T * H * Fs, 1.0 * H * Fs * 2 + cfg.T * Fs * 2 + cfg.T * H * 2)
+    # the other forward workloads of the same family, each timed the same way
+    others = {}
+    for name in OTHER_WORKLOADS:
+        if name == cfg.name or args.only_primary:
+            continue
+        del wl
+        torch.cuda.empty_cache()
+        wl = Workload(moe_synth.CONFIGS[name], dev, fuse)
+        r = wl.run(args.steps, args.warmup, ev)
+        others[name] = r["summary"]
+        print(f"# {name}: {r['ms_per_step']:.3f} ms/forward", file=sys.stderr, flush=True)
 
     # fused SwiGLU + FP8 quantizer on its own workload, HIP events around each launch
     qM, qF = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
@@ -228,6 +286,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, hidden, logits, bias, wgu, wd, swgu, swd, args.cpu_tokens)
 
+    step_pct, flop_fwd = res["step_pct"], res["flop_fwd"]
     value = flop_fwd / (ms_per_step * 1e-3) / 1e12
     line = {
         "metric": "routed-experts fwd ms + grouped-GEMM TFLOPS (% MFMA peak), T=4096",
@@ -245,6 +304,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
 

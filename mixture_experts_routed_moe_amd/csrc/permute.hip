@@ -79,17 +79,27 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(const uint4* 
   }
 }
 
-// One token per workgroup. The k rows' indices and weights are read first;
-// then, two 16-byte chunks of the output at a time, all 2k gathers are issued
-// before they are reduced (fp32, slots in ascending order), scaled, added to
-// the addend and rounded once.
+// Work is cut into wave-sized items: one item is one token's output chunks
+// [128*b, 128*b + 128) (16 bytes each), two per lane, so a 7168-wide row is
+// seven items and every item ends with the loads it issued; each workgroup
+// runs four independent items, one per wave, and there are no barriers. The
+// token's k row indices and weights are wave-uniform (scalar loads); then all
+// 2k gathers are issued before they are reduced (fp32, slots in ascending
+// order), scaled, added to the addend and rounded once.
+constexpr int kUnpermuteChunks = 128;
+constexpr int kUnpermuteWaves = 4;
+
 template <int MAXK>
-__global__ __launch_bounds__(kThreads) void unpermute_kernel(const uint4* __restrict__ y,
-                                                             const int32_t* __restrict__ pair_to_row,
-                                                             const float* __restrict__ weights, int top_k, int h8,
-                                                             float rsf, const uint4* __restrict__ addend,
-                                                             uint4* __restrict__ out) {
-  const int64_t t = blockIdx.x;
+__global__ __launch_bounds__(64 * kUnpermuteWaves) void unpermute_kernel(
+    const uint4* __restrict__ y, const int32_t* __restrict__ pair_to_row, const float* __restrict__ weights,
+    int64_t T, int top_k, int h8, int items_per_token, float rsf, const uint4* __restrict__ addend,
+    uint4* __restrict__ out) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * kUnpermuteWaves +
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t t = item / items_per_token;
+  if (t >= T) return;  // the whole wave leaves together
+  const int lane = threadIdx.x & 63;
+  const int cb = static_cast<int>(item - t * items_per_token) * kUnpermuteChunks;
   int64_t row[MAXK];
   float w[MAXK];
 #pragma unroll
@@ -97,60 +107,49 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const uint4* __rest
     row[j] = static_cast<int64_t>(pair_to_row[t * top_k + (j < top_k ? j : 0)]) * h8;
     w[j] = j < top_k ? weights[t * top_k + j] : 0.0f;
   }
-  for (int c0 = threadIdx.x; c0 < h8; c0 += 2 * kThreads) {
-    const int c1 = c0 + kThreads;
-    const bool two = c1 < h8;
-    // slots past top_k read row 0 of their token's first slot and weigh 0;
-    // a second chunk past the row end re-reads the first: every load is in
-    // bounds, so all of them can be issued before the reduction
-    const int c1r = two ? c1 : c0;
-    uint4 v[2][MAXK];
+  // slots past top_k read their token's first slot and weigh 0; chunks past
+  // the row end are clamped to its last chunk and not stored: every load is in
+  // bounds and used, so all of them go out before the reduction
+  const int c[2] = {cb + lane, cb + 64 + lane};
+  const int cr[2] = {min(c[0], h8 - 1), min(c[1], h8 - 1)};
+  uint4 v[2][MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    v[0][j] = y[row[j] + cr[0]];
+    v[1][j] = y[row[j] + cr[1]];
+  }
+  uint4 a[2] = {};
+  if (addend != nullptr) {
+    a[0] = addend[t * h8 + cr[0]];
+    a[1] = addend[t * h8 + cr[1]];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int j = 0; j < MAXK; ++j) {
-      v[0][j] = y[row[j] + c0];
-      v[1][j] = y[row[j] + c1r];
-    }
-    uint4 a[2] = {};
-    if (addend != nullptr) {
-      a[0] = addend[t * h8 + c0];
-      a[1] = addend[t * h8 + c1r];
-    }
+      const uint32_t u[4] = {v[h][j].x, v[h][j].y, v[h][j].z, v[h][j].w};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // every slot and both chunks are reduced (slots past top_k weigh 0, a
-      // second chunk past the row end is not stored), so each load is used
-      // unconditionally and all of them go out before the reduction
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < MAXK; ++j) {
-        const uint32_t u[4] = {v[h][j].x, v[h][j].y, v[h][j].z, v[h][j].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += w[j] * moe::bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
-          acc[2 * i + 1] += w[j] * moe::bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
-        }
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += w[j] * moe::bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
+        acc[2 * i + 1] += w[j] * moe::bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
       }
-      float add[8];
-      if (addend != nullptr) {
-        const uint32_t u[4] = {a[h].x, a[h].y, a[h].z, a[h].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          add[2 * i] = moe::bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
-          add[2 * i + 1] = moe::bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) add[i] = 0.0f;
-      }
-      uint4 o;
-      o.x = moe::pack_bf16x2(rsf * acc[0] + add[0], rsf * acc[1] + add[1]);
-      o.y = moe::pack_bf16x2(rsf * acc[2] + add[2], rsf * acc[3] + add[3]);
-      o.z = moe::pack_bf16x2(rsf * acc[4] + add[4], rsf * acc[5] + add[5]);
-      o.w = moe::pack_bf16x2(rsf * acc[6] + add[6], rsf * acc[7] + add[7]);
-      if (h == 0 || two) out[t * h8 + (h == 0 ? c0 : c1)] = o;
     }
+    float add[8];
+    const uint32_t u[4] = {a[h].x, a[h].y, a[h].z, a[h].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      add[2 * i] = moe::bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
+      add[2 * i + 1] = moe::bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
+    }
+    uint4 o;
+    o.x = moe::pack_bf16x2(rsf * acc[0] + add[0], rsf * acc[1] + add[1]);
+    o.y = moe::pack_bf16x2(rsf * acc[2] + add[2], rsf * acc[3] + add[3]);
+    o.z = moe::pack_bf16x2(rsf * acc[4] + add[4], rsf * acc[5] + add[5]);
+    o.w = moe::pack_bf16x2(rsf * acc[6] + add[6], rsf * acc[7] + add[7]);
+    if (c[h] < h8) out[t * h8 + c[h]] = o;
   }
 }
 
@@ -223,21 +222,27 @@ extern "C" int moe_unpermute(const uint16_t* y, const int32_t* pair_to_row, cons
     return fail(MOE_ERR_INVALID_ARG, "moe_unpermute: y/out/addend not 16-byte aligned");
   if (static_cast<const void*>(out) == static_cast<const void*>(y))
     return fail(MOE_ERR_INVALID_ARG, "moe_unpermute: out aliases y");
-  const unsigned grid = static_cast<unsigned>(T);
+  const int h8 = H / 8;
+  const int items_per_token = static_cast<int>(ceil_div(h8, kUnpermuteChunks));
+  const int64_t blocks = ceil_div(T * items_per_token, kUnpermuteWaves);
+  if (blocks > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "moe_unpermute: T*H too large");
+  const unsigned grid = static_cast<unsigned>(blocks);
+  const int threads = 64 * kUnpermuteWaves;
   const uint4* y4 = reinterpret_cast<const uint4*>(y);
   const uint4* a4 = reinterpret_cast<const uint4*>(addend);
   uint4* o4 = reinterpret_cast<uint4*>(out);
+  const float rsf = routed_scaling_factor;
   if (top_k <= 2)
-    unpermute_kernel<2><<<grid, kThreads, 0, stream>>>(y4, pair_to_row, topk_weights, top_k, H / 8,
-                                                       routed_scaling_factor, a4, o4);
+    unpermute_kernel<2><<<grid, threads, 0, stream>>>(y4, pair_to_row, topk_weights, T, top_k, h8, items_per_token,
+                                                      rsf, a4, o4);
   else if (top_k <= 4)
-    unpermute_kernel<4><<<grid, kThreads, 0, stream>>>(y4, pair_to_row, topk_weights, top_k, H / 8,
-                                                       routed_scaling_factor, a4, o4);
+    unpermute_kernel<4><<<grid, threads, 0, stream>>>(y4, pair_to_row, topk_weights, T, top_k, h8, items_per_token,
+                                                      rsf, a4, o4);
   else if (top_k <= 8)
-    unpermute_kernel<8><<<grid, kThreads, 0, stream>>>(y4, pair_to_row, topk_weights, top_k, H / 8,
-                                                       routed_scaling_factor, a4, o4);
+    unpermute_kernel<8><<<grid, threads, 0, stream>>>(y4, pair_to_row, topk_weights, T, top_k, h8, items_per_token,
+                                                      rsf, a4, o4);
   else
-    unpermute_kernel<16><<<grid, kThreads, 0, stream>>>(y4, pair_to_row, topk_weights, top_k, H / 8,
-                                                        routed_scaling_factor, a4, o4);
+    unpermute_kernel<16><<<grid, threads, 0, stream>>>(y4, pair_to_row, topk_weights, T, top_k, h8, items_per_token,
+                                                       rsf, a4, o4);
   return check_launch("moe_unpermute");
 }

@@ -304,6 +304,26 @@ def test_unpermute_and_linearity(name):
         assert np.array_equal(o, rsf * o1)
 
 
+@pytest.mark.parametrize("T,k,H,E", [(7, 3, 200, 5), (37, 16, 64, 40), (5, 2, 16392, 4), (301, 1, 2056, 3),
+                                     (3, 5, 1024, 9)])
+def test_unpermute_ragged_shapes(T, k, H, E):
+    """Rows that end inside a wave's 128-chunk item, several items per row, a
+    token count that leaves the last workgroup's waves partly idle, every top_k
+    template (1..16), with and without the addend."""
+    d = dev()
+    rng = np.random.default_rng(T * 7 + H)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    tb = mx.moe_align(_t(ids, d), E, 16, 16)
+    y = moe_synth.normal_bf16(moe_synth.tensor_key(75, H, k), (T * k, H), 0.5, d)
+    add = moe_synth.normal_bf16(moe_synth.tensor_key(76, H, k), (T, H), 0.5, d)
+    w = torch.as_tensor(rng.uniform(0.0, 1.0, (T, k)).astype(np.float32), device=d)
+    p2r = host(tb["pair_to_row"])
+    o = mx.moe_unpermute(y, tb["pair_to_row"], w, 1.5)
+    assert_bf16_close(bits(o), oracle.unpermute(bits(y), p2r, host(w), k, 1.5), "unpermute")
+    o = mx.moe_unpermute(y, tb["pair_to_row"], w, 1.5, addend=add)
+    assert_bf16_close(bits(o), oracle.unpermute(bits(y), p2r, host(w), k, 1.5, bits(add)), "unpermute+addend")
+
+
 # -------------------------------------------------------------- quantizer --
 
 def _quant_compare(x_bits, F, q, rows=None):
