@@ -20,6 +20,9 @@ sample of tokens on the host cores. `other_workloads` repeats the timed loop
 (same steps and warmup) on the other forward shapes of the family (the Qwen3
 prefill and decode shapes when the DeepSeek-V3 prefill is the primary one) and
 reports each one's ms per forward, TFLOP/s and per-kernel figures.
+`aligned_grouped_gemm` times the grouped GEMM alone on the aligned shapes of
+the pages' grouped-GEMM baseline table (E groups of M rows each), with that
+table's H200 figure beside each case as context.
 """
 from __future__ import annotations
 
@@ -48,6 +51,10 @@ def parse():
                    choices=["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-primary", action="store_true", help="skip the other forward workloads")
+    p.add_argument("--gemm-table-only", action="store_true",
+                   help="time only the aligned grouped-GEMM cases (prints their JSON object)")
+    p.add_argument("--gemm-cases", default="all",
+                   help="aligned grouped-GEMM cases to time: 'all', 'none' or a comma-separated list of names")
     p.add_argument("--cpu-tokens", type=int, default=24, help="tokens in the oracle's timed sample")
     p.add_argument("--unfused", action="store_true", help="gate_up GEMM then a separate SwiGLU kernel")
     p.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +192,47 @@ class Workload:
                 "bytes_gate_up": bytes_gate_up, "group_sizes": gs, "summary": summary}
 
 
+def aligned_gemm_table(names, steps, warmup, ev, dev):
+    """The grouped GEMM C[e] = A[e] @ B[e]^T on the aligned shapes of the pages'
+    grouped-GEMM baseline table (E groups of exactly M rows), each timed with HIP
+    events around every launch; the tables come from moe_align on a one-slot
+    routing that sends M consecutive rows to each group, outside the timed loop."""
+    import torch
+    import moe_synth
+    import mixture_experts_routed_moe_amd as mx
+    out = {}
+    for name in names:
+        case = moe_synth.GEMM_CASES[name]
+        T = case.E * case.M
+        A = moe_synth.gemm_a(case, dev)
+        W = moe_synth.gemm_w(case, dev)
+        ids = torch.arange(case.E, dtype=torch.int32, device=dev).repeat_interleave(case.M).view(T, 1)
+        tb = mx.moe_align(ids, case.E, 128, 128)
+        y = torch.empty(T, case.N, dtype=torch.bfloat16, device=dev)
+        for _ in range(warmup):
+            mx.grouped_gemm_down(A, W, tb, 128, 128, y)
+        evs = []
+        for _ in range(steps):
+            a = ev()
+            mx.grouped_gemm_down(A, W, tb, 128, 128, y)
+            evs.append((a, ev()))
+        torch.cuda.synchronize()
+        ms_list = [a.elapsed_time(b) for a, b in evs]
+        ms = sum(ms_list) / len(ms_list)
+        flop = 2.0 * T * case.N * case.K
+        byts = 2.0 * (T * case.K + case.E * case.N * case.K + T * case.N)
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"M": case.M, "N": case.N, "K": case.K, "E": case.E, "ms": round(ms, 4), **pct(ms_list),
+                     "tflops": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "roofline_frac": round(max(flop / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
+                                            / (ms * 1e-3), 4),
+                     "page_h200_tflops": case.page_tflops}
+        print(f"# aligned GEMM {name}: {ms:.3f} ms, {tf:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        del A, W, y, tb, ids
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -199,6 +247,17 @@ def main():
     dev = torch.device("cuda", 0)
     cfg = moe_synth.CONFIGS[args.config]
     fuse = not args.unfused
+    if args.gemm_table_only:
+        stream0 = torch.cuda.current_stream(dev)
+
+        def ev0():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream0)
+            return e
+        names = list(moe_synth.GEMM_CASES) if args.gemm_cases in ("all", "none") else args.gemm_cases.split(",")
+        print(json.dumps({"aligned_grouped_gemm": aligned_gemm_table(names, args.steps, args.warmup, ev0, dev)}),
+              flush=True)
+        return
     t_gen = time.time()
     wl = Workload(cfg, dev, fuse)
     qx = moe_synth.quant_input(moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F, dev)
@@ -233,6 +292,15 @@ def main():
         r = wl.run(args.steps, args.warmup, ev)
         others[name] = r["summary"]
         print(f"# {name}: {r['ms_per_step']:.3f} ms/forward", file=sys.stderr, flush=True)
+
+    # aligned grouped GEMM at the pages' table shapes
+    if args.gemm_cases == "none":
+        gemm_names = []
+    elif args.gemm_cases == "all":
+        gemm_names = list(moe_synth.GEMM_CASES)
+    else:
+        gemm_names = args.gemm_cases.split(",")
+    gemm_table = aligned_gemm_table(gemm_names, args.steps, args.warmup, ev, dev) if gemm_names else {}
 
     # fused SwiGLU + FP8 quantizer on its own workload, HIP events around each launch
     qM, qF = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
@@ -305,6 +373,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "other_workloads": others,
+        "aligned_grouped_gemm": gemm_table,
     }
     print(json.dumps(line), flush=True)
 

@@ -483,14 +483,43 @@ constexpr int kWideRows = 256;
 constexpr int kWideW = 256;
 
 // The wide tile's K loop, K step 64 (whole 128-byte rows, so every L1 -> L2
-// request moves a full line): the A and the W part of a step are
-// separate 32 KiB "half stages", H(2kt) = A(kt) and H(2kt+1) = W(kt), kept in
-// a ring of five slots (H(i) in slot i % 5, 160 KiB). During step kt the
-// loads of W(kt+1) and A(kt+2) go into the two slots step kt-1 used, and the
-// wait at the top of step kt+1 leaves A(kt+2) in flight: between one and
-// three half stages are in flight at any time and the ring never drains.
-constexpr int kRingSlots = 5;
-constexpr int kRingSlotBytes = kWideRows * 128;
+// request moves a full line). The A part and the W part of a step are 32 KiB
+// each; A(kt) goes to A slot kt % 3 and W(kt) to W slot kt % 2 (LDS: three A
+// slots, then two W slots, 160 KiB). During step kt the loads of W(kt+1) and
+// A(kt+2) go into the slots steps kt-1 used, and the wait at the top of step
+// kt+1 leaves A(kt+2) in flight: between one and three 32 KiB parts are in
+// flight at any time and the ring never drains.
+//
+// The loop is unrolled over the six steps after which both slot sequences
+// repeat, so every slot index is a compile-time constant: the LDS fragment
+// reads take per-lane offsets computed once (opaque to the optimizer, so the
+// slot base stays in the instruction's immediate offset) and the
+// direct-to-LDS loads take an SGPR destination (M0) and a uniform global base
+// plus a per-lane offset that does not change over K. The inner loop then
+// issues almost nothing besides MFMAs, LDS reads and loads.
+// Chunk position XOR of the wide tile's LDS rows: (r & 7) ^ ((r >> 3) & 1).
+// Any 8 consecutive rows from a multiple of 8 take 8 different positions (one
+// 128-byte bank sweep), and the 8 rows of one parity among 16 consecutive rows
+// from a multiple of 16 take 8 different positions (one 256-byte sweep), so
+// the fragment reads are conflict-free in 8- and in 16-lane phases. Rows 16
+// apart share the XOR, so every fragment of a sub-step sits at a constant
+// offset from the first one (32 rows = 4 KiB apart) and one per-lane offset
+// serves all of them.
+__device__ __forceinline__ int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+#ifndef MOE_WIDE_SKIP
+#define MOE_WIDE_SKIP 1
+#endif
+constexpr int kWideSlotBytes = kWideRows * 128;
+constexpr int kWideASlots = 3;
+constexpr int kWideWSlots = 2;
+constexpr int kWideWRing = kWideASlots * kWideSlotBytes;  // first W slot
+constexpr int kWideLds = (kWideASlots + kWideWSlots) * kWideSlotBytes;
+
+template <int V>
+struct Ic {
+  static constexpr int value = V;
+};
 
 template <bool FUSED, bool HALF, int NW>
 __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __restrict__ A,
@@ -500,60 +529,38 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   constexpr int AROWS = HALF ? kWideRows / 2 : kWideRows;
   constexpr int WM = NW / 2;                         // wave rows (two wave columns)
   constexpr int TM = kWideRows / WM / 32;            // 32-row MFMA tiles per wave
-  constexpr int A_LOADS = AROWS / (NW * RPL);        // per wave per half stage
+  constexpr int A_LOADS = AROWS / (NW * RPL);        // per wave per step
   constexpr int B_LOADS = kWideW / (NW * RPL);
   constexpr int NS = BK / 16;
   constexpr int MY_NS = HALF ? NS / 2 : NS;
   constexpr int L = A_LOADS + B_LOADS;               // loads issued per step
   constexpr int PER = (L + MY_NS - 1) / MY_NS;
-  static_assert(kRingSlotBytes == kWideW * ROWB, "slot holds one 256-row part");
+  static_assert(kWideSlotBytes == kWideW * ROWB, "a slot holds one 256-row part");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = lane / CPR;
   const int lpos = lane % CPR;
 
-  const uint16_t* a_src[A_LOADS];
-  int a_lds[A_LOADS];
+  // direct-to-LDS sources: a uniform base per step plus fixed per-lane offsets
+  const char* a_base = reinterpret_cast<const char*>(A + m_start * K);
+  const char* w_base = reinterpret_cast<const char*>(Wb + static_cast<int64_t>(nt) * (FUSED ? kWideW / 2 : kWideW) * K);
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
-    const int rb = (wave * A_LOADS + i) * RPL;
-    const int r = rb + lrow;
+    const int r = (wave * A_LOADS + i) * RPL + lrow;
     const int rr = min(r, rows - 1);
-    a_src[i] = A + (m_start + rr) * K + (lpos ^ row_xor(r)) * 8;
-    a_lds[i] = rb * ROWB;
+    a_off[i] = static_cast<uint32_t>(rr) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
   }
-  const uint16_t* b_src[B_LOADS];
-  int b_lds[B_LOADS];
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
-    const int rb = (wave * B_LOADS + i) * RPL;
-    const int r = rb + lrow;
-    int64_t wrow;
-    if (FUSED)
-      wrow = r < kWideW / 2 ? static_cast<int64_t>(nt) * (kWideW / 2) + r
-                            : static_cast<int64_t>(up_row) + static_cast<int64_t>(nt) * (kWideW / 2) + (r - kWideW / 2);
-    else
-      wrow = static_cast<int64_t>(nt) * kWideW + r;
-    b_src[i] = Wb + wrow * K + (lpos ^ row_xor(r)) * 8;
-    b_lds[i] = rb * ROWB;
+    const int r = (wave * B_LOADS + i) * RPL + lrow;
+    const int lr = (FUSED && r >= kWideW / 2) ? up_row + (r - kWideW / 2) : r;
+    b_off[i] = static_cast<uint32_t>(lr) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
   }
-  auto slot = [&](int h) __attribute__((always_inline)) { return smem + (h % kRingSlots) * kRingSlotBytes; };
-  // loads [first, first+count) of the step-kt issue list: W(kt+1) then A(kt+2)
-  auto issue = [&](int kt, int first, int count, int nk) __attribute__((always_inline)) {
-    uint8_t* ws = slot(2 * (kt + 1) + 1);
-    uint8_t* as = slot(2 * (kt + 2));
-    const int kw = (kt + 1) * BK, ka = (kt + 2) * BK;
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      if (i < first || i >= first + count) continue;
-      if (i < B_LOADS) {
-        if (kt + 1 < nk) dma16(b_src[i] + kw, ws + b_lds[i]);
-      } else {
-        if (kt + 2 < nk) dma16(a_src[i - B_LOADS] + ka, as + a_lds[i - B_LOADS]);
-      }
-    }
-  };
+  const int a_lds0 = wave * A_LOADS * RPL * ROWB;
+  const int b_lds0 = kWideWRing + wave * B_LOADS * RPL * ROWB;
 
   floatx16 acc[TM][4];
 #pragma unroll
@@ -567,64 +574,97 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   // the even sub-steps, the second the odd ones
   const int kpar = HALF ? (wm >= WM / 2) : 0;
   const int row0 = (HALF ? wm % (WM / 2) : wm) * TM * 32;
+#if MOE_WIDE_SKIP
   // 32-row MFMA tiles of this wave that hold valid rows (the others are
   // skipped: with two waves per SIMD the partner wave gets the matrix core)
   const int live_tm = __builtin_amdgcn_readfirstlane(min(TM, max(0, (rows - row0 + 31) / 32)));
-  int a_row[TM], b_row[4];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) a_row[tm] = row0 + tm * 32 + (lane & 31);
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-    b_row[tn] = (FUSED ? (tn < 2 ? wn * 64 + tn * 32 : kWideW / 2 + wn * 64 + (tn - 2) * 32) : wn * 128 + tn * 32) +
-                (lane & 31);
+#endif
   const int khalf = lane >> 5;
+  // per-lane LDS byte offset of this wave's first A and first W fragment in
+  // each sub-step; the other fragments sit at constant offsets from them
+  const int a_r0 = row0 + (lane & 31);
+  const int b_r0 = (FUSED ? wn * 64 : wn * 128) + (lane & 31);
+  uint32_t a_rd[MY_NS], b_rd[MY_NS];
+#pragma unroll
+  for (int i = 0; i < MY_NS; ++i) {
+    const int chunk = (HALF ? 2 * i + kpar : i) * 2 + khalf;
+    a_rd[i] = static_cast<uint32_t>(a_r0 * ROWB + ((chunk ^ wide_swz(a_r0)) << 4));
+    b_rd[i] = static_cast<uint32_t>(kWideWRing + b_r0 * ROWB + ((chunk ^ wide_swz(b_r0)) << 4));
+    asm volatile("" : "+v"(a_rd[i]), "+v"(b_rd[i]));
+  }
+  // W fragment tn: rows b_r0 + b_frag_row(tn)
+  constexpr int kBFragRow[4] = {0, 32, FUSED ? kWideW / 2 : 64, FUSED ? kWideW / 2 + 32 : 96};
 
   const int nk = K / BK;
   // prologue: A(0), W(0), A(1)
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) dma16(a_src[i], slot(0) + a_lds[i]);
+  for (int i = 0; i < A_LOADS; ++i) dma16(a_base + a_off[i], smem + a_lds0 + i * RPL * ROWB);
 #pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) dma16(b_src[i], slot(1) + b_lds[i]);
+  for (int i = 0; i < B_LOADS; ++i) dma16(w_base + b_off[i], smem + b_lds0 + i * RPL * ROWB);
   if (nk > 1) {
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) dma16(a_src[i] + BK, slot(2) + a_lds[i]);
+    for (int i = 0; i < A_LOADS; ++i)
+      dma16(a_base + BK * 2 + a_off[i], smem + kWideSlotBytes + a_lds0 + i * RPL * ROWB);
   }
 
   bf16x8_t af[2][TM], bfr[2][4];
-  auto read_frags = [&](const uint8_t* as, const uint8_t* bs, int ks, int buf) __attribute__((always_inline)) {
-    const int chunk = ks * 2 + khalf;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int r = a_row[tm];
-      af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(as + r * ROWB + ((chunk ^ row_xor(r)) << 4));
-    }
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-      const int r = b_row[tn];
-      bfr[buf][tn] = *reinterpret_cast<const bf16x8_t*>(bs + r * ROWB + ((chunk ^ row_xor(r)) << 4));
-    }
-  };
-  auto my_ks = [&](int i) __attribute__((always_inline)) { return HALF ? 2 * i + kpar : i; };
-
-  for (int kt = 0; kt < nk; ++kt) {
+  auto step = [&](auto sa, auto sw, int kt) __attribute__((always_inline)) {
+    constexpr int SA = decltype(sa)::value, SW = decltype(sw)::value;
+    constexpr int A_NEXT = (SA + 2) % kWideASlots, W_NEXT = (SW + 1) % kWideWSlots;
     // every load except A(kt+1) (the last issued) must have landed
     if (kt + 1 < nk) wait_dma_barrier<A_LOADS>();
     else wait_dma_barrier<0>();
-    const uint8_t* as = slot(2 * kt);
-    const uint8_t* bs = slot(2 * kt + 1);
-    read_frags(as, bs, my_ks(0), 0);
+    auto read_frags = [&](int i, int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(smem + a_rd[i] + SA * kWideSlotBytes + tm * 32 * ROWB);
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+        bfr[buf][tn] =
+            *reinterpret_cast<const bf16x8_t*>(smem + b_rd[i] + SW * kWideSlotBytes + kBFragRow[tn] * ROWB);
+    };
+    const char* w_src = w_base + (kt + 1) * BK * 2;
+    const char* a_src = a_base + (kt + 2) * BK * 2;
+    read_frags(0, 0);
 #pragma unroll
     for (int i = 0; i < MY_NS; ++i) {
-      if (i + 1 < MY_NS) read_frags(as, bs, my_ks(i + 1), (i + 1) & 1);
+      // a sub-step is: the reads of the next sub-step's fragments, this
+      // sub-step's MFMAs, its share of the loads; the scheduler keeps them in
+      // that order (left free, it hoists every read of a step and spills)
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < MY_NS) read_frags(i + 1, (i + 1) & 1);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
+#if MOE_WIDE_SKIP
         if (tm >= live_tm) break;  // wave-uniform: this and later row tiles hold no valid rows
+#endif
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i & 1][tm], bfr[i & 1][tn], acc[tm][tn], 0, 0, 0);
       }
-      issue(kt, i * PER, PER, nk);
+      // this sub-step's share of the loads for W(kt+1), then A(kt+2)
+#pragma unroll
+      for (int j = i * PER; j < i * PER + PER && j < L; ++j) {
+        if (j < B_LOADS) {
+          if (kt + 1 < nk)
+            dma16(w_src + b_off[j], smem + b_lds0 + W_NEXT * kWideSlotBytes + j * RPL * ROWB);
+        } else {
+          if (kt + 2 < nk)
+            dma16(a_src + a_off[j - B_LOADS],
+                  smem + a_lds0 + A_NEXT * kWideSlotBytes + (j - B_LOADS) * RPL * ROWB);
+        }
+      }
     }
+  };
+  // six steps per iteration (both slot sequences repeat after six), each
+  // guarded, so the loop has a single exit
+  for (int kt = 0; kt < nk; kt += 6) {
+    step(Ic<0>{}, Ic<0>{}, kt);
+    if (kt + 1 < nk) step(Ic<1>{}, Ic<1>{}, kt + 1);
+    if (kt + 2 < nk) step(Ic<2>{}, Ic<0>{}, kt + 2);
+    if (kt + 3 < nk) step(Ic<0>{}, Ic<1>{}, kt + 3);
+    if (kt + 4 < nk) step(Ic<1>{}, Ic<0>{}, kt + 4);
+    if (kt + 5 < nk) step(Ic<2>{}, Ic<1>{}, kt + 5);
   }
 
   if constexpr (HALF) {
@@ -633,7 +673,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     typedef float floatx4 __attribute__((ext_vector_type(4)));
     constexpr int XCH = TM * 4 * 4 * 64;                 // floatx4 per wave
-    static_assert(NW / 2 * XCH * 16 <= kRingSlots * kRingSlotBytes, "exchange fits the ring");
+    static_assert(NW / 2 * XCH * 16 <= kWideLds, "exchange fits the ring");
     floatx4* xch = reinterpret_cast<floatx4*>(smem) + ((wm % (WM / 2)) * 2 + wn) * XCH;
     if (kpar) {
 #pragma unroll
@@ -649,15 +689,21 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kpar) return;
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int tm = 0; tm < TM; ++tm) {
+      // one row tile's partial sums at a time, added here (not sunk into the
+      // conditional stores below, which would keep every read live at once)
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
+      for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const floatx4 v = xch[((tm * 4 + tn) * 4 + q) * 64 + lane];
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[tm][tn][4 * q + e] += v[e];
         }
+        asm volatile("" : "+v"(acc[tm][tn]));
+      }
+    }
   }
 
 #pragma unroll
@@ -715,7 +761,7 @@ template <bool FUSED, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel, int m_tiles,
     int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int gm, int gn) {
-  constexpr int SMEM = kRingSlots * kRingSlotBytes;
+  constexpr int SMEM = kWideLds;
   static_assert(SMEM <= 160 * 1024, "LDS ring too large");
   static_assert(SMEM >= 128 * 1024, "the half-tile exchange needs 128 KiB");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -821,7 +867,10 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
 #ifndef MOE_WIDE_MIN_ROWS
 #define MOE_WIDE_MIN_ROWS 128
 #endif
-  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && numel >= static_cast<int64_t>(MOE_WIDE_MIN_ROWS) * E)
+  // the wide kernel addresses a tile's A and W rows with 32-bit byte offsets
+  const bool wide_fits = (static_cast<int64_t>(up_row) + kWideW) * K * 2 < (int64_t(1) << 32);
+  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits &&
+      numel >= static_cast<int64_t>(MOE_WIDE_MIN_ROWS) * E)
     return launch_wide<FUSED>(A, W, tb, E, numel, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
   if (block_m == kPipeBM && ldc % pipe_cols == 0)
     return launch_pipe<FUSED>(A, W, tb, numel, m_blocks, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);

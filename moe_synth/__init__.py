@@ -176,6 +176,59 @@ QUANT_CONFIG = QuantConfig(4, "swiglu_quant_fp8", M=32768, F=2048)
 QUANT_EDGE_M = (0, 1, 127, 128, 129)
 
 
+TAG_GEMM_A, TAG_GEMM_W = 8, 9
+
+
+@dataclasses.dataclass(frozen=True)
+class GemmCase:
+    """Aligned grouped GEMM C[e] = A[e] @ B[e]^T over E groups of exactly M rows:
+    A [E*M, K] bf16 ~N(0,1) (groups stored one after another), B [E, N, K] bf16
+    ~N(0,1/K). The shapes are those of the TileOPs grouped-GEMM baseline table
+    (PR #1580, "Benchmark results - grouped-GEMM baselines"), whose cases give the
+    rows per expert M and the token count T; E = T / M (rounded down where T is
+    not a multiple of M). `page_tflops` is that table's H200 figure for the
+    persistent kernel, kept as context."""
+    cid: int
+    name: str
+    M: int
+    N: int
+    K: int
+    E: int
+    page_tflops: float
+
+
+GEMM_CASES = {c.name: c for c in (
+    GemmCase(20, "glm5_up_t32768", 1024, 4096, 6144, 32, 599.8),
+    GemmCase(21, "glm5_up_t65536", 2048, 4096, 6144, 32, 607.6),
+    GemmCase(22, "glm5_up_t131072", 4096, 4096, 6144, 32, 614.8),
+    GemmCase(23, "glm5_up_t262144", 8192, 4096, 6144, 32, 612.7),
+    GemmCase(24, "glm5_down_t32768", 1024, 6144, 2048, 32, 564.6),
+    GemmCase(25, "glm5_down_t65536", 2048, 6144, 2048, 32, 596.3),
+    GemmCase(26, "glm5_down_t131072", 4096, 6144, 2048, 32, 603.0),
+    GemmCase(27, "glm5_down_t262144", 8192, 6144, 2048, 32, 602.9),
+    GemmCase(28, "llama4_128e_up_t131072", 1024, 16384, 5120, 128, 549.9),
+    GemmCase(29, "llama4_128e_down_t131072", 1024, 5120, 8192, 128, 604.8),
+    GemmCase(30, "qwen3.5_397b_up_t52429", 1024, 2048, 4096, 51, 613.5),
+    GemmCase(31, "qwen3.5_397b_down_t52429", 1024, 4096, 1024, 51, 575.8),
+)}
+
+
+def gemm_a(case: GemmCase, device="cpu", rows: Optional[slice] = None) -> torch.Tensor:
+    """A [E*M, K] (or the given rows of it)."""
+    r0, r1 = (0, case.E * case.M) if rows is None else (rows.start, rows.stop)
+    return normal_bf16(tensor_key(case.cid, TAG_GEMM_A), (r1 - r0, case.K), 1.0, device, start=r0 * case.K)
+
+
+def gemm_w(case: GemmCase, device="cpu", experts: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """B [E, N, K] (or [len(experts), N, K] for a subset)."""
+    per = case.N * case.K
+    key = tensor_key(case.cid, TAG_GEMM_W)
+    sigma = 1.0 / math.sqrt(case.K)
+    if experts is None:
+        return normal_bf16(key, (case.E, case.N, case.K), sigma, device)
+    return torch.stack([normal_bf16(key, (case.N, case.K), sigma, device, start=e * per) for e in experts])
+
+
 def zipf_bias(cfg: MoEConfig) -> np.ndarray:
     """Per-expert logit bias -s*ln(rank), rank a seeded permutation of 1..E (float32)."""
     rng = np.random.Generator(np.random.PCG64(tensor_key(cfg.cid, TAG_BIAS)))

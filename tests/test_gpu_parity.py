@@ -281,6 +281,51 @@ def test_swiglu_bit_exact_including_extremes():
     assert np.array_equal(bits(h), oracle.swiglu(x, F))
 
 
+# ------------------------------------------------ aligned grouped GEMM --
+
+def _aligned_tables(E, M, d):
+    T = E * M
+    ids = torch.arange(E, dtype=torch.int32, device=d).repeat_interleave(M).view(T, 1)
+    tb = mx.moe_align(ids, E, 128, 128)
+    assert np.array_equal(host(tb["group_sizes"]), np.full(E, M))
+    return tb
+
+
+@pytest.mark.parametrize("E,M,N,K", [(3, 512, 256, 384), (2, 1024, 640, 192), (5, 256, 128, 128)])
+def test_aligned_gemm_small(E, M, N, K):
+    """Aligned groups (every group a whole number of 256-row tiles), every output."""
+    d = dev()
+    key = moe_synth.tensor_key(77, E, M, N, K)
+    a = moe_synth.normal_bf16(key, (E * M, K), 1.0, d)
+    w = moe_synth.normal_bf16(key + 1, (E, N, K), K ** -0.5, d)
+    tb = _aligned_tables(E, M, d)
+    y = mx.grouped_gemm_down(a, w, tb, 128, 128)
+    ref = oracle.grouped_gemm(bits(a), bits(w), np.full(E, M), np.arange(E) * M)
+    assert_bf16_close(bits(y), ref, "aligned grouped GEMM")
+
+
+@pytest.mark.parametrize("name", ["glm5_up_t32768", "glm5_down_t262144", "llama4_128e_down_t131072",
+                                  "qwen3.5_397b_down_t52429"])
+def test_aligned_gemm_table_shape_sampled_rows(name):
+    """A table shape at full size, launched as the benchmark launches it: every
+    output column of sampled rows (tile edges and random rows) in sampled
+    groups (first, last, random), against the oracle."""
+    d = dev()
+    case = moe_synth.GEMM_CASES[name]
+    say("aligned gemm", name)
+    a = moe_synth.gemm_a(case, d)
+    w = moe_synth.gemm_w(case, d)
+    tb = _aligned_tables(case.E, case.M, d)
+    y = mx.grouped_gemm_down(a, w, tb, 128, 128)
+    rng = np.random.default_rng(case.cid)
+    groups = sorted({0, case.E - 1, *rng.choice(case.E, 2, replace=False).tolist()})
+    rows = sorted({0, 127, 128, 255, 256, case.M - 1, *rng.choice(case.M, 4, replace=False).tolist()})
+    for e in groups:
+        r = torch.as_tensor(e * case.M + np.asarray(rows), device=d)
+        ref = oracle.grouped_gemm(bits(a[r]), bits(w[e:e + 1]), np.array([len(rows)]), np.array([0]))
+        assert_bf16_close(bits(y[r]), ref, f"{name} group {e}")
+
+
 # ------------------------------------------------------------- unpermute --
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3_decode"])
