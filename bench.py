@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="dsv3_prefill",
-                   choices=["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"])
+                   choices=["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill", "kimi_k2_t1", "kimi_k2_t32",
+                            "kimi_k2_t512", "kimi_k2_t2048", "kimi_k2_t4096"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-primary", action="store_true", help="skip the other forward workloads")
     p.add_argument("--gemm-table-only", action="store_true",
@@ -62,7 +63,11 @@ def parse():
     return p.parse_args()
 
 
-OTHER_WORKLOADS = ("qwen3_prefill", "qwen3_decode", "dsv3_prefill")
+OTHER_WORKLOADS = ("qwen3_prefill", "qwen3_decode", "dsv3_prefill", "kimi_k2_t1", "kimi_k2_t32", "kimi_k2_t512",
+                   "kimi_k2_t2048", "kimi_k2_t4096")
+# context only (other hardware): the pages' H200 ms per forward of the Kimi-K2-scale
+# routed + shared op (TileOPs #778 "Benchmark", TileOPs column) at each token count
+KIMI_K2_PAGE_H200_MS = {1: 0.95, 32: 5.46, 512: 10.44, 2048: 19.99, 4096: 32.63}
 STAGES = ("topk_softmax", "align", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "unpermute")
 
 
@@ -70,17 +75,21 @@ class Workload:
     """One forward configuration: seeded inputs and weights resident on the GPU,
     the buffers of the forward, and a timed loop over whole forwards."""
 
-    def __init__(self, cfg, dev, fuse):
+    def __init__(self, cfg, dev, fuse, like=None):
         import moe_synth
         import mixture_experts_routed_moe_amd as mx
         self.cfg, self.fuse, self.mx = cfg, fuse, mx
         self.hidden = moe_synth.hidden(cfg, dev)
         self.logits = moe_synth.router_logits(cfg, dev)
         self.bias = moe_synth.expert_bias(cfg, dev)
-        self.wgu = moe_synth.w_gate_up(cfg, dev)
-        self.wd = moe_synth.w_down(cfg, dev)
-        self.swgu = moe_synth.shared_w_gate_up(cfg, dev) if cfg.shared_F else None
-        self.swd = moe_synth.shared_w_down(cfg, dev) if cfg.shared_F else None
+        if like is not None and like.cfg.cid == cfg.cid:
+            # same workload id: the same weight tensors (only the token count differs)
+            self.wgu, self.wd, self.swgu, self.swd = like.wgu, like.wd, like.swgu, like.swd
+        else:
+            self.wgu = moe_synth.w_gate_up(cfg, dev)
+            self.wd = moe_synth.w_down(cfg, dev)
+            self.swgu = moe_synth.shared_w_gate_up(cfg, dev) if cfg.shared_F else None
+            self.swd = moe_synth.shared_w_down(cfg, dev) if cfg.shared_F else None
         shape = mx.MoEShape(cfg.T, cfg.H, cfg.F, cfg.E, cfg.top_k, cfg.padding_m, cfg.block_m, cfg.shared_F)
         self.bufs = mx.MoEBuffers(shape, dev, fuse_swiglu=fuse)
 
@@ -88,7 +97,7 @@ class Workload:
         cfg, mx, bufs, fuse = self.cfg, self.mx, self.bufs, self.fuse
         tb = bufs.tables
         run("topk_softmax", lambda: mx.moe_topk_softmax(self.logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights,
-                                                        self.bias))
+                                                        self.bias, cfg.scoring, cfg.renormalize))
         run("align", lambda: mx.moe_align(bufs.topk_ids, cfg.E, cfg.padding_m, cfg.block_m, tb))
         run("permute", lambda: mx.moe_permute(self.hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm,
                                               tb["pair_to_row"]))
@@ -184,7 +193,8 @@ class Workload:
             "grouped_gemm_tflops": round((flop_gate_up + flop_down) / gemm_s / 1e12, 2),
             "grouped_gemm_mfma_frac": round((flop_gate_up + flop_down) / gemm_s / 1e12 / BF16_PEAK_TFLOPS, 4),
             "config": {"T": cfg.T, "H": H, "F": F, "E": E, "top_k": cfg.top_k, "padding_m": cfg.padding_m,
-                       "shared_F": cfg.shared_F, "active_experts": active, "max_rows_per_expert": int(gs.max())},
+                       "shared_F": cfg.shared_F, "scoring": cfg.scoring, "active_experts": active,
+                       "max_rows_per_expert": int(gs.max())},
             "kernels": kernels,
         }
         return {"ms_per_step": ms_per_step, "step_pct": step_pct, "stage_ms": stage_ms, "kernels": kernels,
@@ -286,11 +296,17 @@ def main():
     for name in OTHER_WORKLOADS:
         if name == cfg.name or args.only_primary:
             continue
+        prev = wl
         del wl
-        torch.cuda.empty_cache()
-        wl = Workload(moe_synth.CONFIGS[name], dev, fuse)
+        if prev.cfg.cid != moe_synth.CONFIGS[name].cid:
+            prev = None
+            torch.cuda.empty_cache()
+        wl = Workload(moe_synth.CONFIGS[name], dev, fuse, like=prev)
+        del prev
         r = wl.run(args.steps, args.warmup, ev)
         others[name] = r["summary"]
+        if name.startswith("kimi_k2_t"):
+            others[name]["page_h200_ms"] = KIMI_K2_PAGE_H200_MS.get(moe_synth.CONFIGS[name].T)
         print(f"# {name}: {r['ms_per_step']:.3f} ms/forward", file=sys.stderr, flush=True)
 
     # aligned grouped GEMM at the pages' table shapes
@@ -428,7 +444,7 @@ def cpu_baseline(cfg, hidden, logits, bias, wgu, wd, swgu, swd, n_tokens):
     hid = moe_synth.bits16(hidden[tsel])
     lg = logits[tsel].cpu().numpy()
     bias_h = None if bias is None else bias.cpu().numpy()
-    ids, _ = oracle.route(lg, cfg.top_k, bias_h)
+    ids, _ = oracle.route(lg, cfg.top_k, bias_h, cfg.scoring, cfg.renormalize)
     used = np.unique(ids)
     sel = torch.as_tensor(used, device=wgu.device)
     wgu_h = moe_synth.bits16(wgu[sel])
@@ -439,7 +455,7 @@ def cpu_baseline(cfg, hidden, logits, bias, wgu, wd, swgu, swd, n_tokens):
     remap[used] = np.arange(used.size)
     # the oracle's forward on the sampled tokens, restricted to the experts they reach
     t0 = time.perf_counter()
-    ids2, w = oracle.route(lg, cfg.top_k, bias_h)
+    ids2, w = oracle.route(lg, cfg.top_k, bias_h, cfg.scoring, cfg.renormalize)
     ids_r = remap[ids2].astype(np.int32)
     tab = oracle.dispatch_tables(ids_r, used.size, cfg.padding_m, cfg.block_m)
     xp = oracle.permute(hid, tab["sorted_pair"], cfg.top_k)

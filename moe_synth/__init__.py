@@ -148,6 +148,8 @@ class MoEConfig:
     rsf: float = 1.0
     zipf_s: Optional[float] = None
     shared_F: int = 0
+    scoring: str = "softmax"
+    renormalize: bool = True
 
     @property
     def numel(self) -> int:
@@ -172,6 +174,15 @@ CONFIGS = {
     "dsv3_prefill": MoEConfig(3, "dsv3_prefill", T=4096, H=7168, F=2048, E=256, top_k=8,
                               padding_m=128, block_m=128, rsf=2.827, zipf_s=1.1, shared_F=2048),
 }
+# Kimi-K2-scale routed + shared forward (TileOPs #778 "Benchmark": E=384, K=8,
+# H=7168, F=2048, F_s=18432, bf16, sigmoid routing) at the token counts of that
+# table. One workload id for all of them: the weights are the same tensors and
+# each token count's hidden states and logits are the first T rows of the
+# T=4096 ones.
+KIMI_K2_TOKENS = (1, 32, 512, 2048, 4096)
+for _t in KIMI_K2_TOKENS:
+    CONFIGS[f"kimi_k2_t{_t}"] = MoEConfig(5, f"kimi_k2_t{_t}", T=_t, H=7168, F=2048, E=384, top_k=8, padding_m=128,
+                                          block_m=128, shared_F=18432, scoring="sigmoid")
 QUANT_CONFIG = QuantConfig(4, "swiglu_quant_fp8", M=32768, F=2048)
 QUANT_EDGE_M = (0, 1, 127, 128, 129)
 

@@ -68,7 +68,8 @@ def oracle_tokens(cfg, inp, tokens):
     tokens = np.asarray(tokens)
     hid = bits(inp["hidden"][torch.as_tensor(tokens, device=inp["hidden"].device)])
     logits = host(inp["logits"][torch.as_tensor(tokens, device=inp["logits"].device)])
-    ids, w = oracle.route(logits, cfg.top_k, host(inp["bias"]) if "bias" in inp else None)
+    ids, w = oracle.route(logits, cfg.top_k, host(inp["bias"]) if "bias" in inp else None, cfg.scoring,
+                          cfg.renormalize)
     used = np.unique(ids)
     remap = {int(e): i for i, e in enumerate(used)}
     ids_r = np.vectorize(lambda e: remap[int(e)])(ids).astype(np.int32)

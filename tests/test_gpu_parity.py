@@ -49,15 +49,17 @@ def test_generator_same_bits_on_gpu():
 
 # --------------------------------------------------------------- routing --
 
-@pytest.mark.parametrize("name", ["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"])
+@pytest.mark.parametrize("name", ["tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill", "kimi_k2_t4096"])
 def test_route(name):
     d = dev()
     cfg = moe_synth.CONFIGS[name]
     say("route", name)
     logits = moe_synth.router_logits(cfg, d)
     bias = moe_synth.expert_bias(cfg, d)
-    ids, w = mx.moe_topk_softmax(logits, cfg.top_k, expert_bias=bias)
-    rid, rw = oracle.route(host(logits), cfg.top_k, None if bias is None else host(bias))
+    ids, w = mx.moe_topk_softmax(logits, cfg.top_k, expert_bias=bias, scoring=cfg.scoring,
+                                 renormalize=cfg.renormalize)
+    rid, rw = oracle.route(host(logits), cfg.top_k, None if bias is None else host(bias), cfg.scoring,
+                           cfg.renormalize)
     assert np.array_equal(host(ids), rid)
     np.testing.assert_allclose(host(w), rw, rtol=2e-6, atol=1e-7)
 
@@ -101,10 +103,11 @@ def _align_cases(golden_dir):
     yield "pad128_block64", np.stack([rng.permutation(16)[:4] for _ in range(777)]).astype(np.int32), 16, 128, 64
     yield "E1", np.zeros((50, 1), np.int32), 1, 16, 16
     yield "E1000", np.stack([rng.permutation(1000)[:8] for _ in range(2100)]).astype(np.int32), 1000, 32, 32
-    for name in ("tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill"):
+    for name in ("tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill", "kimi_k2_t4096"):
         cfg = moe_synth.CONFIGS[name]
         bias = moe_synth.expert_bias(cfg)
-        ids, _ = oracle.route(moe_synth.router_logits(cfg).numpy(), cfg.top_k, None if bias is None else bias.numpy())
+        ids, _ = oracle.route(moe_synth.router_logits(cfg).numpy(), cfg.top_k, None if bias is None else bias.numpy(),
+                              cfg.scoring, cfg.renormalize)
         yield name, ids, cfg.E, cfg.padding_m, cfg.block_m
 
 
@@ -449,7 +452,8 @@ def test_swiglu_quant_full_size_sampled_blocks():
 def _gpu_forward(cfg, inp, fuse=True, **kw):
     return mx.routed_moe_forward(inp["hidden"], inp["logits"], inp["w_gate_up"], inp["w_down"], cfg.top_k,
                                  cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"),
-                                 inp.get("shared_w_down"), fuse_swiglu=fuse, expert_bias=inp.get("bias"), **kw)
+                                 inp.get("shared_w_down"), fuse_swiglu=fuse, expert_bias=inp.get("bias"),
+                                 scoring=cfg.scoring, renormalize=cfg.renormalize, **kw)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3_decode"])
@@ -460,14 +464,33 @@ def test_forward_full_oracle(name):
     inp = inputs(cfg, d)
     ref = oracle.forward(bits(inp["hidden"]), host(inp["logits"]), bits(inp["w_gate_up"]), bits(inp["w_down"]),
                          cfg.top_k, cfg.rsf, cfg.padding_m, cfg.block_m)
-    assert "bias" not in inp
+    assert "bias" not in inp and cfg.scoring == "softmax"
     for fuse in (True, False):
         out = _gpu_forward(cfg, inp, fuse)
         err = assert_bf16_close(bits(out), ref["out"], f"{name} out fuse={fuse}")
         say("  out max abs err", err, "fuse", fuse)
 
 
-@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_prefill"])
+def test_forward_kimi_k2_single_token():
+    """The Kimi-K2-shaped forward at T=1 (decode of one token: 8 of 384 experts,
+    one row each, plus the 18432-wide shared expert), every output element
+    against the oracle."""
+    d = dev()
+    cfg = moe_synth.CONFIGS["kimi_k2_t1"]
+    say("forward", cfg.name)
+    inp = inputs(cfg, d)
+    ref = oracle_tokens(cfg, inp, [0])
+    for fuse in (True, False):
+        out = _gpu_forward(cfg, inp, fuse)
+        err = assert_bf16_close(bits(out), ref["out"], f"kimi T=1 out fuse={fuse}")
+        say("  out max abs err", err, "fuse", fuse)
+
+
+# sampled tokens per workload: each one brings up to k experts' weights to the host
+SAMPLED_TOKENS = {"qwen3_prefill": 21, "dsv3_prefill": 21, "kimi_k2_t32": 3, "kimi_k2_t512": 3, "kimi_k2_t4096": 3}
+
+
+@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_prefill", "kimi_k2_t32", "kimi_k2_t512", "kimi_k2_t4096"])
 def test_forward_full_size_sampled_tokens(name):
     d = dev()
     cfg = moe_synth.CONFIGS[name]
@@ -479,14 +502,16 @@ def test_forward_full_size_sampled_tokens(name):
     torch.cuda.synchronize()
     # full-size tables against the oracle's
     ids = host(bufs.topk_ids)
-    ref_ids, _ = oracle.route(host(inp["logits"]), cfg.top_k, host(inp["bias"]) if "bias" in inp else None)
+    ref_ids, _ = oracle.route(host(inp["logits"]), cfg.top_k, host(inp["bias"]) if "bias" in inp else None,
+                              cfg.scoring, cfg.renormalize)
     assert np.array_equal(ids, ref_ids)
     ref_tab = oracle.dispatch_tables(ref_ids, cfg.E, cfg.padding_m, cfg.block_m)
     for key in ("group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx", "sorted_pair",
                 "pair_to_row"):
         assert np.array_equal(host(bufs.tables[key]), ref_tab[key]), key
     say("  active experts", int((ref_tab["group_sizes"] > 0).sum()), "max rows", int(ref_tab["group_sizes"].max()))
-    tokens = np.unique(np.concatenate([[0, 1, cfg.T - 1], np.random.default_rng(cfg.cid).choice(cfg.T, 21)]))
+    tokens = np.unique(np.concatenate([[0, 1, cfg.T - 1],
+                                       np.random.default_rng(cfg.cid).choice(cfg.T, SAMPLED_TOKENS[name])]))
     ref = oracle_tokens(cfg, inp, tokens)
     err = assert_bf16_close(bits(out[torch.as_tensor(tokens, device=d)]), ref["out"], f"{name} sampled out")
     say("  sampled out max abs err", err)
