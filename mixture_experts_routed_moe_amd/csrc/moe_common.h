@@ -83,6 +83,16 @@ __device__ __forceinline__ uint16_t swiglu_bf16(uint16_t gate, uint16_t up) {
   return f32_to_bf16(s * bf16_to_f32(up));
 }
 
+// ------------------------------------------ streaming (non-temporal) access --
+// A 16-byte load of data read once per kernel, marked non-temporal so it
+// does not displace reused lines in the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------ SiLU lookup in LDS --
 // The gate input of every SwiGLU is bf16, so silu_spec(g) has 2^16 possible
 // arguments. A table of the 2 * 32 * 128 = 8192 values with |g| in

@@ -8,6 +8,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Rows that are read once (hidden in the permute, y and the addend in the
+// unpermute) are loaded non-temporally: measured on the DeepSeek-V3-shaped
+// workload, the unpermute goes from 0.112 to 0.102 ms and the permute gains
+// about 1%; non-temporal stores made the permute 35% slower, so stores are
+// plain.
+
 // R rows per workgroup, CPT 16-byte chunks per thread per row and pass (a
 // row wider than 256*CPT chunks takes several passes): the R source-row
 // indices are read first, then every load of a pass is issued before its
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(const uint4* 
 #pragma unroll
     for (int q = 0; q < R; ++q)
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) v[q][i] = hidden[src[q] + min(cb + tid + i * kThreads, h8 - 1)];
+      for (int i = 0; i < CPT; ++i) v[q][i] = moe::load_stream16(hidden + src[q] + min(cb + tid + i * kThreads, h8 - 1));
 #pragma unroll
     for (int q = 0; q < R; ++q)
 #pragma unroll
@@ -86,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(const uint4* 
 // token's k row indices and weights are wave-uniform (scalar loads); then all
 // 2k gathers are issued before they are reduced (fp32, slots in ascending
 // order), scaled, added to the addend and rounded once.
-constexpr int kUnpermuteChunks = 128;
+constexpr int kUnpermuteCpl = 2;                          // 16-byte chunks per lane and row
+constexpr int kUnpermuteChunks = 64 * kUnpermuteCpl;      // chunks per item
 constexpr int kUnpermuteWaves = 4;
 
 template <int MAXK>
@@ -94,6 +101,7 @@ __global__ __launch_bounds__(64 * kUnpermuteWaves) void unpermute_kernel(
     const uint4* __restrict__ y, const int32_t* __restrict__ pair_to_row, const float* __restrict__ weights,
     int64_t T, int top_k, int h8, int items_per_token, float rsf, const uint4* __restrict__ addend,
     uint4* __restrict__ out) {
+  constexpr int CPL = kUnpermuteCpl;
   const int64_t item = static_cast<int64_t>(blockIdx.x) * kUnpermuteWaves +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t t = item / items_per_token;
@@ -110,21 +118,24 @@ __global__ __launch_bounds__(64 * kUnpermuteWaves) void unpermute_kernel(
   // slots past top_k read their token's first slot and weigh 0; chunks past
   // the row end are clamped to its last chunk and not stored: every load is in
   // bounds and used, so all of them go out before the reduction
-  const int c[2] = {cb + lane, cb + 64 + lane};
-  const int cr[2] = {min(c[0], h8 - 1), min(c[1], h8 - 1)};
-  uint4 v[2][MAXK];
+  int c[CPL], cr[CPL];
 #pragma unroll
-  for (int j = 0; j < MAXK; ++j) {
-    v[0][j] = y[row[j] + cr[0]];
-    v[1][j] = y[row[j] + cr[1]];
+  for (int h = 0; h < CPL; ++h) {
+    c[h] = cb + h * 64 + lane;
+    cr[h] = min(c[h], h8 - 1);
   }
-  uint4 a[2] = {};
+  uint4 v[CPL][MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j)
+#pragma unroll
+    for (int h = 0; h < CPL; ++h) v[h][j] = moe::load_stream16(y + row[j] + cr[h]);
+  uint4 a[CPL] = {};
   if (addend != nullptr) {
-    a[0] = addend[t * h8 + cr[0]];
-    a[1] = addend[t * h8 + cr[1]];
+#pragma unroll
+    for (int h = 0; h < CPL; ++h) a[h] = moe::load_stream16(addend + t * h8 + cr[h]);
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < CPL; ++h) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
