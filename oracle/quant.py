@@ -10,6 +10,11 @@ xtuner #2089 ("Summary", "Changes") describes the kernels this restates:
     both layouts in one pass, equal byte for byte to running the SwiGLU and
     the two quantizers one after the other ("Correctness"; the review thread
     asks for bitwise comparisons).
+  * per_tile_quant_with_trans_per_block / per_tile_quant_with_trans_per_tile:
+    the same two layouts without the SwiGLU, on an activation whose rows are
+    grouped by expert; the transposed copy is "expand_128x" per group (its
+    tests use group sizes such as [0, 1, 127, 128, 129] with 6144 columns),
+    and its scales are per 128x128 block or per 128-row tile of one column.
 The workload fixes the format (OCP e4m3, max 448) and the fp32 scale
 amax / 448.
 
@@ -22,6 +27,14 @@ Readings where the pages are silent (each side implements the same):
     block's amax runs over real rows only.
   * The SwiGLU value quantized is the bf16 one (see moe.swiglu), which is what
     makes the fused kernel equal to the unfused pair.
+  * Grouped ("expand_128x") transposed layout: the groups are consecutive row
+    ranges of the given sizes; group g's rows fill ceil(s_g/128)*128 columns of
+    q_t starting at the sum of the previous groups' padded sizes (an empty
+    group takes none), pad columns hold 0x00, and a 128-row tile never spans
+    two groups. Per-block scales: s_t [K/128, m_pad/128]; per-tile scales (one
+    per column and 128-row tile of a group, amax over its real rows): s_t
+    [K, m_pad/128]. Columns past the groups' padded total (when the caller's
+    width m_pad is larger) hold 0x00 and their scales 0.
 """
 from __future__ import annotations
 
@@ -82,3 +95,65 @@ def swiglu_quant_fp8(gate_up_bits: np.ndarray, F: int) -> Dict[str, np.ndarray]:
     res = quant_fp8(h)
     res["h"] = h
     return res
+
+
+def expand_128x_starts(group_sizes) -> tuple:
+    """First q_t column of each group in the expanded layout, and the padded total."""
+    padded = [-(-int(n) // TILE) * TILE for n in group_sizes]
+    starts, acc = [], 0
+    for p in padded:
+        starts.append(acc)
+        acc += p
+    return starts, acc
+
+
+def quant_fp8_grouped(h_bits: np.ndarray, group_sizes=None, trans: str = "block",
+                      m_pad=None) -> Dict[str, np.ndarray]:
+    """Row layout (1x128 tiles) and the grouped, expand_128x transposed layout of bf16 h [M, K].
+
+    group_sizes: row counts of consecutive groups summing to M (None: one
+    group of M rows). trans: "block" (one scale per 128x128 block) or "tile"
+    (one scale per column and 128-row tile). m_pad: width of q_t, a multiple
+    of 128 no smaller than the groups' padded total (None: that total).
+    """
+    h = bf16_to_f32(np.asarray(h_bits))
+    M, K = h.shape
+    if K % TILE != 0:
+        raise ValueError("K must be a multiple of 128")
+    if trans not in ("block", "tile"):
+        raise ValueError("trans must be 'block' or 'tile'")
+    sizes = [M] if group_sizes is None else [int(n) for n in group_sizes]
+    if any(n < 0 for n in sizes) or sum(sizes) != M:
+        raise ValueError("group sizes must be non-negative and sum to M")
+    starts, total = expand_128x_starts(sizes)
+    m_pad = total if m_pad is None else int(m_pad)
+    if m_pad < total or m_pad % TILE != 0:
+        raise ValueError("m_pad must be a multiple of 128 covering every group's padded rows")
+    nt = K // TILE
+
+    # row layout: as quant_fp8, independent of the groups
+    ht = h.reshape(M, nt, TILE)
+    amax_row = np.abs(ht).max(axis=2, initial=F32(0)).astype(F32)
+    s_row, q_row = _tile_codes(ht, amax_row[:, :, None])
+
+    q_t = np.zeros((K, m_pad), dtype=np.uint8)
+    s_t = np.zeros((nt if trans == "block" else K, m_pad // TILE), dtype=F32)
+    row0 = 0
+    for n, col0 in zip(sizes, starts):
+        for j in range(-(-n // TILE)):
+            r0, r1 = row0 + j * TILE, min(row0 + n, row0 + (j + 1) * TILE)
+            c0 = col0 + j * TILE
+            tile = h[r0:r1]                                             # [rows, K]
+            if trans == "block":
+                for fb in range(nt):
+                    blk = tile[:, fb * TILE:(fb + 1) * TILE]
+                    s, q = _tile_codes(blk, np.abs(blk).max(initial=F32(0)).astype(F32))
+                    s_t[fb, c0 // TILE] = s
+                    q_t[fb * TILE:(fb + 1) * TILE, c0:c0 + (r1 - r0)] = q.T
+            else:
+                amax_col = np.abs(tile).max(axis=0, initial=F32(0)).astype(F32)    # [K]
+                s, q = _tile_codes(tile, amax_col[None, :])
+                s_t[:, c0 // TILE] = s
+                q_t[:, c0:c0 + (r1 - r0)] = q.T
+        row0 += n
+    return {"q_row": q_row.reshape(M, K), "s_row": s_row.reshape(M, nt), "q_t": q_t, "s_t": s_t}

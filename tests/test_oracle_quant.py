@@ -82,3 +82,109 @@ def test_quant_invariants_on_workload_rows():
     q2 = oracle.quant_fp8(oracle.swiglu(x, F))
     for key in ("q_row", "s_row", "q_t", "s_t"):
         assert np.array_equal(q[key], q2[key])
+
+
+# ------------------------------------------------ grouped (expand_128x) --
+
+PAGE_GROUPS = [0, 1, 127, 128, 129]     # the grouped quantizers' test sizes in xtuner #2089
+
+
+def _grouped_h(sizes, K, key=81):
+    M = int(sum(sizes))
+    return moe_synth.bits16(moe_synth.normal_bf16(moe_synth.tensor_key(key, M, K), (M, K), 1.0))
+
+
+def test_expand_128x_offsets_of_the_page_sizes():
+    """[0, 1, 127, 128, 129] rows expand to [0, 128, 128, 128, 256] columns:
+    groups start at columns 0, 0, 128, 256, 384 of a 640-column q_t."""
+    starts, total = oracle.expand_128x_starts(PAGE_GROUPS)
+    assert starts == [0, 0, 128, 256, 384] and total == 640
+    h = _grouped_h(PAGE_GROUPS, 256)
+    for trans, s_rows in (("block", 2), ("tile", 256)):
+        q = oracle.quant_fp8_grouped(h, PAGE_GROUPS, trans)
+        assert q["q_t"].shape == (256, 640) and q["s_t"].shape == (s_rows, 5)
+        assert q["q_row"].shape == (385, 256) and q["s_row"].shape == (385, 2)
+        # pad columns of each group are zero: group 1 uses 1 of 128, group 2 127, group 4 129 of 256
+        assert not q["q_t"][:, 1:128].any() and not q["q_t"][:, 255:256].any()
+        assert not q["q_t"][:, 384 + 129:].any()
+
+
+def test_grouped_block_mode_with_one_group_is_the_plain_quantizer():
+    for M in (1, 127, 300):
+        h = _grouped_h([M], 256, key=82)
+        a, b = oracle.quant_fp8_grouped(h, None, "block"), oracle.quant_fp8(h)
+        for k in ("q_row", "s_row", "q_t", "s_t"):
+            assert np.array_equal(a[k], b[k]), (M, k)
+
+
+@pytest.mark.parametrize("sizes", [PAGE_GROUPS, [300, 0, 0, 5, 256]])
+def test_grouped_layout_is_each_group_quantized_alone(sizes):
+    """Group g's columns of q_t (and s_t) are what the plain quantizer gives
+    for g's rows alone, at the group's expanded offset; the row layout is the
+    plain one of all rows."""
+    K = 256
+    h = _grouped_h(sizes, K, key=83)
+    q = oracle.quant_fp8_grouped(h, sizes, "block", m_pad=1024)
+    whole = oracle.quant_fp8(h)
+    assert np.array_equal(q["q_row"], whole["q_row"]) and np.array_equal(q["s_row"], whole["s_row"])
+    starts, total = oracle.expand_128x_starts(sizes)
+    r0 = 0
+    for n, c0 in zip(sizes, starts):
+        if n:
+            alone = oracle.quant_fp8(h[r0:r0 + n])
+            w = alone["q_t"].shape[1]
+            assert np.array_equal(q["q_t"][:, c0:c0 + w], alone["q_t"])
+            assert np.array_equal(q["s_t"][:, c0 // 128:(c0 + w) // 128], alone["s_t"])
+        r0 += n
+    assert not q["q_t"][:, total:].any() and not q["s_t"][:, total // 128:].any()
+
+
+@pytest.mark.parametrize("sizes", [PAGE_GROUPS, [1, 300]])
+def test_grouped_tile_mode_is_the_row_quantizer_on_each_transposed_group(sizes):
+    """Per-tile transposed scales run along the rows of one column, 128 rows of
+    a group at a time: that is the row-layout (1x128) quantizer applied to the
+    group's transpose, zero-padded to its expanded width (zeros change no
+    amax and encode as 0x00)."""
+    K = 256
+    h = _grouped_h(sizes, K, key=84)
+    q = oracle.quant_fp8_grouped(h, sizes, "tile")
+    starts, _ = oracle.expand_128x_starts(sizes)
+    r0 = 0
+    for n, c0 in zip(sizes, starts):
+        if n:
+            w = -(-n // 128) * 128
+            ht = np.zeros((K, w), np.uint16)
+            ht[:, :n] = h[r0:r0 + n].T
+            rq = oracle.quant_fp8(ht)
+            assert np.array_equal(q["q_t"][:, c0:c0 + w], rq["q_row"])
+            assert np.array_equal(q["s_t"][:, c0 // 128:(c0 + w) // 128], rq["s_row"])
+        r0 += n
+
+
+def test_grouped_tile_mode_brute_force():
+    """Per-element check of a few tiles: scale = fl32(amax/448) over the
+    tile's real rows of one column, code = e4m3(fl32(h/s))."""
+    sizes = [5, 140]
+    h = _grouped_h(sizes, 128, key=85)
+    hf = nm.bf16_to_f32(h)
+    q = oracle.quant_fp8_grouped(h, sizes, "tile")
+    # group 1, second tile: rows 5 + 128 .. 5 + 139 -> columns 128 + 128 .. 128 + 139
+    for col in (0, 63, 127):
+        rows = range(133, 145)
+        amax = max(abs(float(hf[m, col])) for m in rows)
+        s = np.float32(np.float32(amax) / np.float32(448.0))
+        assert q["s_t"][col, 2] == s
+        for m in rows:
+            code = nm.e4m3_encode(np.array([np.float32(hf[m, col]) / s], np.float32))[0]
+            assert q["q_t"][col, 256 + (m - 133)] == code
+    assert not q["q_t"][:, 5:128].any() and not q["q_t"][:, 268:].any()
+
+
+def test_grouped_rejects_bad_sizes():
+    h = _grouped_h([4], 128, key=86)
+    with pytest.raises(ValueError):
+        oracle.quant_fp8_grouped(h, [3], "block")
+    with pytest.raises(ValueError):
+        oracle.quant_fp8_grouped(h, [4], "block", m_pad=64)
+    with pytest.raises(ValueError):
+        oracle.quant_fp8_grouped(h, [4], "row")
