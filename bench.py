@@ -22,7 +22,9 @@ prefill and decode shapes when the DeepSeek-V3 prefill is the primary one) and
 reports each one's ms per forward, TFLOP/s and per-kernel figures.
 `aligned_grouped_gemm` times the grouped GEMM alone on the aligned shapes of
 the pages' grouped-GEMM baseline table (E groups of M rows each), with that
-table's H200 figure beside each case as context.
+table's H200 figure beside each case as context. `grouped_quant` times the
+grouped (expand_128x) FP8 quantizer on the pages' single-kernel benchmark
+shapes.
 """
 from __future__ import annotations
 
@@ -243,6 +245,48 @@ def aligned_gemm_table(names, steps, warmup, ev, dev):
     return out
 
 
+def grouped_quant_table(steps, warmup, ev, dev):
+    """The 1x128-tile FP8 quantizer with the grouped expand_128x transposed
+    layout on the pages' single-kernel benchmark shapes (256 expert groups),
+    per-block and per-tile transposed scales; HIP events around each launch,
+    a 512 MiB read between launches."""
+    import torch
+    import moe_synth
+    import mixture_experts_routed_moe_amd as mx
+    out = {}
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    for name, per_tile in (("quant_131072x6144_e256", False), ("quant_131072x6144_e256", True),
+                           ("swiglu_quant_131072x8192_e256", False)):
+        case = moe_synth.GROUPED_QUANT_CASES[name]
+        sizes = moe_synth.grouped_quant_sizes(case)
+        x = moe_synth.grouped_quant_input(case, dev)
+        gs = torch.as_tensor(sizes, device=dev)
+        m_pad = int(((sizes + 127) // 128).sum() * 128)
+        bufs = mx.tile_quant_fp8(x, gs, per_tile=per_tile, swiglu=case.swiglu, m_pad=m_pad)
+        for _ in range(warmup):
+            mx.tile_quant_fp8(x, gs, per_tile=per_tile, swiglu=case.swiglu, m_pad=m_pad, out=bufs)
+        evs = []
+        for _ in range(max(10, steps)):
+            flush.sum()
+            a = ev()
+            mx.tile_quant_fp8(x, gs, per_tile=per_tile, swiglu=case.swiglu, m_pad=m_pad, out=bufs)
+            evs.append((a, ev()))
+        torch.cuda.synchronize()
+        ms_list = [a.elapsed_time(b) for a, b in evs]
+        ms = sum(ms_list) / len(ms_list)
+        K, M = case.K, case.M
+        byts = (M * K * 2 * (2 if case.swiglu else 1) + M * K + 4 * M * K // 128 + K * m_pad
+                + 4 * (K if per_tile else K // 128) * (m_pad // 128))
+        key = f"{name}_{'per_tile' if per_tile else 'per_block'}"
+        out[key] = {"M": M, "K": K, "E": case.E, "swiglu": case.swiglu, "m_pad": m_pad, "ms": round(ms, 4),
+                    **pct(ms_list), "gbs": round(byts / ms / 1e6, 1), "hbm_frac": round(byts / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        print(f"# grouped quant {key}: {ms * 1e3:.1f} us, {byts / ms / 1e6:.0f} GB/s", file=sys.stderr, flush=True)
+        del x, bufs, gs
+        torch.cuda.empty_cache()
+    del flush
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -318,6 +362,8 @@ def main():
         gemm_names = args.gemm_cases.split(",")
     gemm_table = aligned_gemm_table(gemm_names, args.steps, args.warmup, ev, dev) if gemm_names else {}
 
+    grouped_quant = {} if args.only_primary else grouped_quant_table(args.steps, args.warmup, ev, dev)
+
     # fused SwiGLU + FP8 quantizer on its own workload, HIP events around each launch
     qM, qF = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
     for _ in range(5):
@@ -390,6 +436,7 @@ def main():
         "kernels": kernels,
         "other_workloads": others,
         "aligned_grouped_gemm": gemm_table,
+        "grouped_quant": grouped_quant,
     }
     print(json.dumps(line), flush=True)
 

@@ -185,6 +185,41 @@ int moe_unpermute(const uint16_t* y, const int32_t* pair_to_row, const float* to
 int swiglu_quant_fp8(const uint16_t* gate_up, int64_t M, int F, uint8_t* q_row, float* s_row,
                      uint8_t* q_t, float* s_t, hipStream_t stream);
 
+/* The 1x128-tile FP8 quantizer family of xtuner #2089 ("Changes":
+ * per_tile_quant_with_trans_per_block, per_tile_quant_with_trans_per_tile,
+ * and with swiglu=1 swiglu_per_tile_quant_with_trans_per_block), on rows
+ * grouped by expert with the "expand_128x" transposed layout.
+ *   x            swiglu=0: the bf16 activation [M, K]; swiglu=1: gate_up
+ *                [M, 2K] (gate columns first), quantizing h = swiglu(x) [M, K]
+ *                exactly as swiglu_quant_fp8 does.
+ *   group_sizes  device int32 [E], consecutive row ranges summing to M, or
+ *                NULL for one group of M rows (E is then ignored).
+ *   m_pad        width of q_t: a multiple of 128 no smaller than the groups'
+ *                padded total sum(ceil(group_sizes[e]/128)*128) (with NULL
+ *                groups, ceil(M/128)*128); tile_quant_fp8_m_pad_bound(M, E)
+ *                always suffices. With grouped rows the kernel cannot check
+ *                it: a group past m_pad gets no outputs at all.
+ *   row layout   q_row [M, K] uint8, s_row [M, K/128] float32, per 1x128 tile
+ *                of a row (as swiglu_quant_fp8).
+ *   transposed   q_t [K, m_pad] uint8: group e's rows fill ceil(gs/128)*128
+ *                columns starting at the previous groups' padded total; pad
+ *                columns and columns past the total are 0x00.
+ *                per_tile=0: s_t [K/128, m_pad/128], one scale per 128x128
+ *                block of a group (amax over real rows);
+ *                per_tile=1: s_t [K, m_pad/128], one scale per column and
+ *                128-row tile of a group. Scales past the total are 0.
+ * Scales fl32(amax/448), codes e4m3(fl32(h/s)), zero tiles 0x00 as above.
+ * Rows must be 16-byte aligned (x, q_row, q_t); K % 128 == 0; M, m_pad < 2^31.
+ * Returns MOE_ERR_INVALID_ARG for bad sizes or flags (nothing enqueued);
+ * M = 0 with m_pad > 0 zero-fills q_t and s_t. */
+int tile_quant_fp8(const uint16_t* x, int64_t M, int K, int swiglu, const int32_t* group_sizes, int E,
+                   int per_tile, int64_t m_pad, uint8_t* q_row, float* s_row, uint8_t* q_t, float* s_t,
+                   hipStream_t stream);
+
+/* 128 * (ceil(M/128) + E): a q_t width that covers any grouping of M rows into
+ * E groups (host-only; -1 for negative arguments). */
+int64_t tile_quant_fp8_m_pad_bound(int64_t M, int E);
+
 #ifdef __cplusplus
 }
 #endif

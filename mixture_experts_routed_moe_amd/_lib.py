@@ -31,7 +31,7 @@ class MoeError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 SCORING = {"softmax": 0, "sigmoid": 1}
 
 
@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
         "grouped_gemm_down": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, P, P]),
         "moe_unpermute": (I, [P, P, P, I64, I, I, F, P, P, P]),
         "swiglu_quant_fp8": (I, [P, I64, I, P, P, P, P, P]),
+        "tile_quant_fp8": (I, [P, I64, I, I, P, I, I, I64, P, P, P, P, P]),
+        "tile_quant_fp8_m_pad_bound": (I64, [I64, I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -70,7 +72,8 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_workspace_bytes",
            "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up", "swiglu",
-           "grouped_gemm_down", "moe_unpermute", "swiglu_quant_fp8")
+           "grouped_gemm_down", "moe_unpermute", "swiglu_quant_fp8", "tile_quant_fp8",
+           "tile_quant_fp8_m_pad_bound")
 
 
 def lib() -> ctypes.CDLL:
@@ -252,4 +255,31 @@ def swiglu_quant_fp8(gate_up: torch.Tensor, out: Optional[Dict[str, torch.Tensor
     _call("swiglu_quant_fp8", _ptr(gate_up, torch.bfloat16, "gate_up"), M, F, _ptr(q_row, torch.uint8, "q_row"),
           _ptr(s_row, torch.float32, "s_row"), _ptr(q_t, torch.uint8, "q_t"), _ptr(s_t, torch.float32, "s_t"),
           _stream(gate_up))
+    return {"q_row": q_row, "s_row": s_row, "q_t": q_t, "s_t": s_t}
+
+
+def tile_quant_fp8_m_pad_bound(M: int, E: int) -> int:
+    return int(lib().tile_quant_fp8_m_pad_bound(M, E))
+
+
+def tile_quant_fp8(x: torch.Tensor, group_sizes: Optional[torch.Tensor] = None, per_tile: bool = False,
+                   swiglu: bool = False, m_pad: Optional[int] = None,
+                   out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Row (1x128) and grouped expand_128x transposed e4m3 quantization of x
+    ([M, K] bf16, or gate_up [M, 2K] with swiglu=True). Without m_pad, q_t is
+    ceil(M/128)*128 wide for one group and tile_quant_fp8_m_pad_bound(M, E)
+    wide for E groups (the group sizes stay on the device)."""
+    M, W = x.shape
+    K = W // 2 if swiglu else W
+    E = 0 if group_sizes is None else int(group_sizes.numel())
+    if m_pad is None:
+        m_pad = -(-M // 128) * 128 if group_sizes is None else tile_quant_fp8_m_pad_bound(M, E)
+    o = out or {}
+    q_row = _out(o.get("q_row"), (M, K), torch.uint8, x, "q_row")
+    s_row = _out(o.get("s_row"), (M, K // 128), torch.float32, x, "s_row")
+    q_t = _out(o.get("q_t"), (K, m_pad), torch.uint8, x, "q_t")
+    s_t = _out(o.get("s_t"), ((K if per_tile else K // 128), m_pad // 128), torch.float32, x, "s_t")
+    _call("tile_quant_fp8", _ptr(x, torch.bfloat16, "x"), M, K, int(swiglu), _ptr(group_sizes, torch.int32, "group_sizes"),
+          E, int(per_tile), m_pad, _ptr(q_row, torch.uint8, "q_row"), _ptr(s_row, torch.float32, "s_row"),
+          _ptr(q_t, torch.uint8, "q_t"), _ptr(s_t, torch.float32, "s_t"), _stream(x))
     return {"q_row": q_row, "s_row": s_row, "q_t": q_t, "s_t": s_t}

@@ -240,6 +240,47 @@ def gemm_w(case: GemmCase, device="cpu", experts: Optional[Sequence[int]] = None
     return torch.stack([normal_bf16(key, (case.N, case.K), sigma, device, start=e * per) for e in experts])
 
 
+TAG_GQ_X, TAG_GQ_SIZES = 10, 11
+
+
+@dataclasses.dataclass(frozen=True)
+class GroupedQuantCase:
+    """Grouped 1x128-tile FP8 quantizer workload (xtuner #2089, "Single-kernel
+    benchmark" and its tests): x [M, K] bf16 ~N(0,1) (gate_up [M, 2K] when
+    swiglu), rows in E consecutive expert groups. `sizes` fixes the group
+    sizes; otherwise they are a seeded multinomial split of M over E equally
+    likely experts (unaligned counts, the pages give no distribution)."""
+    cid: int
+    name: str
+    M: int
+    K: int
+    E: int
+    swiglu: bool = False
+    sizes: Optional[tuple] = None
+
+
+GROUPED_QUANT_CASES = {c.name: c for c in (
+    GroupedQuantCase(40, "quant_groups_0_1_127_128_129_k6144", 385, 6144, 5, sizes=(0, 1, 127, 128, 129)),
+    GroupedQuantCase(41, "quant_131072x6144_e256", 131072, 6144, 256),
+    GroupedQuantCase(42, "swiglu_quant_131072x8192_e256", 131072, 4096, 256, swiglu=True),
+)}
+
+
+def grouped_quant_sizes(case: GroupedQuantCase) -> np.ndarray:
+    """int32 [E] group sizes summing to M."""
+    if case.sizes is not None:
+        return np.asarray(case.sizes, dtype=np.int32)
+    rng = np.random.Generator(np.random.PCG64(tensor_key(case.cid, TAG_GQ_SIZES)))
+    return rng.multinomial(case.M, np.full(case.E, 1.0 / case.E)).astype(np.int32)
+
+
+def grouped_quant_input(case: GroupedQuantCase, device="cpu", rows: Optional[slice] = None) -> torch.Tensor:
+    """x [M, K] (or [M, 2K] with swiglu), or the given rows of it."""
+    w = (2 if case.swiglu else 1) * case.K
+    r0, r1 = (0, case.M) if rows is None else (rows.start, rows.stop)
+    return normal_bf16(tensor_key(case.cid, TAG_GQ_X), (r1 - r0, w), 1.0, device, start=r0 * w)
+
+
 def zipf_bias(cfg: MoEConfig) -> np.ndarray:
     """Per-expert logit bias -s*ln(rank), rank a seeded permutation of 1..E (float32)."""
     rng = np.random.Generator(np.random.PCG64(tensor_key(cfg.cid, TAG_BIAS)))

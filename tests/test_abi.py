@@ -61,7 +61,7 @@ def test_num_blocks_matches_worked_example(lib):
     assert lib.moe_num_blocks(100, 3, 64, 128) == 2 + 6
     assert lib.moe_num_blocks(10, 3, 64, 96) == -1
     assert lib.moe_num_blocks(0, 8, 64, 64) == 8
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_workspace_size(lib):
@@ -90,6 +90,20 @@ def test_argument_errors_return_before_launch(lib):
     lib.swiglu_quant_fp8.argtypes = [P, c.c_int64, c.c_int] + [P] * 5
     assert lib.swiglu_quant_fp8(None, 4, 100, None, None, None, None, None) == -1
     assert lib.swiglu_quant_fp8(None, 0, 256, None, None, None, None, None) == 0
+    # the grouped tile quantizer: sizes, flags and widths are checked before any launch
+    lib.tile_quant_fp8.argtypes = [P, c.c_int64, c.c_int, c.c_int, P, c.c_int, c.c_int, c.c_int64] + [P] * 5
+    lib.tile_quant_fp8_m_pad_bound.restype = c.c_int64
+    lib.tile_quant_fp8_m_pad_bound.argtypes = [c.c_int64, c.c_int]
+    assert lib.tile_quant_fp8_m_pad_bound(385, 5) == 128 * (4 + 5)
+    assert lib.tile_quant_fp8_m_pad_bound(-1, 5) == -1
+    assert lib.tile_quant_fp8(None, 4, 100, 0, None, 0, 0, 128, None, None, None, None, None) == -1   # K % 128
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 100, None, None, None, None, None) == -1   # m_pad % 128
+    assert lib.tile_quant_fp8(None, 300, 128, 0, None, 0, 0, 256, None, None, None, None, None) == -1  # m_pad < 384
+    assert lib.tile_quant_fp8(None, 4, 128, 2, None, 0, 0, 128, None, None, None, None, None) == -1   # swiglu flag
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 3, 128, None, None, None, None, None) == -1   # per_tile flag
+    assert lib.tile_quant_fp8(None, 4, 128, 0, 1, 0, 0, 128, None, None, None, None, None) == -1      # E < 1 with groups
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 128, None, None, None, None, None) == -1   # null outputs
+    assert lib.tile_quant_fp8(None, 0, 128, 0, None, 0, 0, 0, None, None, None, None, None) == 0      # nothing to do
     # routing limits
     lib.moe_topk_softmax.argtypes = [P, P, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int, P, P, P]
     assert lib.moe_topk_softmax(None, None, 4, 2048, 8, 0, 1, None, None, None) == -2

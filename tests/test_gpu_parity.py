@@ -3,6 +3,7 @@ and end to end. Every stage is fed the same inputs on both sides; integer
 tables, permutations and FP8 bytes must match exactly, bf16 results within
 atol = rtol = 1e-2, routing weights within 2e-6 relative.
 """
+import dataclasses
 import json
 import os
 
@@ -445,6 +446,108 @@ def test_swiglu_quant_full_size_sampled_blocks():
     q = mx.swiglu_quant_fp8(x)
     for r0 in (0, 128 * 97, M - 128):
         _quant_compare(bits(x[r0:r0 + 128]), F, q, rows=(r0, r0 + 128))
+
+
+# ------------------------------------------- grouped tile quantizer --
+
+def _tq_equal(got, ref, name, rows=None, cols=None, scols=None):
+    for k in ("q_row", "s_row"):
+        g = host(got[k]) if rows is None else host(got[k][rows[0]:rows[1]])
+        assert np.array_equal(g.view(np.uint8 if k == "q_row" else np.uint32),
+                              ref[k].view(np.uint8 if k == "q_row" else np.uint32)), (name, k)
+    qt = host(got["q_t"]) if cols is None else host(got["q_t"][:, cols[0]:cols[1]])
+    st = host(got["s_t"]) if scols is None else host(got["s_t"][:, scols[0]:scols[1]])
+    assert np.array_equal(qt, ref["q_t"]), (name, "q_t")
+    assert np.array_equal(st.view(np.uint32), ref["s_t"].view(np.uint32)), (name, "s_t")
+
+
+@pytest.mark.parametrize("per_tile", [False, True])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_tile_quant_page_group_sizes(per_tile, swiglu):
+    """Group sizes [0, 1, 127, 128, 129] with K=6144 (the grouped quantizers'
+    test case), at the exact padded width and at the bound width (the columns
+    past the groups' total must come back zero), every output byte."""
+    d = dev()
+    case = dataclasses.replace(moe_synth.GROUPED_QUANT_CASES["quant_groups_0_1_127_128_129_k6144"], swiglu=swiglu)
+    sizes = moe_synth.grouped_quant_sizes(case)
+    x = moe_synth.grouped_quant_input(case, d)
+    h = oracle.swiglu(bits(x), case.K) if swiglu else bits(x)
+    trans = "tile" if per_tile else "block"
+    gs = _t(sizes, d)
+    for m_pad in (640, mx.tile_quant_fp8_m_pad_bound(case.M, case.E)):
+        q = mx.tile_quant_fp8(x, gs, per_tile=per_tile, swiglu=swiglu, m_pad=m_pad)
+        ref = oracle.quant_fp8_grouped(h, sizes, trans, m_pad=m_pad)
+        _tq_equal(q, ref, f"page groups m_pad={m_pad}")
+
+
+@pytest.mark.parametrize("per_tile", [False, True])
+def test_tile_quant_random_groups_and_overwrite(per_tile):
+    """Random group sizes (empty groups, tiny groups, several blocks), outputs
+    pre-filled with 0xFF / NaN so every byte the contract covers must be written."""
+    d = dev()
+    rng = np.random.default_rng(90 + per_tile)
+    sizes = rng.choice([0, 1, 5, 127, 128, 129, 300, 513], size=11).astype(np.int32)
+    M, K = int(sizes.sum()), 256
+    x = moe_synth.normal_bf16(moe_synth.tensor_key(91, M, per_tile), (M, K), 1.0, d)
+    m_pad = mx.tile_quant_fp8_m_pad_bound(M, len(sizes))
+    out = {"q_row": torch.full((M, K), 0xFF, dtype=torch.uint8, device=d),
+           "s_row": torch.full((M, K // 128), float("nan"), device=d),
+           "q_t": torch.full((K, m_pad), 0xFF, dtype=torch.uint8, device=d),
+           "s_t": torch.full(((K if per_tile else K // 128), m_pad // 128), float("nan"), device=d)}
+    q = mx.tile_quant_fp8(x, _t(sizes, d), per_tile=per_tile, m_pad=m_pad, out=out)
+    ref = oracle.quant_fp8_grouped(bits(x), sizes, "tile" if per_tile else "block", m_pad=m_pad)
+    _tq_equal(q, ref, f"random groups {sizes.tolist()}")
+
+
+def test_tile_quant_ungrouped_equals_swiglu_quant_fp8():
+    """One group, block scales, SwiGLU input: the same bytes as swiglu_quant_fp8
+    (and as quantizing the unfused SwiGLU output without it)."""
+    d = dev()
+    for M in (1, 129, 1000):
+        x = moe_synth.quant_input(M, 256, d)
+        a = mx.swiglu_quant_fp8(x)
+        b = mx.tile_quant_fp8(x, None, per_tile=False, swiglu=True)
+        c = mx.tile_quant_fp8(mx.swiglu(x), None)
+        for k in a:
+            assert torch.equal(a[k], b[k]), (M, k)
+            assert torch.equal(a[k], c[k]), (M, k, "h")
+
+
+def test_tile_quant_zero_rows_zero_fills():
+    d = dev()
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=d)
+    gs = _t(np.zeros(3, np.int32), d)
+    q = mx.tile_quant_fp8(x, gs, per_tile=True, m_pad=384,
+                          out={"q_t": torch.full((256, 384), 7, dtype=torch.uint8, device=d),
+                               "s_t": torch.full((256, 3), 7.0, device=d)})
+    assert not q["q_t"].any() and not q["s_t"].any()
+
+
+@pytest.mark.parametrize("name,per_tile", [("quant_131072x6144_e256", False), ("quant_131072x6144_e256", True),
+                                           ("swiglu_quant_131072x8192_e256", False)])
+def test_tile_quant_benchmark_shapes_sampled_groups(name, per_tile):
+    """The benchmark shapes at full size, launched as the benchmark launches
+    them: the row layout of sampled groups' rows, and their transposed columns
+    and scales (each group's part is the oracle run on that group's rows
+    alone, at its expanded offset); columns past the total are zero."""
+    d = dev()
+    case = moe_synth.GROUPED_QUANT_CASES[name]
+    say("tile quant", name, per_tile)
+    sizes = moe_synth.grouped_quant_sizes(case)
+    x = moe_synth.grouped_quant_input(case, d)
+    q = mx.tile_quant_fp8(x, _t(sizes, d), per_tile=per_tile, swiglu=case.swiglu)
+    starts, total = oracle.expand_128x_starts(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    trans = "tile" if per_tile else "block"
+    for g in sorted({0, 1, len(sizes) - 1, *np.random.default_rng(case.cid).choice(len(sizes), 3).tolist()}):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        xb = bits(x[r0:r1])
+        h = oracle.swiglu(xb, case.K) if case.swiglu else xb
+        ref = oracle.quant_fp8_grouped(h, None, trans)
+        w = ref["q_t"].shape[1]
+        _tq_equal(q, ref, f"{name} group {g}", rows=(r0, r1), cols=(starts[g], starts[g] + w),
+                  scols=(starts[g] // 128, (starts[g] + w) // 128))
+    assert not q["q_t"][:, total:].any() and not q["s_t"][:, total // 128:].any()
 
 
 # ----------------------------------------------------------- end to end --
