@@ -15,11 +15,12 @@ from .numerics import (bf16_to_f32, bf16_to_f64, e4m3_decode, e4m3_encode, exp32
                        round_bf16, silu32, to_bf16)
 from .moe import (block_decode, dispatch_tables, forward, grouped_gemm, num_blocks,
                   permute, route, shared_expert, swiglu, unpermute)
-from .quant import expand_128x_starts, quant_fp8, quant_fp8_grouped, swiglu_quant_fp8
+from .quant import (block_quant_fp8, expand_128x_starts, grouped_gemm_fp8, quant_fp8, quant_fp8_grouped,
+                    swiglu_quant_fp8)
 
 __all__ = [
     "bf16_to_f32", "bf16_to_f64", "e4m3_decode", "e4m3_encode", "exp32", "round_bf16",
     "silu32", "to_bf16", "block_decode", "dispatch_tables", "forward", "grouped_gemm",
     "num_blocks", "permute", "route", "shared_expert", "swiglu", "unpermute", "quant_fp8",
-    "swiglu_quant_fp8", "quant_fp8_grouped", "expand_128x_starts",
+    "swiglu_quant_fp8", "quant_fp8_grouped", "expand_128x_starts", "block_quant_fp8", "grouped_gemm_fp8",
 ]

@@ -43,7 +43,7 @@ from typing import Dict
 import numpy as np
 
 from .moe import swiglu
-from .numerics import E4M3_MAX, bf16_to_f32, e4m3_encode
+from .numerics import E4M3_MAX, bf16_to_f32, bf16_to_f64, e4m3_decode, e4m3_encode, to_bf16
 
 TILE = 128
 F32 = np.float32
@@ -157,3 +157,45 @@ def quant_fp8_grouped(h_bits: np.ndarray, group_sizes=None, trans: str = "block"
                 q_t[:, c0:c0 + (r1 - r0)] = q.T
         row0 += n
     return {"q_row": q_row.reshape(M, K), "s_row": s_row.reshape(M, nt), "q_t": q_t, "s_t": s_t}
+
+
+def block_quant_fp8(w_bits: np.ndarray) -> Dict[str, np.ndarray]:
+    """e4m3 quantization of a bf16 weight matrix [N, K] with one scale per
+    128x128 block, kept in the weight's own row-major layout: q [N, K] uint8,
+    s [N/128, K/128] float32, s = fl32(amax/448), code = e4m3(fl32(w/s)).
+
+    The FP8 grouped-GEMM item of the MoE path pairs the 1x128-tile activation
+    codes with "128x128-block-scaled e4m3 weights"; a block of the weight is
+    quantized exactly as a block of the transposed activation layout is.
+    """
+    w = bf16_to_f32(np.asarray(w_bits))
+    N, K = w.shape
+    if N % TILE or K % TILE:
+        raise ValueError("N and K must be multiples of 128")
+    blocks = w.reshape(N // TILE, TILE, K // TILE, TILE)
+    amax = np.abs(blocks).max(axis=(1, 3), initial=F32(0)).astype(F32)       # [N/128, K/128]
+    s, q = _tile_codes(blocks, amax[:, None, :, None])
+    return {"q": q.reshape(N, K), "s": s.reshape(N // TILE, K // TILE)}
+
+
+def grouped_gemm_fp8(qa: np.ndarray, sa: np.ndarray, qw: np.ndarray, sw: np.ndarray,
+                     group_sizes: np.ndarray, group_offsets: np.ndarray) -> np.ndarray:
+    """y[e] = bf16(A_e @ W_e^T) on block-scaled e4m3 operands, in float64:
+    A [numel, K] codes qa with one scale per row and 128-column tile sa
+    [numel, K/128] (the quantizer's row layout); W_e [N, K] codes qw[e] with
+    one scale per 128x128 block sw[e] [N/128, K/128]. Each operand is its
+    decoded code times its scale; returns uint16 bf16 bits [numel, N].
+    """
+    E, N, K = qw.shape
+    numel = qa.shape[0]
+    out = np.zeros((numel, N), dtype=np.uint16)
+    a_all = e4m3_decode(np.asarray(qa)).astype(np.float64) * np.repeat(np.asarray(sa, np.float64), TILE, axis=1)
+    for e in range(E):
+        n = int(group_sizes[e])
+        if n == 0:
+            continue
+        o = int(group_offsets[e])
+        wdec = e4m3_decode(np.asarray(qw[e])).astype(np.float64)
+        wscale = np.repeat(np.repeat(np.asarray(sw[e], np.float64), TILE, axis=0), TILE, axis=1)
+        out[o:o + n] = to_bf16(a_all[o:o + n] @ (wdec * wscale).T)
+    return out

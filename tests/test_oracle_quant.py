@@ -188,3 +188,61 @@ def test_grouped_rejects_bad_sizes():
         oracle.quant_fp8_grouped(h, [4], "block", m_pad=64)
     with pytest.raises(ValueError):
         oracle.quant_fp8_grouped(h, [4], "row")
+
+
+# ------------------------------------------ block-scaled FP8 GEMM (oracle) --
+
+def test_block_weight_quant_is_the_transposed_activation_layout():
+    """A 128x128 block of the weight is quantized as a block of the transposed
+    activation layout: block_quant_fp8(W) == quant_fp8(W^T)'s (q_t, s_t)."""
+    w = moe_synth.bits16(moe_synth.normal_bf16(moe_synth.tensor_key(87), (256, 384), 0.05))
+    b = oracle.block_quant_fp8(w)
+    t = oracle.quant_fp8(np.ascontiguousarray(w.T))
+    assert np.array_equal(b["q"], t["q_t"]) and np.array_equal(b["s"], t["s_t"])
+    # every non-zero block holds a code of magnitude 448
+    for nb in range(2):
+        for kb in range(3):
+            blk = b["q"][nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
+            assert ((blk & 0x7F) == 0x7E).any()
+
+
+def test_fp8_gemm_exact_on_integer_codes():
+    """Codes that decode to small integers with unit scales (and power-of-two
+    scales, which commute with every rounding): the result is the exact integer
+    product, so a transposed operand, a wrong scale index or a dropped block
+    shows up. Three groups, one empty, one ragged."""
+    rng = np.random.default_rng(5)
+    sizes = np.array([3, 0, 130], np.int64)
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    M, N, K = int(sizes.sum()), 128, 256
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0])     # 0, 1, 2, 3, 4, -1, -2
+    vals = nm.e4m3_decode(ints)
+    ia = rng.integers(0, len(ints), (M, K))
+    iw = rng.integers(0, len(ints), (3, N, K))
+    qa, qw = ints[ia].astype(np.uint8), ints[iw].astype(np.uint8)
+    for sa_v, sw_v in ((1.0, 1.0), (0.5, 4.0)):
+        sa = np.full((M, K // 128), sa_v, np.float32)
+        sw = np.full((3, N // 128, K // 128), sw_v, np.float32)
+        y = oracle.grouped_gemm_fp8(qa, sa, qw, sw, sizes, offs)
+        for e in (0, 2):
+            o, n = int(offs[e]), int(sizes[e])
+            exact = (vals[ia[o:o + n]] @ vals[iw[e]].T) * sa_v * sw_v
+            assert np.array_equal(nm.bf16_to_f64(y[o:o + n]), nm.bf16_to_f64(nm.to_bf16(exact)))
+
+
+def test_fp8_gemm_scales_apply_per_block():
+    """Brute force on one output: sum over 128-column blocks of
+    (decoded a * a-scale of the row's block) * (decoded w * w-scale of its block)."""
+    rng = np.random.default_rng(6)
+    M, N, K = 4, 256, 384
+    qa = rng.integers(0, 0x7E, (M, K)).astype(np.uint8)
+    qw = rng.integers(0, 0x7E, (1, N, K)).astype(np.uint8)
+    sa = rng.uniform(0.01, 2.0, (M, K // 128)).astype(np.float32)
+    sw = rng.uniform(0.01, 2.0, (1, N // 128, K // 128)).astype(np.float32)
+    y = oracle.grouped_gemm_fp8(qa, sa, qw, sw, np.array([M]), np.array([0]))
+    for m, n in ((0, 0), (3, 255), (2, 129)):
+        acc = 0.0
+        for k in range(K):
+            acc += (nm.e4m3_decode(qa[m, k:k + 1])[0] * float(sa[m, k // 128])) * \
+                   (nm.e4m3_decode(qw[0, n, k:k + 1])[0] * float(sw[0, n // 128, k // 128]))
+        assert nm.bf16_to_f64(y[m:m + 1, n])[0] == nm.bf16_to_f64(nm.to_bf16(np.array([acc])))[0]
