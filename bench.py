@@ -24,7 +24,8 @@ reports each one's ms per forward, TFLOP/s and per-kernel figures.
 the pages' grouped-GEMM baseline table (E groups of M rows each), with that
 table's H200 figure beside each case as context. `grouped_quant` times the
 grouped (expand_128x) FP8 quantizer on the pages' single-kernel benchmark
-shapes.
+shapes; `fp8_down` the primary workload's down projection on the FP8 path
+(1x128-tile e4m3 activations, 128x128-block e4m3 weights) beside the bf16 one.
 """
 from __future__ import annotations
 
@@ -42,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def parse():
@@ -287,6 +289,39 @@ def grouped_quant_table(steps, warmup, ev, dev):
     return out
 
 
+def fp8_down(wl, steps, warmup, ev):
+    """The down projection on the FP8 path for the workload's routing: h (the
+    forward's bf16 SwiGLU output, left in the buffers by the timed forwards)
+    quantized to 1x128-tile e4m3 codes (tile_quant_fp8), then the
+    block-scaled FP8 grouped GEMM against 128x128-block e4m3 weights prepared
+    once. HIP events around each launch; FLOP as for the bf16 down."""
+    import torch
+    mx, cfg, bufs = wl.mx, wl.cfg, wl.bufs
+    qw = mx.fp8_block_quant_weights(wl.wd)
+    qa = mx.tile_quant_fp8(bufs.h, None)
+    y = torch.empty_like(bufs.y)
+    for _ in range(warmup):
+        mx.tile_quant_fp8(bufs.h, None, out=qa)
+        mx.grouped_gemm_fp8(qa["q_row"], qa["s_row"], qw["q"], qw["s"], bufs.tables, cfg.padding_m, cfg.block_m, y)
+    eq, eg = [], []
+    for _ in range(steps):
+        a = ev()
+        mx.tile_quant_fp8(bufs.h, None, out=qa)
+        b = ev()
+        mx.grouped_gemm_fp8(qa["q_row"], qa["s_row"], qw["q"], qw["s"], bufs.tables, cfg.padding_m, cfg.block_m, y)
+        eg.append((b, ev()))
+        eq.append((a, b))
+    torch.cuda.synchronize()
+    q_ms = sum(a.elapsed_time(b) for a, b in eq) / len(eq)
+    g_list = [a.elapsed_time(b) for a, b in eg]
+    g_ms = sum(g_list) / len(g_list)
+    flop = 2.0 * cfg.numel * cfg.H * cfg.F
+    return {"gemm_ms": round(g_ms, 4), **pct(g_list), "quant_h_ms": round(q_ms, 4),
+            "tflops": round(flop / (g_ms * 1e-3) / 1e12, 2),
+            "fp8_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "bf16_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -334,6 +369,11 @@ def main():
     active = int((gs > 0).sum())
     H, F, E = cfg.H, cfg.F, cfg.E
     hidden, logits, bias, wgu, wd, swgu, swd = (wl.hidden, wl.logits, wl.bias, wl.wgu, wl.wd, wl.swgu, wl.swd)
+
+    fp8 = None if args.only_primary else fp8_down(wl, args.steps, args.warmup, ev)
+    if fp8 is not None:
+        fp8["bf16_down_ms"] = round(stage_ms["down"], 4)
+        print(f"# fp8 down: {fp8['gemm_ms']:.3f} ms (bf16 {stage_ms['down']:.3f} ms)", file=sys.stderr, flush=True)
 
     # the other forward workloads of the same family, each timed the same way
     others = {}
@@ -437,6 +477,7 @@ def main():
         "other_workloads": others,
         "aligned_grouped_gemm": gemm_table,
         "grouped_quant": grouped_quant,
+        "fp8_down": fp8,
     }
     print(json.dumps(line), flush=True)
 

@@ -220,6 +220,29 @@ int tile_quant_fp8(const uint16_t* x, int64_t M, int K, int swiglu, const int32_
  * E groups (host-only; -1 for negative arguments). */
 int64_t tile_quant_fp8_m_pad_bound(int64_t M, int E);
 
+/* Weight preparation for grouped_gemm_fp8: e4m3 codes of a bf16 weight matrix
+ * w [rows, K] (for expert weights, rows = E*N) with one scale per 128x128
+ * block, in the weight's own row-major layout: q [rows, K] uint8, s [rows/128,
+ * K/128] float32, s = fl32(amax/448), code = e4m3(fl32(w/s)), an all-zero
+ * block has scale 0 and codes 0x00. rows and K multiples of 128; w and q
+ * 16-byte aligned. */
+int fp8_block_quant_weights(const uint16_t* w, int64_t rows, int K, uint8_t* q, float* s, hipStream_t stream);
+
+/* Block-scaled FP8 grouped GEMM, C[e] = A[e] @ W[e]^T on e4m3 operands (the
+ * MoE path's down projection fed by the FP8 quantizer, xtuner #2089 "Summary":
+ * W2 input quantization). A: codes qa [numel, K] with one scale per row and
+ * 128-column tile sa [numel, K/128] (tile_quant_fp8's row layout); W: codes
+ * qw [E, N, K] with one scale per 128x128 block sw [E, N/128, K/128]
+ * (fp8_block_quant_weights). y [numel, N] bf16 = the fp32-accumulated sum of
+ * the decoded products, each operand times its scale, rounded once. The four
+ * dispatch tables as for grouped_gemm_down (all NULL: one dense group, E = 1).
+ * N and K multiples of 128, block_m = 128, padding_m a multiple of 128;
+ * qa, qw, y 16-byte aligned. */
+int grouped_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                     const int32_t* group_sizes, const int32_t* group_offsets, const int32_t* group_padded_offsets,
+                     const int32_t* group_idx_for_bx, int64_t numel, int E, int N, int K, int padding_m,
+                     int block_m, uint16_t* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

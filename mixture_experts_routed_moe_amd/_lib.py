@@ -14,6 +14,7 @@ import ctypes
 import os
 from typing import Dict, Optional
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +32,7 @@ class MoeError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 SCORING = {"softmax": 0, "sigmoid": 1}
 
 
@@ -57,6 +58,8 @@ def _load() -> ctypes.CDLL:
         "swiglu_quant_fp8": (I, [P, I64, I, P, P, P, P, P]),
         "tile_quant_fp8": (I, [P, I64, I, I, P, I, I, I64, P, P, P, P, P]),
         "tile_quant_fp8_m_pad_bound": (I64, [I64, I]),
+        "fp8_block_quant_weights": (I, [P, I64, I, P, P, P]),
+        "grouped_gemm_fp8": (I, [P, P, P, P, P, P, P, P, I64, I, I, I, I, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -73,7 +76,7 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_workspace_bytes",
            "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up", "swiglu",
            "grouped_gemm_down", "moe_unpermute", "swiglu_quant_fp8", "tile_quant_fp8",
-           "tile_quant_fp8_m_pad_bound")
+           "tile_quant_fp8_m_pad_bound", "fp8_block_quant_weights", "grouped_gemm_fp8")
 
 
 def lib() -> ctypes.CDLL:
@@ -283,3 +286,31 @@ def tile_quant_fp8(x: torch.Tensor, group_sizes: Optional[torch.Tensor] = None, 
           E, int(per_tile), m_pad, _ptr(q_row, torch.uint8, "q_row"), _ptr(s_row, torch.float32, "s_row"),
           _ptr(q_t, torch.uint8, "q_t"), _ptr(s_t, torch.float32, "s_t"), _stream(x))
     return {"q_row": q_row, "s_row": s_row, "q_t": q_t, "s_t": s_t}
+
+
+def fp8_block_quant_weights(w: torch.Tensor, out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """e4m3 codes of a bf16 weight [..., N, K] with one scale per 128x128 block: q like w (uint8), s [..., N/128, K/128]."""
+    *lead, N, K = w.shape
+    rows = int(np.prod(lead, dtype=np.int64)) * N if lead else N
+    o = out or {}
+    q = _out(o.get("q"), tuple(w.shape), torch.uint8, w, "q")
+    s = _out(o.get("s"), (*lead, N // 128, K // 128), torch.float32, w, "s")
+    _call("fp8_block_quant_weights", _ptr(w, torch.bfloat16, "w"), rows, K, _ptr(q, torch.uint8, "q"),
+          _ptr(s, torch.float32, "s"), _stream(w))
+    return {"q": q, "s": s}
+
+
+def grouped_gemm_fp8(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                     tables: Optional[Dict[str, torch.Tensor]], padding_m: int, block_m: int = 128,
+                     out=None) -> torch.Tensor:
+    if qw.dim() == 2:
+        qw, sw = qw.unsqueeze(0), sw.unsqueeze(0)
+    E, N, K = qw.shape
+    numel = qa.shape[0]
+    if qa.shape[1] != K:
+        raise ValueError("grouped_gemm_fp8: qa width != K")
+    y = _out(out, (numel, N), torch.bfloat16, qa, "y")
+    _call("grouped_gemm_fp8", _ptr(qa, torch.uint8, "qa"), _ptr(sa, torch.float32, "sa"), _ptr(qw, torch.uint8, "qw"),
+          _ptr(sw, torch.float32, "sw"), *_table_ptrs(tables), numel, E, N, K, padding_m, block_m,
+          _ptr(y, torch.bfloat16, "y"), _stream(qa))
+    return y

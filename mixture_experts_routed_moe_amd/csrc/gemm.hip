@@ -34,28 +34,8 @@ constexpr int kBK = 64;
 constexpr int kBN = 128;
 constexpr int kThreads = 256;
 
-struct Tables {
-  const int32_t* gs;
-  const int32_t* go;
-  const int32_t* gpo;
-  const int32_t* gidx;
-};
-
-// Row recovery of padded block bx: expert g, first compact row and valid rows.
-__device__ __forceinline__ void decode_block(const Tables& tb, int bx, int bm, int64_t numel, int& g,
-                                             int64_t& m_start, int& rows) {
-  int64_t r;
-  if (tb.gs == nullptr) {
-    g = 0;
-    m_start = static_cast<int64_t>(bx) * bm;
-    r = numel - m_start;
-  } else {
-    g = tb.gidx[bx];
-    m_start = static_cast<int64_t>(bx) * bm - tb.gpo[g] + tb.go[g];
-    r = static_cast<int64_t>(tb.go[g]) + tb.gs[g] - m_start;
-  }
-  rows = r <= 0 ? 0 : (r >= bm ? bm : static_cast<int>(r));
-}
+using moe::Tables;
+using moe::decode_block;
 
 // LDS position of 16-byte chunk c in a 128-byte row r: c ^ g(r) with
 // g(r) = (r ^ (r >> 3)) & 7. A ds_read_b128 of an MFMA fragment reads one

@@ -1,0 +1,264 @@
+// Block-scaled FP8 (OCP e4m3) grouped GEMM for the down projection, and the
+// 128x128-block weight quantizer it takes its weights from.
+//
+// Operands: the activation codes qa [numel, K] with one fp32 scale per row and
+// 128-column tile, sa [numel, K/128] (the FP8 quantizer's row layout), and
+// expert weights qw [E, N, K] with one scale per 128x128 block,
+// sw [E, N/128, K/128]. y[m, n] = bf16(sum over 128-wide K blocks kb of
+// sa[m, kb] * sw[e, n/128, kb] * sum_{k in kb} qa[m, k] * qw[e, n, k]).
+//
+// gfx950's fp8 matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4 takes its
+// own per-32-element power-of-two scales; the fp32 scales here are not powers
+// of two, so it runs with unit scales and each 128-wide K block's two products
+// are scaled into the fp32 accumulator in registers. The instruction's A
+// operand is the weight and its B operand the activation: a lane of the
+// 32 x 32 result then holds one activation row (its column index), whose
+// scale is one register, against 16 weight rows of one 128-row scale block,
+// whose scale is one wave-uniform value.
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kT = 128;                                  // tile edge and scale block
+constexpr int kF8Threads = 256;                          // four waves, 2 x 2, each 64 x 64
+constexpr int kF8StageBytes = 2 * kT * kT + kT * 4;      // A rows, W rows, A row scales
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Chunk-position XOR of a 128-byte LDS row (eight 16-byte chunks): the 32
+// rows of a fragment read are conflict-free in 8- and 16-lane phases.
+__device__ __forceinline__ int f8_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// direct-to-LDS loads: lane i writes lds + 16 i (or + 4 i)
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One 256-thread workgroup per 128x128 block of w [rows, K]; thread t holds
+// row t/2, columns (t%2)*64 .. +64. s = fl32(amax/448); code = e4m3 of the
+// fp32 quotient RN32(w * RN64(1/s)), which is the correctly rounded fp32 w/s
+// (w has 8 significant bits: the argument made for the activation quantizer).
+__global__ __launch_bounds__(256) void block_quant_kernel(const uint16_t* __restrict__ w, int K, int n_kb,
+                                                           uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ uint32_t s_max[4];
+  const int kb = blockIdx.x % n_kb;
+  const int64_t nb = blockIdx.x / n_kb;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t row = nb * kT + (t >> 1);
+  const int64_t off = row * K + kb * kT + (t & 1) * 64;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = reinterpret_cast<const uint4*>(w + off)[i];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t ws[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(ws[k] & 0x7FFFu, (ws[k] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), d)));
+  if (lane == 0) s_max[wave] = m;
+  __syncthreads();
+  const uint32_t bb = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  const float sc = __uint_as_float(bb << 16) / 448.0f;
+  const double inv = sc > 0.0f ? 1.0 / static_cast<double>(sc) : 0.0;
+  if (t == 0) s[nb * n_kb + kb] = sc;
+  uint32_t out[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t ws[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; k += 2) {
+      const float a0 = static_cast<float>(static_cast<double>(__uint_as_float(ws[k] << 16)) * inv);
+      const float a1 = static_cast<float>(static_cast<double>(__uint_as_float(ws[k] & 0xFFFF0000u)) * inv);
+      const float b0 = static_cast<float>(static_cast<double>(__uint_as_float(ws[k + 1] << 16)) * inv);
+      const float b1 = static_cast<float>(static_cast<double>(__uint_as_float(ws[k + 1] & 0xFFFF0000u)) * inv);
+      uint32_t word = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false));
+      word = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(b0, b1, static_cast<int>(word), true));
+      out[i * 2 + k / 2] = sc > 0.0f ? word : 0u;   // an all-zero block: codes 0 (no -0.0 codes)
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q + off);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+}
+
+// One workgroup per (128-row block bx of the padded expert-major row space,
+// 128-column tile nt of y). K advances 128 bytes (one scale block) per step;
+// the A rows, the W rows and the 128 A row scales of step kb+1 load
+// (direct-to-LDS) into the other half of a two-stage buffer while step kb
+// computes. A rows past the block's valid rows are read from its last row and
+// never stored.
+__global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
+    const float* __restrict__ sw, moe::Tables tb, int64_t numel, int n_tiles, int N, int K,
+    uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kF8StageBytes];
+  const int bx = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
+  int g, rows;
+  int64_t m_start;
+  moe::decode_block(tb, bx, kT, numel, g, m_start, rows);
+  if (rows == 0) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nkb = K / kT;
+  const int lrow = lane >> 3, lpos = lane & 7;
+
+  // this wave's 32 A rows and 32 W rows of every step: four 8-row loads each
+  const uint8_t* a_src[4];
+  const uint8_t* w_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + lrow;
+    const int rr = min(r, rows - 1);
+    const int pos = (lpos ^ f8_swz(r)) * 16;
+    a_src[i] = qa + (m_start + rr) * K + pos;
+    w_src[i] = qw + (static_cast<int64_t>(g) * N + static_cast<int64_t>(nt) * kT + r) * K + pos;
+  }
+  // waves 0 and 1 load the 128 A row scales of a step, 64 rows each
+  const float* sa_src = sa + (m_start + min(wave * 64 + lane, rows - 1)) * nkb;
+  const float* sw_blk = sw + (static_cast<int64_t>(g) * (N / kT) + nt) * nkb;
+
+  auto issue = [&](int kb, int st) __attribute__((always_inline)) {
+    uint8_t* base = smem + st * kF8StageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(a_src[i] + kb * kT, base + (wave * 32 + i * 8) * kT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(w_src[i] + kb * kT, base + kT * kT + (wave * 32 + i * 8) * kT);
+    if (wave < 2) dma4(sa_src + kb, base + 2 * kT * kT + wave * 64 * 4);
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  // fragment rows and the two 16-byte chunks of each 64-wide K half: lane
+  // half h of half j takes chunks 4j + 2h and 4j + 2h + 1 (the same mapping
+  // for both operands, which is all the dot products need)
+  const int h = lane >> 5;
+  const int a_row0 = wm * 64 + (lane & 31);
+  const int w_row0 = wn * 64 + (lane & 31);
+  auto frag = [&](const uint8_t* rows_base, int r, int j) __attribute__((always_inline)) {
+    const int c0 = 4 * j + 2 * h;
+    const v4i lo = *reinterpret_cast<const v4i*>(rows_base + r * kT + ((c0 ^ f8_swz(r)) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(rows_base + r * kT + (((c0 + 1) ^ f8_swz(r)) << 4));
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+
+  issue(0, 0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    // stage kb has landed for every wave, and every wave is done with stage kb-1
+    wait_vm_barrier<0>();
+    if (kb + 1 < nkb) issue(kb + 1, (kb + 1) & 1);
+    const uint8_t* st = smem + (kb & 1) * kF8StageBytes;
+    const float* s_rows = reinterpret_cast<const float*>(st + 2 * kT * kT);
+    const float w_scale = sw_blk[kb];
+    v8i af[2][2], wf[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm) af[tm][j] = frag(st, a_row0 + tm * 32, j);
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) wf[tn][j] = frag(st + kT * kT, w_row0 + tn * 32, j);
+    }
+    float sc[2];
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) sc[tm] = s_rows[a_row0 + tm * 32] * w_scale;
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) {
+        floatx16 p = {};
+        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[tn][0], af[tm][0], p, 0, 0, 0, 127, 0, 127);
+        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[tn][1], af[tm][1], p, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tm][tn][r] += p[r] * sc[tm];
+      }
+  }
+
+  // lane (h, c): activation row a_row0 + tm*32; result element r is weight
+  // row w_row0-relative (r & 3) + 4h + 8(r >> 2), four consecutive columns per
+  // quad of registers
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm) {
+    const int lr = a_row0 + tm * 32;
+    if (lr >= rows) continue;
+    uint16_t* yrow = y + (m_start + lr) * N + static_cast<int64_t>(nt) * kT + wn * 64;
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int n = tn * 32 + 8 * q4 + 4 * h;
+        const uint32_t lo = moe::pack_bf16x2(acc[tm][tn][4 * q4], acc[tm][tn][4 * q4 + 1]);
+        const uint32_t hi = moe::pack_bf16x2(acc[tm][tn][4 * q4 + 2], acc[tm][tn][4 * q4 + 3]);
+        *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
+      }
+  }
+}
+
+}  // namespace
+
+extern "C" int fp8_block_quant_weights(const uint16_t* w, int64_t rows, int K, uint8_t* q, float* s,
+                                       hipStream_t stream) {
+  using namespace moe;
+  const char* name = "fp8_block_quant_weights";
+  if (rows < 0 || rows % kT != 0 || K < kT || K % kT != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: rows=%lld K=%d (both multiples of 128)", name, (long long)rows, K);
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !s) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (!aligned16(w) || !aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "%s: w/q not 16-byte aligned", name);
+  const int64_t blocks = (rows / kT) * (K / kT);
+  if (blocks > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "%s: too many blocks", name);
+  block_quant_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(w, K, K / kT, q, s);
+  return check_launch(name);
+}
+
+extern "C" int grouped_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                                const int32_t* group_sizes, const int32_t* group_offsets,
+                                const int32_t* group_padded_offsets, const int32_t* group_idx_for_bx, int64_t numel,
+                                int E, int N, int K, int padding_m, int block_m, uint16_t* y, hipStream_t stream) {
+  using namespace moe;
+  const char* name = "grouped_gemm_fp8";
+  if (numel < 0 || N < kT || N % kT != 0 || K < kT || K % kT != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: numel=%lld N=%d K=%d (N, K multiples of 128)", name, (long long)numel, N,
+                K);
+  if (block_m != kT) return fail(MOE_ERR_UNSUPPORTED, "%s: block_m=%d (only 128)", name, block_m);
+  const bool dense = group_sizes == nullptr;
+  if (dense != (group_offsets == nullptr) || dense != (group_padded_offsets == nullptr) ||
+      dense != (group_idx_for_bx == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "%s: tables must be all NULL (dense) or all non-NULL", name);
+  if (dense && E != 1) return fail(MOE_ERR_INVALID_ARG, "%s: dense mode (NULL tables) needs E=1", name);
+  if (!dense && (E < 1 || padding_m <= 0 || padding_m % kT != 0))
+    return fail(MOE_ERR_INVALID_ARG, "%s: E=%d padding_m=%d (a positive multiple of 128)", name, E, padding_m);
+  if (numel >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: numel >= 2^31", name);
+  if (numel == 0) return MOE_OK;
+  if (!qa || !sa || !qw || !sw || !y) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (!aligned16(qa) || !aligned16(qw) || !aligned16(y))
+    return fail(MOE_ERR_INVALID_ARG, "%s: qa/qw/y not 16-byte aligned", name);
+  const int64_t m_blocks = dense ? ceil_div(numel, kT) : moe_num_blocks(numel, E, kT, padding_m);
+  const int n_tiles = N / kT;
+  const int64_t blocks = m_blocks * n_tiles;
+  if (blocks > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
+  const Tables tb{group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx};
+  grouped_gemm_fp8_kernel<<<static_cast<unsigned>(blocks), kF8Threads, 0, stream>>>(qa, sa, qw, sw, tb, numel,
+                                                                                   n_tiles, N, K, y);
+  return check_launch(name);
+}

@@ -83,6 +83,33 @@ __device__ __forceinline__ uint16_t swiglu_bf16(uint16_t gate, uint16_t up) {
   return f32_to_bf16(s * bf16_to_f32(up));
 }
 
+// ------------------------------------------------- dispatch-table decode --
+// The four dispatch tables of the grouped GEMMs (all NULL: one dense group).
+struct Tables {
+  const int32_t* gs;
+  const int32_t* go;
+  const int32_t* gpo;
+  const int32_t* gidx;
+};
+
+// Row recovery of padded block bx (the tutorial's m_start identity): expert
+// g, first compact row m_start = bx*bm - gpo[g] + go[g], and the block's
+// valid rows, clamped to [0, bm].
+__device__ __forceinline__ void decode_block(const Tables& tb, int bx, int bm, int64_t numel, int& g,
+                                             int64_t& m_start, int& rows) {
+  int64_t r;
+  if (tb.gs == nullptr) {
+    g = 0;
+    m_start = static_cast<int64_t>(bx) * bm;
+    r = numel - m_start;
+  } else {
+    g = tb.gidx[bx];
+    m_start = static_cast<int64_t>(bx) * bm - tb.gpo[g] + tb.go[g];
+    r = static_cast<int64_t>(tb.go[g]) + tb.gs[g] - m_start;
+  }
+  rows = r <= 0 ? 0 : (r >= bm ? bm : static_cast<int>(r));
+}
+
 // ------------------------------------------ streaming (non-temporal) access --
 // A 16-byte load of data read once per kernel, marked non-temporal so it
 // does not displace reused lines in the caches.

@@ -61,7 +61,7 @@ def test_num_blocks_matches_worked_example(lib):
     assert lib.moe_num_blocks(100, 3, 64, 128) == 2 + 6
     assert lib.moe_num_blocks(10, 3, 64, 96) == -1
     assert lib.moe_num_blocks(0, 8, 64, 64) == 8
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_workspace_size(lib):
@@ -104,6 +104,16 @@ def test_argument_errors_return_before_launch(lib):
     assert lib.tile_quant_fp8(None, 4, 128, 0, 1, 0, 0, 128, None, None, None, None, None) == -1      # E < 1 with groups
     assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 128, None, None, None, None, None) == -1   # null outputs
     assert lib.tile_quant_fp8(None, 0, 128, 0, None, 0, 0, 0, None, None, None, None, None) == 0      # nothing to do
+    # FP8 weight preparation and the block-scaled FP8 grouped GEMM
+    lib.fp8_block_quant_weights.argtypes = [P, c.c_int64, c.c_int, P, P, P]
+    assert lib.fp8_block_quant_weights(None, 100, 128, None, None, None) == -1     # rows % 128
+    assert lib.fp8_block_quant_weights(None, 128, 64, None, None, None) == -1      # K % 128
+    assert lib.fp8_block_quant_weights(None, 0, 128, None, None, None) == 0
+    lib.grouped_gemm_fp8.argtypes = [P] * 8 + [c.c_int64] + [c.c_int] * 5 + [P, P]
+    assert lib.grouped_gemm_fp8(*[None] * 8, 64, 1, 200, 128, 128, 128, None, None) == -1   # N % 128
+    assert lib.grouped_gemm_fp8(*[None] * 8, 64, 1, 256, 128, 128, 64, None, None) == -2    # block_m != 128
+    assert lib.grouped_gemm_fp8(*[None] * 8, 64, 2, 256, 128, 128, 128, None, None) == -1   # dense needs E=1
+    assert lib.grouped_gemm_fp8(*[None] * 8, 0, 1, 256, 128, 128, 128, None, None) == 0
     # routing limits
     lib.moe_topk_softmax.argtypes = [P, P, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int, P, P, P]
     assert lib.moe_topk_softmax(None, None, 4, 2048, 8, 0, 1, None, None, None) == -2

@@ -448,6 +448,96 @@ def test_swiglu_quant_full_size_sampled_blocks():
         _quant_compare(bits(x[r0:r0 + 128]), F, q, rows=(r0, r0 + 128))
 
 
+# ------------------------------------------------- block-scaled FP8 GEMM --
+
+def _fp8_case(sizes, N, K, key, d, shuffle=True):
+    """Routing with the given per-expert row counts, bf16 activations h and
+    weights w; returns (tables, h, w, group sizes, offsets)."""
+    E = len(sizes)
+    ids = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    if shuffle:
+        ids = ids[np.random.default_rng(key).permutation(ids.size)]
+    tb = mx.moe_align(_t(ids[:, None], d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    assert list(gs) == list(sizes)
+    numel = int(sum(sizes))
+    h = moe_synth.normal_bf16(moe_synth.tensor_key(key, numel, K), (numel, K), 1.0, d)
+    w = moe_synth.normal_bf16(moe_synth.tensor_key(key + 1, N, K), (E, N, K), K ** -0.5, d)
+    return tb, h, w, gs, go
+
+
+def test_fp8_block_quant_weights_bit_exact():
+    d = dev()
+    w = moe_synth.normal_bf16(moe_synth.tensor_key(95), (3, 256, 384), 0.05, d)
+    w[1, :128, 128:256] = 0.0                      # an all-zero block
+    q = mx.fp8_block_quant_weights(w)
+    for e in range(3):
+        ref = oracle.block_quant_fp8(bits(w[e]))
+        assert np.array_equal(host(q["q"][e]), ref["q"]), e
+        assert np.array_equal(host(q["s"][e]).view(np.uint32), ref["s"].view(np.uint32)), e
+    assert not q["q"][1, :128, 128:256].any() and q["s"][1, 0, 1].item() == 0.0
+
+
+@pytest.mark.parametrize("N,K,extra_empty", [(256, 256, 0), (384, 512, 3)])
+def test_grouped_gemm_fp8_expert_size_edges(N, K, extra_empty):
+    """Expert sizes around the 128-row block (0, 1, 127..129, 255..257, ...),
+    empty experts, every output against the oracle on the oracle's own codes;
+    the GPU's codes equal the oracle's bit for bit."""
+    d = dev()
+    sizes = EDGE_SIZES + [0] * extra_empty
+    tb, h, w, gs, go = _fp8_case(sizes, N, K, 96 + extra_empty, d)
+    qa = mx.tile_quant_fp8(h, None)
+    qw = mx.fp8_block_quant_weights(w)
+    y = mx.grouped_gemm_fp8(qa["q_row"], qa["s_row"], qw["q"], qw["s"], tb, 128)
+    ra = oracle.quant_fp8(bits(h))
+    rw = [oracle.block_quant_fp8(bits(w[e])) for e in range(len(sizes))]
+    assert np.array_equal(host(qa["q_row"]), ra["q_row"]) and np.array_equal(host(qa["s_row"]), ra["s_row"])
+    rq = np.stack([r["q"] for r in rw]); rs = np.stack([r["s"] for r in rw])
+    assert np.array_equal(host(qw["q"]), rq) and np.array_equal(host(qw["s"]), rs)
+    ref = oracle.grouped_gemm_fp8(ra["q_row"], ra["s_row"], rq, rs, gs, go)
+    err = assert_bf16_close(bits(y), ref, "fp8 grouped gemm")
+    say("  fp8 gemm max abs err", err)
+
+
+def test_grouped_gemm_fp8_dense_group():
+    d = dev()
+    M, N, K = 300, 256, 384
+    h = moe_synth.normal_bf16(moe_synth.tensor_key(97), (M, K), 1.0, d)
+    w = moe_synth.normal_bf16(moe_synth.tensor_key(98), (N, K), K ** -0.5, d)
+    qa, qw = mx.tile_quant_fp8(h, None), mx.fp8_block_quant_weights(w)
+    y = mx.grouped_gemm_fp8(qa["q_row"], qa["s_row"], qw["q"], qw["s"], None, 128)
+    ra, rw = oracle.quant_fp8(bits(h)), oracle.block_quant_fp8(bits(w))
+    ref = oracle.grouped_gemm_fp8(ra["q_row"], ra["s_row"], rw["q"][None], rw["s"][None], np.array([M]), np.array([0]))
+    assert_bf16_close(bits(y), ref, "fp8 dense")
+
+
+def test_grouped_gemm_fp8_dsv3_down_sampled_rows():
+    """The DeepSeek-V3-shaped routed down projection at full size (numel 32768,
+    N = H = 7168, K = F = 2048, 256 experts, Zipf-biased routing): rows of
+    sampled experts against the oracle on its own codes."""
+    d = dev()
+    cfg = moe_synth.CONFIGS["dsv3_prefill"]
+    say("fp8 down", cfg.name)
+    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k, expert_bias=moe_synth.expert_bias(cfg, d))
+    tb = mx.moe_align(ids, cfg.E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    h = moe_synth.normal_bf16(moe_synth.tensor_key(99), (cfg.numel, cfg.F), 1.0, d)
+    wd = moe_synth.w_down(cfg, d)
+    qa, qw = mx.tile_quant_fp8(h, None), mx.fp8_block_quant_weights(wd)
+    y = mx.grouped_gemm_fp8(qa["q_row"], qa["s_row"], qw["q"], qw["s"], tb, 128)
+    active = np.nonzero(gs)[0]
+    rng = np.random.default_rng(3)
+    for e in sorted({int(active[0]), int(active[-1]), int(np.argmax(gs)), *rng.choice(active, 2).tolist()}):
+        o, n = int(go[e]), int(gs[e])
+        rows = sorted({0, n - 1, *rng.choice(n, min(n, 6), replace=False).tolist()})
+        sel = torch.as_tensor(o + np.asarray(rows), device=d)
+        ra = oracle.quant_fp8(bits(h[sel]))
+        rw = oracle.block_quant_fp8(bits(wd[e]))
+        ref = oracle.grouped_gemm_fp8(ra["q_row"], ra["s_row"], rw["q"][None], rw["s"][None],
+                                      np.array([len(rows)]), np.array([0]))
+        assert_bf16_close(bits(y[sel]), ref, f"fp8 down expert {e}")
+
+
 # ------------------------------------------- grouped tile quantizer --
 
 def _tq_equal(got, ref, name, rows=None, cols=None, scols=None):
