@@ -222,6 +222,33 @@ def test_dense_group_gemm(numel, bm):
 EDGE_SIZES = [0, 1, 127, 128, 129, 255, 256, 257, 383, 384, 385, 700]
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_grouped_gemm_wide_expert_groups(fused):
+    """16 column tiles (the expert-grouped tile order of the 256-row kernel):
+    experts of 0 .. 9 row tiles, so blocks of 1, 2 and 4 row tiles and
+    left-over row tiles all occur; every output against the oracle."""
+    d = dev()
+    sizes = [0, 1, 127, 128, 129, 255, 256, 257, 700, 1300, 2100, 513, 1025]
+    E, H, F = len(sizes), 128, 2048
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    ids_np = ids_np[np.random.default_rng(11).permutation(ids_np.size)][:, None]
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    T = ids_np.shape[0]
+    key = moe_synth.tensor_key(79, int(fused))
+    xp = moe_synth.normal_bf16(key, (T, H), 1.0, d)
+    wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, H), H ** -0.5, d)
+    gu_ref = oracle.grouped_gemm(bits(xp), bits(wgu), gs, go)
+    if fused:
+        h = mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, fuse_swiglu=True)
+        assert np.array_equal(bits(h), oracle.swiglu(bits(mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, False)), F))
+        assert_bf16_close(bits(mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, False)), gu_ref, "gate_up (16 col tiles)")
+    else:
+        wd = moe_synth.normal_bf16(key + 2, (E, 4096, H), H ** -0.5, d)
+        y = mx.grouped_gemm_down(xp, wd, tb, 128, 128)
+        assert_bf16_close(bits(y), oracle.grouped_gemm(bits(xp), bits(wd), gs, go), "down (16 col tiles)")
+
+
 @pytest.mark.parametrize("H,F,extra_empty", [(256, 256, 0), (512, 384, 0), (256, 256, 20)])
 def test_grouped_gemm_expert_size_edges(H, F, extra_empty):
     """extra_empty appends empty experts; with 20 of them the rows per expert
