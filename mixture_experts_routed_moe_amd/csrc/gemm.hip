@@ -23,6 +23,8 @@
 // positions further; each wave holds gate columns and the matching up columns
 // in separate accumulators, so the epilogue pairs them in registers:
 // h = bf16(silu(bf16(g)) * bf16(u)).
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace {
@@ -743,6 +745,9 @@ __device__ __forceinline__ bool find_wide_tile(const int32_t* __restrict__ gs, i
 #ifndef MOE_WIDE_EG_MIN_COLS
 #define MOE_WIDE_EG_MIN_COLS 16
 #endif
+#ifndef MOE_WIDE_EG_MIN_ROW_TILES
+#define MOE_WIDE_EG_MIN_ROW_TILES 32
+#endif
 
 template <bool FUSED, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
@@ -881,7 +886,7 @@ int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
   // tiles: on the DeepSeek-V3-shaped routing (16 and 28 column tiles) gate_up
   // 2.46 -> 2.44 ms and down 1.31 -> 1.28 ms (interleaved A/B); with 6 or 8
   // (the Qwen3 shapes) the fixed 16-tile groups are as fast or faster
-  const int eg = n_tiles >= MOE_WIDE_EG_MIN_COLS;
+  const int eg = n_tiles >= MOE_WIDE_EG_MIN_COLS && m_tiles >= MOE_WIDE_EG_MIN_ROW_TILES;
   const int64_t groups = moe::ceil_div(m_tiles, gm) * (n_tiles / gn);
   const int64_t blocks = eg ? moe::ceil_div(m_tiles, 8) * 8 * n_tiles : moe::ceil_div(groups, 8) * 8 * gm * gn;
   if (blocks > 0x7FFFFFFF || m_tiles > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
@@ -889,6 +894,160 @@ int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
       A, W, tb, E, numel, static_cast<int>(m_tiles), n_tiles, K, w_stride, up_row, ldc, C, gm, gn, eg);
   return moe::check_launch(name);
 }
+
+// ---------------------------------------------------------------------------
+// Few-row kernel (decode). When the groups hold a handful of rows (a one-token
+// shared expert, a few tokens spread over many experts) the time is the weight
+// stream, and 128- or 256-row tiles split the output into too few workgroups
+// to reach HBM bandwidth (28 for a 7168 x 18432 down projection). One
+// 256-thread workgroup per (group, 32 output columns): 8 lanes per weight row
+// each read 16 bytes a step, so a row's lanes cover 128 contiguous bytes, with
+// kGemvUnroll steps in flight per lane, and fp32 dot products against the
+// group's rows, kGemvRows at a time (the rows are few: read from L2).
+constexpr int kGemvCols = 32;
+constexpr int kGemvRows = 4;
+constexpr int kGemvUnroll = 4;
+
+__device__ __forceinline__ void bf16x8_to_f32(uint4 v, float* f) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+
+// The k-th expert with rows (a wave-wide scan over the group sizes, 64 at a
+// time); false past the last one.
+__device__ __forceinline__ bool find_nonempty(const int32_t* __restrict__ gs, int E, int k, int& g) {
+  const int lane = threadIdx.x & 63;
+  int before = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const uint64_t live = __ballot(e < E && gs[e] > 0);
+    const int total = __popcll(live);
+    if (k < before + total) {
+      // the (k - before)-th set bit of live
+      uint64_t m = live;
+      for (int i = 0; i < k - before; ++i) m &= m - 1;
+      g = __builtin_amdgcn_readfirstlane(base + __builtin_ctzll(m));
+      return true;
+    }
+    before += total;
+  }
+  return false;
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(256) void grouped_gemv_kernel(const uint16_t* __restrict__ A,
+                                                           const uint16_t* __restrict__ W, Tables tb, int E,
+                                                           int64_t numel, int n_tiles, int K, int64_t w_stride,
+                                                           int up_row, int ldc, uint16_t* __restrict__ C) {
+  // grid: min(numel, E) expert slots (at most that many experts have rows)
+  // by the column tiles; slot k takes the k-th expert with rows
+  const int k = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
+  int g;
+  int64_t m0;
+  int rows;
+  if (tb.gs == nullptr) {
+    g = 0;
+    m0 = 0;
+    rows = static_cast<int>(numel);
+  } else {
+    if (!find_nonempty(tb.gs, E, k, g)) return;
+    m0 = tb.go[g];
+    rows = tb.gs[g];
+  }
+  if (rows <= 0) return;
+  const int t = threadIdx.x, wr = t >> 3, kc = t & 7;
+  const int col = nt * kGemvCols + wr;
+  const uint16_t* wg = W + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(col) * K;
+  const uint16_t* wu = W + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(FUSED ? up_row + col : col) * K;
+  for (int r0 = 0; r0 < rows; r0 += kGemvRows) {
+    const int nr = min(kGemvRows, rows - r0);
+    const uint16_t* arow[kGemvRows];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) arow[r] = A + (m0 + r0 + min(r, nr - 1)) * K;
+    float acc_g[kGemvRows], acc_u[kGemvRows];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) acc_g[r] = acc_u[r] = 0.0f;
+    // K in steps of 64 (8 lanes x 8 values): whole blocks of kGemvUnroll
+    // steps with every weight load, then every activation load (L1/L2 hits),
+    // issued before the arithmetic; then the remaining steps one at a time
+    auto block = [&](int kb, auto unroll) __attribute__((always_inline)) {
+      constexpr int U = decltype(unroll)::value;
+      uint4 vg[U], vu[U], va[U][kGemvRows];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = kb + u * 64 + kc * 8;
+        vg[u] = *reinterpret_cast<const uint4*>(wg + k);
+        if (FUSED) vu[u] = *reinterpret_cast<const uint4*>(wu + k);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r)
+          va[u][r] = *reinterpret_cast<const uint4*>(arow[r] + kb + u * 64 + kc * 8);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float fg[8], fu[8];
+        bf16x8_to_f32(vg[u], fg);
+        if (FUSED) bf16x8_to_f32(vu[u], fu);
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r) {
+          float fa[8];
+          bf16x8_to_f32(va[u][r], fa);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            acc_g[r] += fa[i] * fg[i];
+            if (FUSED) acc_u[r] += fa[i] * fu[i];
+          }
+        }
+      }
+    };
+    int kb = 0;
+    for (; kb + 64 * kGemvUnroll <= K; kb += 64 * kGemvUnroll) block(kb, Ic<kGemvUnroll>{});
+    for (; kb < K; kb += 64) block(kb, Ic<1>{});
+    // the 8 lanes of a weight row are consecutive: reduce over lanes 1, 2, 4 apart
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+      for (int d = 1; d < 8; d <<= 1) {
+        acc_g[r] += __shfl_xor(acc_g[r], d);
+        if (FUSED) acc_u[r] += __shfl_xor(acc_u[r], d);
+      }
+    if (kc == 0) {
+#pragma unroll
+      for (int r = 0; r < kGemvRows; ++r) {
+        if (r >= nr) break;
+        uint16_t* crow = C + (m0 + r0 + r) * ldc;
+        if (FUSED)
+          crow[col] = moe::swiglu_bf16(moe::f32_to_bf16(acc_g[r]), moe::f32_to_bf16(acc_u[r]));
+        else
+          crow[col] = moe::f32_to_bf16(acc_g[r]);
+      }
+    }
+  }
+}
+
+template <bool FUSED>
+int launch_gemv(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int K, int64_t w_stride,
+                int up_row, int ldc, uint16_t* C, hipStream_t stream, const char* name) {
+  const int n_tiles = ldc / kGemvCols;
+  const int64_t slots = tb.gs ? std::min<int64_t>(numel, E) : 1;
+  const int64_t blocks = slots * n_tiles;
+  if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
+  grouped_gemv_kernel<FUSED><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(A, W, tb, E, numel, n_tiles, K,
+                                                                                w_stride, up_row, ldc, C);
+  return moe::check_launch(name);
+}
+
+#ifndef MOE_GEMV_MAX_ROWS
+#define MOE_GEMV_MAX_ROWS 4
+#endif
+#ifndef MOE_GEMV_GROUPED_PCT
+#define MOE_GEMV_GROUPED_PCT 10
+#endif
 
 template <bool FUSED>
 int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E, int block_m, int padding_m,
@@ -905,6 +1064,11 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
 #ifndef MOE_WIDE_MIN_ROWS
 #define MOE_WIDE_MIN_ROWS 128
 #endif
+  // few rows (at most 4 in one dense group, or at most 2 per expert on
+  // average): the weight-streaming kernel
+  const bool few_rows = tb.gs ? numel * 100 <= MOE_GEMV_GROUPED_PCT * static_cast<int64_t>(E) : numel <= MOE_GEMV_MAX_ROWS;
+  if (few_rows && K % 64 == 0 && ldc % kGemvCols == 0)
+    return launch_gemv<FUSED>(A, W, tb, E, numel, K, w_stride, up_row, ldc, C, stream, name);
   // the wide kernel addresses a tile's A and W rows with 32-bit byte offsets
   const bool wide_fits = (static_cast<int64_t>(up_row) + kWideW) * K * 2 < (int64_t(1) << 32);
   if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits &&

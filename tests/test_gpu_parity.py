@@ -222,6 +222,57 @@ def test_dense_group_gemm(numel, bm):
 EDGE_SIZES = [0, 1, 127, 128, 129, 255, 256, 257, 383, 384, 385, 700]
 
 
+@pytest.mark.parametrize("numel", [1, 3, 4])
+def test_few_row_dense_gemm(numel):
+    """One dense group of at most 4 rows (the decode shared expert): the
+    weight-streaming few-row kernel, K with and without a partial unrolled
+    block (7168 = 28 blocks of 256; 2176 = 8 blocks + 2 steps)."""
+    d = dev()
+    for K in (7168, 2176):
+        key = moe_synth.tensor_key(78, numel, K)
+        x = moe_synth.normal_bf16(key, (numel, K), 1.0, d)
+        wgu = moe_synth.normal_bf16(key + 1, (2 * 256, K), K ** -0.5, d)
+        wd = moe_synth.normal_bf16(key + 2, (K, 256), 256 ** -0.5, d)
+        one, zero = np.array([numel], np.int32), np.array([0], np.int32)
+        gu = mx.grouped_gemm_gate_up(x, wgu, None, 128, 128, fuse_swiglu=False)
+        assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(wgu)[None], one, zero), f"gate_up K={K}")
+        h = mx.grouped_gemm_gate_up(x, wgu, None, 128, 128, fuse_swiglu=True)
+        assert np.array_equal(bits(h), oracle.swiglu(bits(gu), 256))
+        y = mx.grouped_gemm_down(h, wd, None, 128, 128)
+        assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd)[None], one, zero), f"down K={K}")
+
+
+@pytest.mark.parametrize("layout", ["spread", "last"])
+def test_few_row_grouped_gemm(layout):
+    """A grouped launch with numel <= E / 10 rows (one decode token's top-k
+    over many experts): mostly empty experts, single rows, and one expert
+    with 9 rows (more than one pass of the kernel's row batch); "last" puts
+    the rows in the highest experts (the expert scan's second 64-wide
+    chunk and beyond)."""
+    d = dev()
+    E, H, F = 160, 256, 384
+    sizes = np.zeros(E, np.int64)
+    hot = [5, 17, 63, 64, 100, 130, 159] if layout == "spread" else [153, 154, 155, 156, 157, 158, 159]
+    for e in hot:
+        sizes[e] = 1
+    sizes[hot[2]] = 9
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)[:, None]
+    assert ids_np.shape[0] * 10 <= E
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    T = ids_np.shape[0]
+    key = moe_synth.tensor_key(80, T)
+    xp = moe_synth.normal_bf16(key, (T, H), 1.0, d)
+    wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, H), H ** -0.5, d)
+    wd = moe_synth.normal_bf16(key + 2, (E, H, F), F ** -0.5, d)
+    gu = mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, fuse_swiglu=False)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(xp), bits(wgu), gs, go), "few-row gate_up")
+    h = mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, fuse_swiglu=True)
+    assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
+    y = mx.grouped_gemm_down(h, wd, tb, 128, 128)
+    assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd), gs, go), "few-row down")
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_grouped_gemm_wide_expert_groups(fused):
     """16 column tiles (the expert-grouped tile order of the 256-row kernel):
