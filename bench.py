@@ -16,10 +16,12 @@ average duration comes from HIP events recorded on the launch stream around
 every launch inside the timed region; the algorithmic bytes and FLOPs per
 launch are counted from the realized routing (active experts' weights once,
 activations in and out once). `cpu_baseline` times the oracle on a bounded
-sample of tokens on the host cores. `other_workloads` repeats the timed loop
-(same steps and warmup) on the other forward shapes of the family (the Qwen3
-prefill and decode shapes when the DeepSeek-V3 prefill is the primary one) and
-reports each one's ms per forward, TFLOP/s and per-kernel figures.
+sample of tokens on the host cores. `other_workloads` times the same number
+of whole forwards (`routed_moe_forward`, the shared expert on a second stream,
+HIP events only around each forward) on the other forward shapes of the family
+(the Qwen3 prefill and decode shapes, the Kimi-K2 table's token counts when
+the DeepSeek-V3 prefill is the primary one), then as many staged forwards (in
+line, events around every stage) for each one's per-kernel figures.
 `aligned_grouped_gemm` times the grouped GEMM alone on the aligned shapes of
 the pages' grouped-GEMM baseline table (E groups of M rows each), with that
 table's H200 figure beside each case as context. `grouped_quant` times the
@@ -122,7 +124,22 @@ class Workload:
         run("unpermute", lambda: mx.moe_unpermute(bufs.y, tb["pair_to_row"], bufs.topk_weights, cfg.rsf, addend,
                                                   bufs.out))
 
-    def run(self, steps, warmup, ev):
+    def forward(self, side=None):
+        """One forward through the library's composed forward (the shared
+        expert on `side` when given)."""
+        cfg = self.cfg
+        return self.mx.routed_moe_forward(self.hidden, self.logits, self.wgu, self.wd, cfg.top_k, cfg.rsf,
+                                          cfg.padding_m, cfg.block_m, self.swgu, self.swd, fuse_swiglu=self.fuse,
+                                          buffers=self.bufs, expert_bias=self.bias, scoring=cfg.scoring,
+                                          renormalize=cfg.renormalize, shared_stream=side)
+
+    def run(self, steps, warmup, ev, whole=False, side=None):
+        """Times `steps` forwards after `warmup` untimed ones. whole=False:
+        each forward as its stages with HIP events around every stage (the
+        per-kernel figures come from the timed region itself). whole=True:
+        whole forwards through `routed_moe_forward` (shared expert on `side`
+        when given) with events only around each forward, then the same
+        number of staged forwards, in line, for the per-kernel figures."""
         import torch
         cfg, fuse = self.cfg, self.fuse
         ev_log = {s: [] for s in STAGES}
@@ -133,19 +150,29 @@ class Workload:
             ev_log[name].append((a, ev()))
 
         for _ in range(warmup):
-            self.step(lambda name, fn: fn())
+            if whole:
+                self.forward(side)
+            else:
+                self.step(lambda name, fn: fn())
         torch.cuda.synchronize()
         print(f"# {cfg.name}: warmup done ({warmup} steps)", file=sys.stderr, flush=True)
         step_ev = []
         t0 = time.perf_counter()
         for _ in range(steps):
             a = ev()
-            self.step(timed)
+            if whole:
+                self.forward(side)
+            else:
+                self.step(timed)
             step_ev.append((a, ev()))
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms_per_step = (t1 - t0) * 1e3 / steps
         print(f"# {cfg.name}: timed {steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+        if whole:
+            for _ in range(steps):
+                self.step(timed)
+            torch.cuda.synchronize()
 
         stage_ms = {s: (sum(a.elapsed_time(b) for a, b in v) / len(v)) for s, v in ev_log.items() if v}
         stage_pct = {s: pct([a.elapsed_time(b) for a, b in v]) for s, v in ev_log.items() if v}
@@ -193,6 +220,8 @@ class Workload:
         gemm_s = (stage_ms["gate_up"] + stage_ms["down"]) * 1e-3
         summary = {
             "ms_per_forward": round(ms_per_step, 4), **{"step_" + k: v for k, v in step_pct.items()},
+            "timing": ("whole forwards, shared expert on a second stream" if whole and side is not None and cfg.shared_F
+                       else "whole forwards" if whole else "staged forwards, events around every stage"),
             "tflops": round(flop_fwd / (ms_per_step * 1e-3) / 1e12, 2),
             "grouped_gemm_tflops": round((flop_gate_up + flop_down) / gemm_s / 1e12, 2),
             "grouped_gemm_mfma_frac": round((flop_gate_up + flop_down) / gemm_s / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -375,8 +404,10 @@ def main():
         fp8["bf16_down_ms"] = round(stage_ms["down"], 4)
         print(f"# fp8 down: {fp8['gemm_ms']:.3f} ms (bf16 {stage_ms['down']:.3f} ms)", file=sys.stderr, flush=True)
 
-    # the other forward workloads of the same family, each timed the same way
+    # the other forward workloads of the same family: whole forwards, the
+    # shared expert (where there is one) on a second stream of default priority
     others = {}
+    side = torch.cuda.Stream(dev)
     for name in OTHER_WORKLOADS:
         if name == cfg.name or args.only_primary:
             continue
@@ -387,7 +418,7 @@ def main():
             torch.cuda.empty_cache()
         wl = Workload(moe_synth.CONFIGS[name], dev, fuse, like=prev)
         del prev
-        r = wl.run(args.steps, args.warmup, ev)
+        r = wl.run(args.steps, args.warmup, ev, whole=True, side=side)
         others[name] = r["summary"]
         if name.startswith("kimi_k2_t"):
             others[name]["page_h200_ms"] = KIMI_K2_PAGE_H200_MS.get(moe_synth.CONFIGS[name].T)

@@ -9,7 +9,11 @@ all tokens as one dense group and joins the unpermute as its addend.
 
 `MoEBuffers` holds every intermediate for one problem size so a forward
 allocates nothing; all work is enqueued on the current stream without a host
-synchronisation.
+synchronisation. Given `shared_stream`, the shared expert's two GEMMs run on
+that stream instead, concurrently with routing, permute and the routed GEMMs
+(they depend only on the hidden states), and the current stream waits for
+them before the unpermute: the routed kernels leave matrix cores idle while
+they wait on weight loads, and the shared expert's dense tiles fill them.
 """
 from __future__ import annotations
 
@@ -66,7 +70,8 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
                        shared_w_down: Optional[torch.Tensor] = None,
                        fuse_swiglu: bool = True, buffers: Optional[MoEBuffers] = None,
                        expert_bias: Optional[torch.Tensor] = None, scoring: str = "softmax",
-                       renormalize: bool = True, return_parts: bool = False):
+                       renormalize: bool = True, return_parts: bool = False,
+                       shared_stream: Optional[torch.cuda.Stream] = None):
     """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden)).
 
     With return_parts=True returns (shared_out, routed_out) instead, the split
@@ -75,6 +80,11 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     adds them (after its all-reduce of shared_out when the shared expert is
     tensor-parallel). Otherwise the shared output is added inside the
     unpermute before its single rounding.
+
+    shared_stream: a stream (of default priority) for the shared expert's
+    GEMMs; it first waits for the work already on the current stream, and
+    the current stream waits for it before the unpermute (and before
+    returning with return_parts). The results are the same bits either way.
     """
     T, H = hidden.shape
     E, twoF, H2 = w_gate_up.shape
@@ -89,6 +99,20 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     elif dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu:
         raise ValueError("routed_moe_forward: buffers were made for another shape")
 
+    def shared_expert():
+        if fuse_swiglu:
+            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, True, b.shared_h)
+        else:
+            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, False, b.shared_gate_up)
+            _lib.swiglu(b.shared_gate_up, b.shared_h)
+        _lib.grouped_gemm_down(b.shared_h, shared_w_down, None, padding_m, block_m, b.shared_y)
+
+    main = torch.cuda.current_stream(hidden.device)
+    side = shared_stream if shared_F else None
+    if side is not None:
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            shared_expert()
     _lib.moe_topk_softmax(router_logits, top_k, b.topk_ids, b.topk_weights, expert_bias, scoring, renormalize)
     tb = _lib.moe_align(b.topk_ids, E, padding_m, block_m, b.tables)
     _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm, tb["pair_to_row"])
@@ -100,12 +124,10 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     _lib.grouped_gemm_down(b.h, w_down, tb, padding_m, block_m, b.y)
     addend = None
     if shared_F:
-        if fuse_swiglu:
-            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, True, b.shared_h)
+        if side is None:
+            shared_expert()
         else:
-            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, False, b.shared_gate_up)
-            _lib.swiglu(b.shared_gate_up, b.shared_h)
-        _lib.grouped_gemm_down(b.shared_h, shared_w_down, None, padding_m, block_m, b.shared_y)
+            main.wait_stream(side)
         addend = b.shared_y
     if return_parts:
         _lib.moe_unpermute(b.y, tb["pair_to_row"], b.topk_weights, routed_scaling_factor, None, b.out)

@@ -751,10 +751,12 @@ def test_forward_kimi_k2_single_token():
     say("forward", cfg.name)
     inp = inputs(cfg, d)
     ref = oracle_tokens(cfg, inp, [0])
+    side = torch.cuda.Stream(d)
     for fuse in (True, False):
         out = _gpu_forward(cfg, inp, fuse)
         err = assert_bf16_close(bits(out), ref["out"], f"kimi T=1 out fuse={fuse}")
         say("  out max abs err", err, "fuse", fuse)
+        assert torch.equal(_gpu_forward(cfg, inp, fuse, shared_stream=side), out)
 
 
 # sampled tokens per workload: each one brings up to k experts' weights to the host
@@ -792,6 +794,16 @@ def test_forward_full_size_sampled_tokens(name):
     out2 = _gpu_forward(cfg, inp)
     assert torch.equal(out, out2)
     if cfg.shared_F:
+        # the shared expert on a second stream, concurrent with the routed path: same bytes
+        ref_out, ref_shared = out.clone(), bufs.shared_y.clone()
+        side = torch.cuda.Stream(d)
+        for _ in range(2):
+            bufs.out.zero_()
+            bufs.shared_y.zero_()
+            out3 = _gpu_forward(cfg, inp, buffers=bufs, shared_stream=side)
+            assert torch.equal(out3, ref_out) and torch.equal(bufs.shared_y, ref_shared)
+        shared_o, routed_o = _gpu_forward(cfg, inp, buffers=bufs, return_parts=True, shared_stream=side)
+        assert torch.equal(shared_o, ref_shared)
         # the split of the partial-output contract: shared part and routed part, added by the caller
         shared, routed = _gpu_forward(cfg, inp, return_parts=True)
         assert torch.equal(shared, bufs.shared_y)
