@@ -64,6 +64,8 @@ def parse():
                    help="aligned grouped-GEMM cases to time: 'all', 'none' or a comma-separated list of names")
     p.add_argument("--cpu-tokens", type=int, default=24, help="tokens in the oracle's timed sample")
     p.add_argument("--unfused", action="store_true", help="gate_up GEMM then a separate SwiGLU kernel")
+    p.add_argument("--permute-copy", action="store_true",
+                   help="permute as its own copy kernel instead of inside the gate_up GEMM's loads")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     return p.parse_args()
@@ -74,14 +76,15 @@ OTHER_WORKLOADS = ("qwen3_prefill", "qwen3_decode", "dsv3_prefill", "kimi_k2_t1"
 # context only (other hardware): the pages' H200 ms per forward of the Kimi-K2-scale
 # routed + shared op (TileOPs #778 "Benchmark", TileOPs column) at each token count
 KIMI_K2_PAGE_H200_MS = {1: 0.95, 32: 5.46, 512: 10.44, 2048: 19.99, 4096: 32.63}
-STAGES = ("topk_softmax", "align", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "unpermute")
+STAGES = ("topk_softmax", "align", "permute", "gate_up", "swiglu", "down", "shared_gate_up", "shared_down",
+          "unpermute")
 
 
 class Workload:
     """One forward configuration: seeded inputs and weights resident on the GPU,
     the buffers of the forward, and a timed loop over whole forwards."""
 
-    def __init__(self, cfg, dev, fuse, like=None):
+    def __init__(self, cfg, dev, fuse, like=None, fuse_permute=True):
         import moe_synth
         import mixture_experts_routed_moe_amd as mx
         self.cfg, self.fuse, self.mx = cfg, fuse, mx
@@ -97,7 +100,7 @@ class Workload:
             self.swgu = moe_synth.shared_w_gate_up(cfg, dev) if cfg.shared_F else None
             self.swd = moe_synth.shared_w_down(cfg, dev) if cfg.shared_F else None
         shape = mx.MoEShape(cfg.T, cfg.H, cfg.F, cfg.E, cfg.top_k, cfg.padding_m, cfg.block_m, cfg.shared_F)
-        self.bufs = mx.MoEBuffers(shape, dev, fuse_swiglu=fuse)
+        self.bufs = mx.MoEBuffers(shape, dev, fuse_swiglu=fuse, fuse_permute=fuse_permute)
 
     def step(self, run):
         cfg, mx, bufs, fuse = self.cfg, self.mx, self.bufs, self.fuse
@@ -105,14 +108,18 @@ class Workload:
         run("topk_softmax", lambda: mx.moe_topk_softmax(self.logits, cfg.top_k, bufs.topk_ids, bufs.topk_weights,
                                                         self.bias, cfg.scoring, cfg.renormalize))
         run("align", lambda: mx.moe_align(bufs.topk_ids, cfg.E, cfg.padding_m, cfg.block_m, tb))
-        run("permute", lambda: mx.moe_permute(self.hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm,
-                                              tb["pair_to_row"]))
-        if fuse:
-            run("gate_up", lambda: mx.grouped_gemm_gate_up(bufs.x_perm, self.wgu, tb, cfg.padding_m, cfg.block_m,
-                                                           True, bufs.h))
+        gu_out = bufs.h if fuse else bufs.gate_up
+        if bufs.fuse_permute:
+            # the permute folded into the gate_up GEMM's loads
+            run("gate_up", lambda: mx.grouped_gemm_gate_up_gather(self.hidden, self.wgu, tb, cfg.top_k, cfg.padding_m,
+                                                                  cfg.block_m, fuse, gu_out))
         else:
-            run("gate_up", lambda: (mx.grouped_gemm_gate_up(bufs.x_perm, self.wgu, tb, cfg.padding_m, cfg.block_m,
-                                                            False, bufs.gate_up), mx.swiglu(bufs.gate_up, bufs.h)))
+            run("permute", lambda: mx.moe_permute(self.hidden, tb["sorted_pair"], cfg.top_k, bufs.x_perm,
+                                                  tb["pair_to_row"]))
+            run("gate_up", lambda: mx.grouped_gemm_gate_up(bufs.x_perm, self.wgu, tb, cfg.padding_m, cfg.block_m,
+                                                           fuse, gu_out))
+        if not fuse:
+            run("swiglu", lambda: mx.swiglu(bufs.gate_up, bufs.h))
         run("down", lambda: mx.grouped_gemm_down(bufs.h, self.wd, tb, cfg.padding_m, cfg.block_m, bufs.y))
         addend = None
         if cfg.shared_F:
@@ -131,7 +138,8 @@ class Workload:
         return self.mx.routed_moe_forward(self.hidden, self.logits, self.wgu, self.wd, cfg.top_k, cfg.rsf,
                                           cfg.padding_m, cfg.block_m, self.swgu, self.swd, fuse_swiglu=self.fuse,
                                           buffers=self.bufs, expert_bias=self.bias, scoring=cfg.scoring,
-                                          renormalize=cfg.renormalize, shared_stream=side)
+                                          renormalize=cfg.renormalize, shared_stream=side,
+                                          fuse_permute=self.bufs.fuse_permute)
 
     def run(self, steps, warmup, ev, whole=False, side=None):
         """Times `steps` forwards after `warmup` untimed ones. whole=False:
@@ -187,7 +195,9 @@ class Workload:
         flop_shared = 6.0 * cfg.T * H * cfg.shared_F
         flop_fwd = flop_gate_up + flop_down + flop_shared
         h_cols = F if fuse else 2 * F
-        bytes_gate_up = active * 2.0 * F * H * 2 + numel * H * 2 + numel * h_cols * 2
+        # activations in: the permuted copy, or with the gather the hidden states once
+        a_in = cfg.T * H * 2 if self.bufs.fuse_permute else numel * H * 2
+        bytes_gate_up = active * 2.0 * F * H * 2 + a_in + numel * h_cols * 2
         bytes_down = active * 1.0 * H * F * 2 + numel * F * 2 + numel * H * 2
         bytes_permute = (cfg.T + numel) * H * 2 + 4 * numel
         bytes_unpermute = numel * H * 2 + 8 * cfg.T * cfg.top_k + cfg.T * H * 2 * (2 if cfg.shared_F else 1)
@@ -377,7 +387,7 @@ def main():
               flush=True)
         return
     t_gen = time.time()
-    wl = Workload(cfg, dev, fuse)
+    wl = Workload(cfg, dev, fuse, fuse_permute=not args.permute_copy)
     qx = moe_synth.quant_input(moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F, dev)
     qbufs = mx.swiglu_quant_fp8(qx)
     torch.cuda.synchronize()
@@ -416,7 +426,7 @@ def main():
         if prev.cfg.cid != moe_synth.CONFIGS[name].cid:
             prev = None
             torch.cuda.empty_cache()
-        wl = Workload(moe_synth.CONFIGS[name], dev, fuse, like=prev)
+        wl = Workload(moe_synth.CONFIGS[name], dev, fuse, like=prev, fuse_permute=not args.permute_copy)
         del prev
         r = wl.run(args.steps, args.warmup, ev, whole=True, side=side)
         others[name] = r["summary"]
@@ -497,7 +507,7 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded counter-based generator, N(0,1)-shaped inputs, random-init weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": H, "F": F, "E": E, "top_k": cfg.top_k,
                    "padding_m": cfg.padding_m, "block_m": cfg.block_m, "routed_scaling_factor": cfg.rsf,
-                   "zipf_bias_s": cfg.zipf_s, "shared_F": cfg.shared_F, "fused_swiglu": fuse,
+                   "zipf_bias_s": cfg.zipf_s, "shared_F": cfg.shared_F, "fused_swiglu": fuse, "fused_permute": not args.permute_copy,
                    "active_experts": active, "max_rows_per_expert": int(gs.max()),
                    "parallelism": "single GPU"},
         "grouped_gemm_tflops": round((flop_gate_up + flop_down) / ((stage_ms["gate_up"] + stage_ms["down"]) * 1e-3) / 1e12, 2),

@@ -144,6 +144,25 @@ int grouped_gemm_gate_up(const uint16_t* x_perm, const uint16_t* w_gate_up,
                          int64_t numel, int E, int H, int F, int padding_m, int block_m,
                          int fuse_swiglu, uint16_t* out, hipStream_t stream);
 
+/* grouped_gemm_gate_up with the token permute folded into its A loads: the
+ * result is byte-identical to moe_permute followed by grouped_gemm_gate_up
+ * on x_perm, with compact row r of A read from
+ *     hidden[sorted_pair[r] / top_k, :]
+ * (the permute's definition, TileOPs "MoePermuteAlignOp"; the grouped GEMM
+ * of TileOPs #1580 "Grouped-GEMM kernel" on the permuted rows), so x_perm is
+ * never written or read. hidden [T, H] bf16 (16-byte aligned),
+ * sorted_pair [T*top_k] int32 from moe_align (values in [0, T*top_k); not
+ * checked on the device), numel == T*top_k, the four tables non-NULL (no
+ * dense mode). w_gate_up, fuse_swiglu, out, limits: as grouped_gemm_gate_up.
+ * Returns MOE_ERR_INVALID_ARG for a NULL table or sorted_pair, or
+ * numel != T*top_k. */
+int grouped_gemm_gate_up_gather(const uint16_t* hidden, int64_t T, const int32_t* sorted_pair, int top_k,
+                                const uint16_t* w_gate_up, const int32_t* group_sizes,
+                                const int32_t* group_offsets, const int32_t* group_padded_offsets,
+                                const int32_t* group_idx_for_bx, int64_t numel, int E, int H, int F,
+                                int padding_m, int block_m, int fuse_swiglu, uint16_t* out,
+                                hipStream_t stream);
+
 /* SwiGLU on the gate|up halves: h[m, f] = bf16(silu(gate[m, f]) * up[m, f])
  * with gate = gate_up[:, 0:F], up = gate_up[:, F:2F] (TileOPs #778 "SiLU-mul";
  * xtuner #2089 native_swiglu). silu uses the library's fp32 exp sequence

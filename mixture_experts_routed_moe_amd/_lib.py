@@ -32,7 +32,7 @@ class MoeError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 SCORING = {"softmax": 0, "sigmoid": 1}
 
 
@@ -52,6 +52,7 @@ def _load() -> ctypes.CDLL:
         "moe_align": (I, [P, I64, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
         "moe_permute": (I, [P, P, P, I64, I, I, P, P]),
         "grouped_gemm_gate_up": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
+        "grouped_gemm_gate_up_gather": (I, [P, I64, P, I, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
         "swiglu": (I, [P, I64, I, P, P]),
         "grouped_gemm_down": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, P, P]),
         "moe_unpermute": (I, [P, P, P, I64, I, I, F, P, P, P]),
@@ -74,7 +75,8 @@ def _load() -> ctypes.CDLL:
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_workspace_bytes",
-           "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up", "swiglu",
+           "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up",
+           "grouped_gemm_gate_up_gather", "swiglu",
            "grouped_gemm_down", "moe_unpermute", "swiglu_quant_fp8", "tile_quant_fp8",
            "tile_quant_fp8_m_pad_bound", "fp8_block_quant_weights", "grouped_gemm_fp8")
 
@@ -209,6 +211,32 @@ def grouped_gemm_gate_up(x_perm: torch.Tensor, w_gate_up: torch.Tensor, tables: 
     _call("grouped_gemm_gate_up", _ptr(x_perm, torch.bfloat16, "x_perm"), _ptr(w_gate_up, torch.bfloat16, "w_gate_up"),
           *_table_ptrs(tables), numel, E, H, F, padding_m, block_m, int(bool(fuse_swiglu)),
           _ptr(o, torch.bfloat16, "out"), _stream(x_perm))
+    return o
+
+
+def grouped_gemm_gate_up_gather(hidden: torch.Tensor, w_gate_up: torch.Tensor, tables: Dict[str, torch.Tensor],
+                                top_k: int, padding_m: int, block_m: int, fuse_swiglu: bool = True,
+                                out=None) -> torch.Tensor:
+    """grouped_gemm_gate_up on the permuted rows hidden[sorted_pair[r] // top_k]
+    without writing them out (tables from moe_align, which must carry
+    sorted_pair)."""
+    if tables is None:
+        raise ValueError("grouped_gemm_gate_up_gather: needs the dispatch tables")
+    if w_gate_up.dim() == 2:
+        w_gate_up = w_gate_up.unsqueeze(0)
+    E, twoF, H = w_gate_up.shape
+    F = twoF // 2
+    T = hidden.shape[0]
+    if hidden.shape[1] != H:
+        raise ValueError("grouped_gemm_gate_up_gather: hidden width != H")
+    numel = T * top_k
+    sp = tables["sorted_pair"]
+    if sp.numel() != numel:
+        raise ValueError("grouped_gemm_gate_up_gather: sorted_pair length != T*top_k")
+    o = _out(out, (numel, F if fuse_swiglu else 2 * F), torch.bfloat16, hidden, "out")
+    _call("grouped_gemm_gate_up_gather", _ptr(hidden, torch.bfloat16, "hidden"), T, _ptr(sp, torch.int32, "sorted_pair"),
+          top_k, _ptr(w_gate_up, torch.bfloat16, "w_gate_up"), *_table_ptrs(tables), numel, E, H, F, padding_m,
+          block_m, int(bool(fuse_swiglu)), _ptr(o, torch.bfloat16, "out"), _stream(hidden))
     return o
 
 

@@ -69,7 +69,6 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const uint16_t* Ab = A + m_start * K;
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
 
   const uint16_t* a_src[A_CH];
@@ -79,7 +78,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   for (int i = 0; i < A_CH; ++i) {
     const int q = tid + kThreads * i, r = q >> 3, c = q & 7;
     a_ok[i] = r < rows;
-    a_src[i] = Ab + static_cast<int64_t>(a_ok[i] ? r : 0) * K + c * 8;
+    a_src[i] = A + moe::a_row(tb, m_start + (a_ok[i] ? r : 0)) * K + c * 8;
     a_dst[i] = swz(r, c);
   }
   const uint16_t* b_src[B_CH];
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
     const int rb = (wave * A_LOADS + i) * RPL;
     const int r = rb + lrow;
     const int rr = min(r, rows - 1);
-    a_src[i] = A + (m_start + rr) * K + (lpos ^ row_swz<CPR>(r)) * 8;
+    a_src[i] = A + moe::a_row(tb, m_start + rr) * K + (lpos ^ row_swz<CPR>(r)) * 8;
     a_lds[i] = rb * ROWB;
   }
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
@@ -506,7 +505,8 @@ struct Ic {
 template <bool FUSED, bool HALF, int NW>
 __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ Wb, int64_t m_start, int rows, int nt,
-                                               int K, int up_row, int ldc, uint16_t* __restrict__ C) {
+                                               int K, int up_row, int ldc, uint16_t* __restrict__ C,
+                                               const int32_t* __restrict__ gather, int gather_k) {
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
   constexpr int AROWS = HALF ? kWideRows / 2 : kWideRows;
   constexpr int WM = NW / 2;                         // wave rows (two wave columns)
@@ -525,15 +525,18 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   const int lrow = lane / CPR;
   const int lpos = lane % CPR;
 
-  // direct-to-LDS sources: a uniform base per step plus fixed per-lane offsets
-  const char* a_base = reinterpret_cast<const char*>(A + m_start * K);
+  // direct-to-LDS sources: a uniform base per step plus fixed per-lane
+  // offsets (with a gather table, from the start of A: the host checks that
+  // A's rows fit 32-bit byte offsets)
+  const char* a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
   const char* w_base = reinterpret_cast<const char*>(Wb + static_cast<int64_t>(nt) * (FUSED ? kWideW / 2 : kWideW) * K);
   uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     const int r = (wave * A_LOADS + i) * RPL + lrow;
     const int rr = min(r, rows - 1);
-    a_off[i] = static_cast<uint32_t>(rr) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
+    const uint32_t ar = gather ? static_cast<uint32_t>(gather[m_start + rr] / gather_k) : static_cast<uint32_t>(rr);
+    a_off[i] = ar * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
@@ -833,9 +836,9 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
   const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
   if (rows <= kWideRows / 2)
-    wide_ring_tile<FUSED, true, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
+    wide_ring_tile<FUSED, true, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
   else
-    wide_ring_tile<FUSED, false, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C);
+    wide_ring_tile<FUSED, false, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
 }
 
 // Group shape for the tile order: GN column tiles (a divisor of n_tiles, at
@@ -967,7 +970,7 @@ __global__ __launch_bounds__(256) void grouped_gemv_kernel(const uint16_t* __res
     const int nr = min(kGemvRows, rows - r0);
     const uint16_t* arow[kGemvRows];
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) arow[r] = A + (m0 + r0 + min(r, nr - 1)) * K;
+    for (int r = 0; r < kGemvRows; ++r) arow[r] = A + moe::a_row(tb, m0 + r0 + min(r, nr - 1)) * K;
     float acc_g[kGemvRows], acc_u[kGemvRows];
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) acc_g[r] = acc_u[r] = 0.0f;
@@ -1052,7 +1055,7 @@ int launch_gemv(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
 template <bool FUSED>
 int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E, int block_m, int padding_m,
            int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* C, hipStream_t stream,
-           const char* name) {
+           const char* name, bool a_off32 = true) {
   const int64_t m_blocks = tb.gs ? moe_num_blocks(numel, E, block_m, padding_m) : moe::ceil_div(numel, block_m);
   const int64_t blocks = m_blocks * n_tiles;
   if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
@@ -1070,7 +1073,8 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   if (few_rows && K % 64 == 0 && ldc % kGemvCols == 0)
     return launch_gemv<FUSED>(A, W, tb, E, numel, K, w_stride, up_row, ldc, C, stream, name);
   // the wide kernel addresses a tile's A and W rows with 32-bit byte offsets
-  const bool wide_fits = (static_cast<int64_t>(up_row) + kWideW) * K * 2 < (int64_t(1) << 32);
+  // (with a gather table, A's offsets count from its first row: a_off32)
+  const bool wide_fits = (static_cast<int64_t>(up_row) + kWideW) * K * 2 < (int64_t(1) << 32) && a_off32;
   if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits &&
       numel >= static_cast<int64_t>(MOE_WIDE_MIN_ROWS) * E)
     return launch_wide<FUSED>(A, W, tb, E, numel, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
@@ -1128,6 +1132,36 @@ extern "C" int grouped_gemm_gate_up(const uint16_t* x_perm, const uint16_t* w_ga
     return launch<true>(x_perm, w_gate_up, tb, numel, E, block_m, padding_m, F / 64, H, w_stride, F, F, out, stream, name);
   return launch<false>(x_perm, w_gate_up, tb, numel, E, block_m, padding_m, (2 * F) / kBN, H, w_stride, 0, 2 * F, out,
                        stream, name);
+}
+
+extern "C" int grouped_gemm_gate_up_gather(const uint16_t* hidden, int64_t T, const int32_t* sorted_pair, int top_k,
+                                           const uint16_t* w_gate_up, const int32_t* group_sizes,
+                                           const int32_t* group_offsets, const int32_t* group_padded_offsets,
+                                           const int32_t* group_idx_for_bx, int64_t numel, int E, int H, int F,
+                                           int padding_m, int block_m, int fuse_swiglu, uint16_t* out,
+                                           hipStream_t stream) {
+  const char* name = "grouped_gemm_gate_up_gather";
+  if (!group_sizes) return moe::fail(MOE_ERR_INVALID_ARG, "%s: the gather needs the dispatch tables", name);
+  int rc = check_common(name, hidden, w_gate_up, group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx,
+                        numel, E, padding_m, block_m, out);
+  if (rc) return rc;
+  if (T < 0 || top_k < 1 || numel != T * top_k)
+    return moe::fail(MOE_ERR_INVALID_ARG, "%s: numel=%lld must be T=%lld times top_k=%d", name,
+                     static_cast<long long>(numel), static_cast<long long>(T), top_k);
+  if (numel > 0 && !sorted_pair) return moe::fail(MOE_ERR_INVALID_ARG, "%s: null sorted_pair", name);
+  if (H < kBK || H % kBK != 0 || F < 64 || F % 64 != 0)
+    return moe::fail(MOE_ERR_UNSUPPORTED, "%s: H=%d must be a multiple of 64, F=%d a multiple of 64", name, H, F);
+  if (numel == 0) return MOE_OK;
+  Tables tb{group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx};
+  tb.gather = sorted_pair;
+  tb.gather_k = top_k;
+  const bool a_off32 = T * H * 2 < (int64_t(1) << 32);
+  const int64_t w_stride = static_cast<int64_t>(2) * F * H;
+  if (fuse_swiglu)
+    return launch<true>(hidden, w_gate_up, tb, numel, E, block_m, padding_m, F / 64, H, w_stride, F, F, out, stream,
+                        name, a_off32);
+  return launch<false>(hidden, w_gate_up, tb, numel, E, block_m, padding_m, (2 * F) / kBN, H, w_stride, 0, 2 * F, out,
+                       stream, name, a_off32);
 }
 
 extern "C" int grouped_gemm_down(const uint16_t* h, const uint16_t* w_down, const int32_t* group_sizes,

@@ -90,7 +90,17 @@ struct Tables {
   const int32_t* go;
   const int32_t* gpo;
   const int32_t* gidx;
+  // optional gather: compact row R of the GEMM's A operand is row
+  // gather[R] / gather_k of the A pointer (the token of sorted pair R),
+  // so a GEMM reads the unpermuted hidden states directly
+  const int32_t* gather = nullptr;
+  int gather_k = 1;
 };
+
+// The A row that holds compact row R (R itself without a gather table).
+__device__ __forceinline__ int64_t a_row(const Tables& tb, int64_t R) {
+  return tb.gather ? static_cast<int64_t>(tb.gather[R] / tb.gather_k) : R;
+}
 
 // Row recovery of padded block bx (the tutorial's m_start identity): expert
 // g, first compact row m_start = bx*bm - gpo[g] + go[g], and the block's

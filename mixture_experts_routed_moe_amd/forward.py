@@ -5,7 +5,11 @@ kernel" and "Unpermute"; #778, "Partial output contract" for the shared
 expert): routing, dispatch tables, permute, gate_up GEMM (+ SwiGLU), down
 GEMM, unpermute with the routing weights and routed_scaling_factor folded in
 before the store. The shared expert, when given, runs the same two GEMMs on
-all tokens as one dense group and joins the unpermute as its addend.
+all tokens as one dense group and joins the unpermute as its addend. By
+default the permute is folded into the gate_up GEMM, which reads each
+permuted row from the hidden states through the dispatch permutation
+(`grouped_gemm_gate_up_gather`); `fuse_permute=False` runs it as its own
+copy first.
 
 `MoEBuffers` holds every intermediate for one problem size so a forward
 allocates nothing; all work is enqueued on the current stream without a host
@@ -44,15 +48,17 @@ class MoEShape:
 class MoEBuffers:
     """Device buffers for every intermediate of one forward of `shape`."""
 
-    def __init__(self, shape: MoEShape, device, fuse_swiglu: bool = True):
+    def __init__(self, shape: MoEShape, device, fuse_swiglu: bool = True, fuse_permute: bool = True):
         s = shape
         self.shape = s
         self.fuse_swiglu = fuse_swiglu
+        self.fuse_permute = fuse_permute
         bf16 = dict(dtype=torch.bfloat16, device=device)
         self.topk_ids = torch.empty(s.T, s.top_k, dtype=torch.int32, device=device)
         self.topk_weights = torch.empty(s.T, s.top_k, dtype=torch.float32, device=device)
         self.tables = _lib.alloc_tables(s.numel, s.E, s.padding_m, s.block_m, device)
-        self.x_perm = torch.empty(s.numel, s.H, **bf16)
+        # the permuted copy of the hidden states exists only without the gather
+        self.x_perm = None if fuse_permute else torch.empty(s.numel, s.H, **bf16)
         self.gate_up = None if fuse_swiglu else torch.empty(s.numel, 2 * s.F, **bf16)
         self.h = torch.empty(s.numel, s.F, **bf16)
         self.y = torch.empty(s.numel, s.H, **bf16)
@@ -71,7 +77,7 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
                        fuse_swiglu: bool = True, buffers: Optional[MoEBuffers] = None,
                        expert_bias: Optional[torch.Tensor] = None, scoring: str = "softmax",
                        renormalize: bool = True, return_parts: bool = False,
-                       shared_stream: Optional[torch.cuda.Stream] = None):
+                       shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True):
     """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden)).
 
     With return_parts=True returns (shared_out, routed_out) instead, the split
@@ -80,6 +86,10 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     adds them (after its all-reduce of shared_out when the shared expert is
     tensor-parallel). Otherwise the shared output is added inside the
     unpermute before its single rounding.
+
+    fuse_permute: the gate_up GEMM reads each permuted row straight from
+    `hidden` (row sorted_pair[r] // top_k) instead of a permuted copy written
+    by moe_permute: the same bytes, without the copy's write and re-read.
 
     shared_stream: a stream (of default priority) for the shared expert's
     GEMMs; it first waits for the work already on the current stream, and
@@ -95,8 +105,9 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     shape = MoEShape(T, H, F, E, top_k, padding_m, block_m, shared_F)
     b = buffers
     if b is None:
-        b = MoEBuffers(shape, hidden.device, fuse_swiglu)
-    elif dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu:
+        b = MoEBuffers(shape, hidden.device, fuse_swiglu, fuse_permute)
+    elif (dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu
+          or b.fuse_permute != fuse_permute):
         raise ValueError("routed_moe_forward: buffers were made for another shape")
 
     def shared_expert():
@@ -115,11 +126,13 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
             shared_expert()
     _lib.moe_topk_softmax(router_logits, top_k, b.topk_ids, b.topk_weights, expert_bias, scoring, renormalize)
     tb = _lib.moe_align(b.topk_ids, E, padding_m, block_m, b.tables)
-    _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm, tb["pair_to_row"])
-    if fuse_swiglu:
-        _lib.grouped_gemm_gate_up(b.x_perm, w_gate_up, tb, padding_m, block_m, True, b.h)
+    gu_out = b.h if fuse_swiglu else b.gate_up
+    if fuse_permute:
+        _lib.grouped_gemm_gate_up_gather(hidden, w_gate_up, tb, top_k, padding_m, block_m, fuse_swiglu, gu_out)
     else:
-        _lib.grouped_gemm_gate_up(b.x_perm, w_gate_up, tb, padding_m, block_m, False, b.gate_up)
+        _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm, tb["pair_to_row"])
+        _lib.grouped_gemm_gate_up(b.x_perm, w_gate_up, tb, padding_m, block_m, fuse_swiglu, gu_out)
+    if not fuse_swiglu:
         _lib.swiglu(b.gate_up, b.h)
     _lib.grouped_gemm_down(b.h, w_down, tb, padding_m, block_m, b.y)
     addend = None
@@ -137,8 +150,9 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
 
 
 def intermediates(b: MoEBuffers) -> Dict[str, torch.Tensor]:
-    d = {"topk_ids": b.topk_ids, "topk_weights": b.topk_weights, "x_perm": b.x_perm, "h": b.h, "y": b.y,
-         "out": b.out}
+    d = {"topk_ids": b.topk_ids, "topk_weights": b.topk_weights, "h": b.h, "y": b.y, "out": b.out}
+    if b.x_perm is not None:
+        d["x_perm"] = b.x_perm
     d.update({k: v for k, v in b.tables.items() if k != "workspace"})
     if b.gate_up is not None:
         d["gate_up"] = b.gate_up

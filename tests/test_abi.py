@@ -61,7 +61,7 @@ def test_num_blocks_matches_worked_example(lib):
     assert lib.moe_num_blocks(100, 3, 64, 128) == 2 + 6
     assert lib.moe_num_blocks(10, 3, 64, 96) == -1
     assert lib.moe_num_blocks(0, 8, 64, 64) == 8
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def test_workspace_size(lib):
@@ -86,6 +86,16 @@ def test_argument_errors_return_before_launch(lib):
     lib.grouped_gemm_gate_up.argtypes = [P] * 6 + [c.c_int64] + [c.c_int] * 6 + [P, P]
     assert lib.grouped_gemm_gate_up(None, None, None, None, None, None, 8, 1, 128, 128, 128, 96, 1, None, None) == -2
     assert lib.grouped_gemm_gate_up(None, None, 1, None, None, None, 8, 1, 128, 128, 128, 128, 1, None, None) == -1
+    # the gathering gate_up: tables required, numel must be T * top_k; T = 0 is a no-op
+    lib.grouped_gemm_gate_up_gather.argtypes = ([P, c.c_int64, P, c.c_int] + [P] * 5 + [c.c_int64] +
+                                                [c.c_int] * 6 + [P, P])
+    assert lib.grouped_gemm_gate_up_gather(None, 4, None, 2, None, None, None, None, None, 8, 1, 128, 128, 128, 128, 1,
+                                           None, None) == -1                        # dense (NULL tables)
+    assert b"tables" in lib.moe_last_error()
+    assert lib.grouped_gemm_gate_up_gather(None, 4, None, 2, None, 1, 1, 1, 1, 0, 8, 128, 128, 128, 128, 1,
+                                           None, None) == -1                        # numel != T * top_k
+    assert lib.grouped_gemm_gate_up_gather(None, 0, None, 2, None, 1, 1, 1, 1, 0, 8, 128, 128, 128, 128, 1,
+                                           None, None) == 0                         # nothing to do
     # quantizer: F not a multiple of 128; M = 0 is a no-op
     lib.swiglu_quant_fp8.argtypes = [P, c.c_int64, c.c_int] + [P] * 5
     assert lib.swiglu_quant_fp8(None, 4, 100, None, None, None, None, None) == -1

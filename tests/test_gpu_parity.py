@@ -199,6 +199,38 @@ def test_grouped_gemm_gate_up_and_down(cfg):
     say("  down max abs err", err)
 
 
+# the gathering gate_up on each kernel path: 64-row blocks (register-staged),
+# few rows per expert (128-row pipeline), >= 128 rows per expert (256-row
+# kernel), one token's top-k over 160 experts (few-row kernel)
+WIDE = moe_synth.MoEConfig(82, "wide", T=2048, H=256, F=384, E=8, top_k=2, padding_m=128, block_m=128)
+ONE_TOKEN = moe_synth.MoEConfig(83, "one_token", T=1, H=256, F=384, E=160, top_k=8, padding_m=128, block_m=128)
+
+
+@pytest.mark.parametrize("cfg", [MID64, MID, WIDE, ONE_TOKEN], ids=["mid64", "mid", "wide", "one_token"])
+def test_gate_up_gather_equals_permute_then_gemm(cfg):
+    """The permute folded into gate_up's A loads gives the same bytes as
+    moe_permute followed by grouped_gemm_gate_up (whose oracle parity the
+    tests above establish), fused and unfused; plus the oracle directly on the
+    unfused product."""
+    d = dev()
+    say("gather gemm", cfg.name)
+    hid = moe_synth.hidden(cfg, d)
+    xp, tb, _, _ = _gemm_setup(cfg, d)
+    wgu = moe_synth.w_gate_up(cfg, d)
+    for fuse in (True, False):
+        ref = mx.grouped_gemm_gate_up(xp, wgu, tb, cfg.padding_m, cfg.block_m, fuse_swiglu=fuse)
+        got = mx.grouped_gemm_gate_up_gather(hid, wgu, tb, cfg.top_k, cfg.padding_m, cfg.block_m, fuse_swiglu=fuse)
+        assert torch.equal(got, ref), f"fuse={fuse}"
+    # the oracle side from the oracle alone: routing, tables, permute, product
+    ref_ids, _ = oracle.route(host(moe_synth.router_logits(cfg, d)), cfg.top_k)
+    tab = oracle.dispatch_tables(ref_ids, cfg.E, cfg.padding_m, cfg.block_m)
+    for key in ("group_sizes", "group_offsets", "sorted_pair"):
+        assert np.array_equal(host(tb[key]), tab[key]), key
+    ref_xp = oracle.permute(bits(hid), tab["sorted_pair"], cfg.top_k)
+    ref_gu = oracle.grouped_gemm(ref_xp, bits(wgu), tab["group_sizes"], tab["group_offsets"])
+    assert_bf16_close(bits(got), ref_gu, "gather gate_up")
+
+
 @pytest.mark.parametrize("numel,bm", [(1, 64), (200, 128), (333, 64), (4096, 128)])
 def test_dense_group_gemm(numel, bm):
     d = dev()
