@@ -332,6 +332,36 @@ def test_grouped_gemm_wide_expert_groups(fused):
         assert_bf16_close(bits(y), oracle.grouped_gemm(bits(xp), bits(wd), gs, go), "down (16 col tiles)")
 
 
+@pytest.mark.parametrize("K", [64, 192, 448])
+def test_grouped_gemm_small_expert_tiles(K):
+    """Tiles of at most 32 valid rows inside a 256-row-kernel launch (experts
+    of 1 .. 33 rows, and the last rows of 257 / 289-row experts) beside
+    full and half tiles; K of 1, 3 and 7 steps of 64 (the half tiles split
+    their K sub-steps between two wave rows). gate_up with H = K, down with
+    F = K, fused and unfused, against the oracle."""
+    d = dev()
+    say("small expert tiles", K)
+    sizes = [1, 2, 5, 16, 31, 32, 33, 0, 600, 257, 289, 3, 2000]
+    E = len(sizes)
+    assert sum(sizes) >= 128 * E                 # the 256-row kernel's launch rule
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    ids_np = ids_np[np.random.default_rng(K).permutation(ids_np.size)][:, None]
+    T = ids_np.shape[0]
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    key = moe_synth.tensor_key(84, K)
+    F, H = 128, 256
+    x = moe_synth.normal_bf16(key, (T, K), 1.0, d)
+    wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, K), K ** -0.5, d)
+    gu = mx.grouped_gemm_gate_up(x, wgu, tb, 128, 128, fuse_swiglu=False)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(wgu), gs, go), f"gate_up K={K}")
+    h = mx.grouped_gemm_gate_up(x, wgu, tb, 128, 128, fuse_swiglu=True)
+    assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
+    wd = moe_synth.normal_bf16(key + 2, (E, H, K), K ** -0.5, d)
+    y = mx.grouped_gemm_down(x, wd, tb, 128, 128)
+    assert_bf16_close(bits(y), oracle.grouped_gemm(bits(x), bits(wd), gs, go), f"down K={K}")
+
+
 @pytest.mark.parametrize("H,F,extra_empty", [(256, 256, 0), (512, 384, 0), (256, 256, 20)])
 def test_grouped_gemm_expert_size_edges(H, F, extra_empty):
     """extra_empty appends empty experts; with 20 of them the rows per expert
