@@ -62,7 +62,7 @@ def parse():
                    help="time only the aligned grouped-GEMM cases (prints their JSON object)")
     p.add_argument("--gemm-cases", default="all",
                    help="aligned grouped-GEMM cases to time: 'all', 'none' or a comma-separated list of names")
-    p.add_argument("--cpu-tokens", type=int, default=24, help="tokens in the oracle's timed sample")
+    p.add_argument("--cpu-tokens", type=int, default=768, help="tokens in the oracle's timed sample (about 10 s)")
     p.add_argument("--unfused", action="store_true", help="gate_up GEMM then a separate SwiGLU kernel")
     p.add_argument("--permute-copy", action="store_true",
                    help="permute as its own copy kernel instead of inside the gate_up GEMM's loads")
@@ -523,17 +523,26 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def gemm_source_sha() -> str:
+    """First 16 hex digits of the sha256 over the GEMM kernels' sources
+    (gemm.hip, then moe_common.h): the revision a traffic figure belongs to."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "moe_common.h"):
+        with open(os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload, fused):
     """HBM bytes per launch of the routed gate_up GEMM from the committed rocprofv3
     FETCH_SIZE + WRITE_SIZE summary (scaled by the copy calibration), or None when
     that summary is for another workload or another revision of the kernel source."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"grouped_gemm_gate_up_{workload}.txt")
-    src = os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", "gemm.hip")
     if not fused or not os.path.exists(path):
         return None
     kv = dict(line.split("=", 1) for line in open(path).read().splitlines() if "=" in line and not line.startswith("#"))
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = gemm_source_sha()
     if kv.get("kernel_source_sha256_16") != sha:
         return None
     return int(float(kv["traffic_bytes"]))
