@@ -20,8 +20,10 @@ sample of tokens on the host cores. `other_workloads` times the same number
 of whole forwards (`routed_moe_forward`, the shared expert on a second stream,
 HIP events only around each forward) on the other forward shapes of the family
 (the Qwen3 prefill and decode shapes, the Kimi-K2 table's token counts when
-the DeepSeek-V3 prefill is the primary one), then as many staged forwards (in
-line, events around every stage) for each one's per-kernel figures.
+the DeepSeek-V3 prefill is the primary one), then as many replays of the same
+forward captured as a HIP graph (`ms_per_forward_graph`), then as many staged
+forwards (in line, events around every stage) for each one's per-kernel
+figures.
 `aligned_grouped_gemm` times the grouped GEMM alone on the aligned shapes of
 the pages' grouped-GEMM baseline table (E groups of M rows each), with that
 table's H200 figure beside each case as context. `grouped_quant` times the
@@ -177,7 +179,25 @@ class Workload:
         t1 = time.perf_counter()
         ms_per_step = (t1 - t0) * 1e3 / steps
         print(f"# {cfg.name}: timed {steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+        graph_ms = None
         if whole:
+            # the same forward captured once as a HIP graph, then replayed
+            g = self.mx.MoEForwardGraph(self.hidden, self.logits, self.wgu, self.wd, cfg.top_k, cfg.rsf,
+                                        cfg.padding_m, cfg.block_m, self.swgu, self.swd, fuse_swiglu=self.fuse,
+                                        buffers=self.bufs, expert_bias=self.bias, scoring=cfg.scoring,
+                                        renormalize=cfg.renormalize, shared_stream=side,
+                                        fuse_permute=self.bufs.fuse_permute)
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            gev = []
+            for _ in range(steps):
+                a = ev()
+                g.replay()
+                gev.append((a, ev()))
+            torch.cuda.synchronize()
+            graph_ms = sum(a.elapsed_time(b) for a, b in gev) / len(gev)
+            del g
             for _ in range(steps):
                 self.step(timed)
             torch.cuda.synchronize()
@@ -232,6 +252,8 @@ class Workload:
             "ms_per_forward": round(ms_per_step, 4), **{"step_" + k: v for k, v in step_pct.items()},
             "timing": ("whole forwards, shared expert on a second stream" if whole and side is not None and cfg.shared_F
                        else "whole forwards" if whole else "staged forwards, events around every stage"),
+            "ms_per_forward_graph": None if graph_ms is None else round(graph_ms, 4),
+            "tflops_graph": None if graph_ms is None else round(flop_fwd / (graph_ms * 1e-3) / 1e12, 2),
             "tflops": round(flop_fwd / (ms_per_step * 1e-3) / 1e12, 2),
             "grouped_gemm_tflops": round((flop_gate_up + flop_down) / gemm_s / 1e12, 2),
             "grouped_gemm_mfma_frac": round((flop_gate_up + flop_down) / gemm_s / 1e12 / BF16_PEAK_TFLOPS, 4),

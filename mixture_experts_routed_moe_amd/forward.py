@@ -149,6 +149,53 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     return b.out
 
 
+class MoEForwardGraph:
+    """One forward captured as a HIP graph over static input tensors.
+
+    The library's calls allocate nothing, wait on nothing from the host and
+    issue no memset or copy, so with reusable buffers a forward is a fixed
+    sequence of kernel launches (plus, with `shared_stream`, a fork to that
+    stream and a join back) and captures whole. Replaying it costs one graph
+    launch instead of one host call per kernel, which is what the forward of a
+    few decode tokens is bound by. Write new inputs into `.hidden` and
+    `.logits` (in place), call `replay()`, read `.out`; the weights, the expert
+    bias and every other argument are fixed at capture. Replays are ordered on
+    the stream current at `replay()`.
+    """
+
+    def __init__(self, hidden: torch.Tensor, router_logits: torch.Tensor, w_gate_up: torch.Tensor,
+                 w_down: torch.Tensor, top_k: int, routed_scaling_factor: float = 1.0, padding_m: int = 128,
+                 block_m: int = 128, shared_w_gate_up: Optional[torch.Tensor] = None,
+                 shared_w_down: Optional[torch.Tensor] = None, fuse_swiglu: bool = True,
+                 buffers: Optional[MoEBuffers] = None, expert_bias: Optional[torch.Tensor] = None,
+                 scoring: str = "softmax", renormalize: bool = True,
+                 shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True):
+        T, H = hidden.shape
+        E, twoF, _ = w_gate_up.shape
+        shared_F = 0 if shared_w_down is None else shared_w_down.shape[1]
+        if buffers is None:
+            buffers = MoEBuffers(MoEShape(T, H, twoF // 2, E, top_k, padding_m, block_m, shared_F), hidden.device,
+                                 fuse_swiglu, fuse_permute)
+        self.hidden, self.logits, self.buffers = hidden, router_logits, buffers
+
+        def run():
+            return routed_moe_forward(hidden, router_logits, w_gate_up, w_down, top_k, routed_scaling_factor,
+                                      padding_m, block_m, shared_w_gate_up, shared_w_down, fuse_swiglu, buffers,
+                                      expert_bias, scoring, renormalize, shared_stream=shared_stream,
+                                      fuse_permute=fuse_permute)
+
+        # one eager forward first: loads the library and checks every argument
+        run()
+        torch.cuda.current_stream(hidden.device).synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out = run()
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        return self.out
+
+
 def intermediates(b: MoEBuffers) -> Dict[str, torch.Tensor]:
     d = {"topk_ids": b.topk_ids, "topk_weights": b.topk_weights, "h": b.h, "y": b.y, "out": b.out}
     if b.x_perm is not None:

@@ -821,6 +821,49 @@ def test_forward_kimi_k2_single_token():
         assert torch.equal(_gpu_forward(cfg, inp, fuse, shared_stream=side), out)
 
 
+SHARED_SMALL = moe_synth.MoEConfig(85, "shared_small", T=64, H=256, F=128, E=16, top_k=4, padding_m=128,
+                                   block_m=128, shared_F=384, scoring="sigmoid")
+
+
+@pytest.mark.parametrize("name,side", [("qwen3_decode", False), ("shared_small", False), ("shared_small", True)])
+def test_forward_graph_replay(name, side):
+    """The forward captured as a HIP graph (with the shared expert forked onto
+    a second stream for side=True): every replay, with eager work of the
+    program between replays, gives the eager forward's bytes; new inputs
+    written into the static tensors give the eager forward of those inputs,
+    which matches the oracle."""
+    d = dev()
+    cfg = SHARED_SMALL if name == "shared_small" else moe_synth.CONFIGS[name]
+    say("graph", name, side)
+    inp = inputs(cfg, d)
+    ref = _gpu_forward(cfg, inp).clone()
+    stream = torch.cuda.Stream(d) if side else None
+    g = mx.MoEForwardGraph(inp["hidden"].clone(), inp["logits"].clone(), inp["w_gate_up"], inp["w_down"], cfg.top_k,
+                           cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"), inp.get("shared_w_down"),
+                           expert_bias=inp.get("bias"), scoring=cfg.scoring, renormalize=cfg.renormalize,
+                           shared_stream=stream)
+    for rep in range(3):
+        g.out.zero_()
+        other = _gpu_forward(cfg, inp)          # eager work between replays
+        out = g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
+        assert torch.equal(other, ref)
+    # new inputs through the static tensors
+    key = moe_synth.tensor_key(86, cfg.T)
+    hid2 = moe_synth.normal_bf16(key, (cfg.T, cfg.H), 1.0, d)
+    lg2 = moe_synth.normal_f32(key + 1, (cfg.T, cfg.E), 1.0, d)
+    g.hidden.copy_(hid2)
+    g.logits.copy_(lg2)
+    out = g.replay().clone()
+    inp2 = dict(inp, hidden=hid2, logits=lg2)
+    ref2 = _gpu_forward(cfg, inp2)
+    assert torch.equal(out, ref2)
+    if name == "shared_small":
+        exp = oracle_tokens(cfg, inp2, np.arange(cfg.T))
+        assert_bf16_close(bits(out), exp["out"], "graph replay, new inputs")
+
+
 # sampled tokens per workload: each one brings up to k experts' weights to the host
 SAMPLED_TOKENS = {"qwen3_prefill": 21, "dsv3_prefill": 21, "kimi_k2_t32": 3, "kimi_k2_t512": 3, "kimi_k2_t4096": 3}
 
