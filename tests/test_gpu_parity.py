@@ -618,11 +618,12 @@ def test_fp8_block_quant_weights_bit_exact():
     assert not q["q"][1, :128, 128:256].any() and q["s"][1, 0, 1].item() == 0.0
 
 
-@pytest.mark.parametrize("N,K,extra_empty", [(256, 256, 0), (384, 512, 3)])
+@pytest.mark.parametrize("N,K,extra_empty", [(256, 256, 0), (384, 512, 3), (512, 384, 2), (768, 128, 0)])
 def test_grouped_gemm_fp8_expert_size_edges(N, K, extra_empty):
     """Expert sizes around the 128-row block (0, 1, 127..129, 255..257, ...),
     empty experts, every output against the oracle on the oracle's own codes;
-    the GPU's codes equal the oracle's bit for bit."""
+    the GPU's codes equal the oracle's bit for bit; two to six 128-column
+    tiles, K of one to four 128-wide steps."""
     d = dev()
     sizes = EDGE_SIZES + [0] * extra_empty
     tb, h, w, gs, go = _fp8_case(sizes, N, K, 96 + extra_empty, d)
