@@ -803,6 +803,8 @@ def test_forward_full_oracle(name):
         out = _gpu_forward(cfg, inp, fuse)
         err = assert_bf16_close(bits(out), ref["out"], f"{name} out fuse={fuse}")
         say("  out max abs err", err, "fuse", fuse)
+        # the permute as its own copy kernel instead of inside gate_up's loads: same bytes
+        assert torch.equal(_gpu_forward(cfg, inp, fuse, fuse_permute=False), out)
 
 
 def test_forward_kimi_k2_single_token():
