@@ -29,7 +29,8 @@ the pages' grouped-GEMM baseline table (E groups of M rows each), with that
 table's H200 figure beside each case as context. `grouped_quant` times the
 grouped (expand_128x) FP8 quantizer on the pages' single-kernel benchmark
 shapes; `fp8_down` the primary workload's down projection on the FP8 path
-(1x128-tile e4m3 activations, 128x128-block e4m3 weights) beside the bf16 one.
+(1x128-tile e4m3 activations, 128x128-block e4m3 weights) beside the bf16 one,
+and the whole forward with that FP8 down projection (`forward_ms`).
 """
 from __future__ import annotations
 
@@ -377,7 +378,27 @@ def fp8_down(wl, steps, warmup, ev):
     g_list = [a.elapsed_time(b) for a, b in eg]
     g_ms = sum(g_list) / len(g_list)
     flop = 2.0 * cfg.numel * cfg.H * cfg.F
+    # whole forwards with the routed down projection in FP8 (row-layout codes of h)
+    b8 = mx.MoEBuffers(wl.bufs.shape, wl.hidden.device, wl.fuse, wl.bufs.fuse_permute, fp8_down=True)
+
+    def fwd8():
+        mx.routed_moe_forward(wl.hidden, wl.logits, wl.wgu, wl.wd, cfg.top_k, cfg.rsf, cfg.padding_m, cfg.block_m,
+                              wl.swgu, wl.swd, fuse_swiglu=wl.fuse, buffers=b8, expert_bias=wl.bias,
+                              scoring=cfg.scoring, renormalize=cfg.renormalize, fuse_permute=wl.bufs.fuse_permute,
+                              w_down_fp8=qw)
+    for _ in range(warmup):
+        fwd8()
+    ef = []
+    for _ in range(steps):
+        a = ev()
+        fwd8()
+        ef.append((a, ev()))
+    torch.cuda.synchronize()
+    f_ms = sum(a.elapsed_time(b) for a, b in ef) / len(ef)
+    flop_fwd = 6.0 * cfg.numel * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.shared_F
+    del b8
     return {"gemm_ms": round(g_ms, 4), **pct(g_list), "quant_h_ms": round(q_ms, 4),
+            "forward_ms": round(f_ms, 4), "forward_tflops": round(flop_fwd / (f_ms * 1e-3) / 1e12, 2),
             "tflops": round(flop / (g_ms * 1e-3) / 1e12, 2),
             "fp8_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
             "bf16_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}

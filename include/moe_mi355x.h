@@ -227,10 +227,14 @@ int swiglu_quant_fp8(const uint16_t* gate_up, int64_t M, int F, uint8_t* q_row, 
  *                block of a group (amax over real rows);
  *                per_tile=1: s_t [K, m_pad/128], one scale per column and
  *                128-row tile of a group. Scales past the total are 0.
+ *   q_t = s_t = NULL: the row layout only (what a forward GEMM on the
+ *                codes reads); group_sizes, E, per_tile and m_pad then play
+ *                no part, and the row bytes are those of the full call.
  * Scales fl32(amax/448), codes e4m3(fl32(h/s)), zero tiles 0x00 as above.
  * Rows must be 16-byte aligned (x, q_row, q_t); K % 128 == 0; M, m_pad < 2^31.
- * Returns MOE_ERR_INVALID_ARG for bad sizes or flags (nothing enqueued);
- * M = 0 with m_pad > 0 zero-fills q_t and s_t. */
+ * Returns MOE_ERR_INVALID_ARG for bad sizes or flags, or for exactly one of
+ * q_t, s_t NULL (nothing enqueued); M = 0 with m_pad > 0 zero-fills q_t and
+ * s_t. */
 int tile_quant_fp8(const uint16_t* x, int64_t M, int K, int swiglu, const int32_t* group_sizes, int E,
                    int per_tile, int64_t m_pad, uint8_t* q_row, float* s_row, uint8_t* q_t, float* s_t,
                    hipStream_t stream);

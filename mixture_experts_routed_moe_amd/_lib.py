@@ -295,19 +295,24 @@ def tile_quant_fp8_m_pad_bound(M: int, E: int) -> int:
 
 def tile_quant_fp8(x: torch.Tensor, group_sizes: Optional[torch.Tensor] = None, per_tile: bool = False,
                    swiglu: bool = False, m_pad: Optional[int] = None,
-                   out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+                   out: Optional[Dict[str, torch.Tensor]] = None, transposed: bool = True) -> Dict[str, torch.Tensor]:
     """Row (1x128) and grouped expand_128x transposed e4m3 quantization of x
     ([M, K] bf16, or gate_up [M, 2K] with swiglu=True). Without m_pad, q_t is
     ceil(M/128)*128 wide for one group and tile_quant_fp8_m_pad_bound(M, E)
-    wide for E groups (the group sizes stay on the device)."""
+    wide for E groups (the group sizes stay on the device). transposed=False:
+    the row layout only ({"q_row", "s_row"})."""
     M, W = x.shape
     K = W // 2 if swiglu else W
-    E = 0 if group_sizes is None else int(group_sizes.numel())
-    if m_pad is None:
-        m_pad = -(-M // 128) * 128 if group_sizes is None else tile_quant_fp8_m_pad_bound(M, E)
     o = out or {}
     q_row = _out(o.get("q_row"), (M, K), torch.uint8, x, "q_row")
     s_row = _out(o.get("s_row"), (M, K // 128), torch.float32, x, "s_row")
+    if not transposed:
+        _call("tile_quant_fp8", _ptr(x, torch.bfloat16, "x"), M, K, int(swiglu), None, 0, 0, 0,
+              _ptr(q_row, torch.uint8, "q_row"), _ptr(s_row, torch.float32, "s_row"), None, None, _stream(x))
+        return {"q_row": q_row, "s_row": s_row}
+    E = 0 if group_sizes is None else int(group_sizes.numel())
+    if m_pad is None:
+        m_pad = -(-M // 128) * 128 if group_sizes is None else tile_quant_fp8_m_pad_bound(M, E)
     q_t = _out(o.get("q_t"), (K, m_pad), torch.uint8, x, "q_t")
     s_t = _out(o.get("s_t"), ((K if per_tile else K // 128), m_pad // 128), torch.float32, x, "s_t")
     _call("tile_quant_fp8", _ptr(x, torch.bfloat16, "x"), M, K, int(swiglu), _ptr(group_sizes, torch.int32, "group_sizes"),

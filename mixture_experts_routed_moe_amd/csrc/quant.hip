@@ -176,7 +176,7 @@ __device__ __forceinline__ bool find_group_block(const int32_t* __restrict__ gs,
 // q_t row of the block) instead of one per 128x128 block. gs == nullptr: one
 // group of M rows (GROUPED = false). Blocks past the groups' padded total
 // write zero codes and scales into their q_t columns.
-template <bool SWIGLU, bool PER_TILE, bool GROUPED>
+template <bool SWIGLU, bool PER_TILE, bool GROUPED, bool TRANS = true>
 __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                    const int32_t* __restrict__ gs, int E, int m_pad,
                                                                    int n_fb, uint8_t* __restrict__ q_row,
@@ -209,6 +209,7 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
     live = live && r0 >= 0 && rows > 0;
   }
   if (!live) {
+    if constexpr (!TRANS) return;
     // past the last group: zero codes and scales in this block's q_t columns
 #pragma unroll
     for (int r = 0; r < (kTile * kTile / 16) / kQuantThreads; ++r) {
@@ -321,7 +322,9 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
   // thread's column col0 + j)
   float sb = 0.0f, s_col[8];
   double inv_sb = 0.0, inv_col[8];
-  if constexpr (PER_TILE) {
+  if constexpr (!TRANS) {
+    // row layout only: no transposed scales
+  } else if constexpr (PER_TILE) {
     // columns: over the wave's 4 row groups (lanes 16 apart), then the 8 waves through LDS
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -375,13 +378,15 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
       const double d0 = static_cast<double>(hv(i, j)), d1 = static_cast<double>(hv(i + 1, j));
       qr[0][j] = static_cast<float>(d0 * inv_r[0]);
       qr[1][j] = static_cast<float>(d1 * inv_r[1]);
-      const double inv_t = PER_TILE ? inv_col[j] : inv_sb;
-      float b0 = static_cast<float>(d0 * inv_t), b1 = static_cast<float>(d1 * inv_t);
-      if (PER_TILE && !(s_col[j] > 0.0f)) b0 = b1 = 0.0f;   // an all-zero column tile: codes 0
-      if (i == 0)
-        qt[j] = fp8x2<false>(b0, b1, 0u);
-      else
-        qt[j] = fp8x2<true>(b0, b1, qt[j]);
+      if constexpr (TRANS) {
+        const double inv_t = PER_TILE ? inv_col[j] : inv_sb;
+        float b0 = static_cast<float>(d0 * inv_t), b1 = static_cast<float>(d1 * inv_t);
+        if (PER_TILE && !(s_col[j] > 0.0f)) b0 = b1 = 0.0f;   // an all-zero column tile: codes 0
+        if (i == 0)
+          qt[j] = fp8x2<false>(b0, b1, 0u);
+        else
+          qt[j] = fp8x2<true>(b0, b1, qt[j]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -398,6 +403,7 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
       }
     }
   }
+  if constexpr (!TRANS) return;
   if (!PER_TILE && !(sb > 0.0f)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) qt[j] = 0u;
@@ -462,7 +468,11 @@ int launch_tile_quant(const uint16_t* x, int64_t M, int K, const int32_t* gs, in
 #define MOE_TQ(PT, GR)                                                                                   \
   tile_quant_kernel<SWIGLU, PT, GR><<<grid, kQuantThreads, 0, stream>>>(x, Mi, K, gs, E, mp, n_fb, q_row, s_row, \
                                                                         q_t, s_t)
-  if (gs == nullptr) {
+  if (q_t == nullptr) {
+    // row layout only (no transposed outputs): one pass over ceil(M/128) blocks
+    tile_quant_kernel<SWIGLU, false, false, false><<<grid, kQuantThreads, 0, stream>>>(
+        x, Mi, K, nullptr, 0, mp, n_fb, q_row, s_row, nullptr, nullptr);
+  } else if (gs == nullptr) {
     if (per_tile) MOE_TQ(true, false);
     else MOE_TQ(false, false);
   } else {
@@ -504,18 +514,31 @@ extern "C" int tile_quant_fp8(const uint16_t* x, int64_t M, int K, int swiglu, c
   const char* name = "tile_quant_fp8";
   if (M < 0 || K < kTile || K % kTile != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: M=%lld K=%d (K must be a positive multiple of 128)", name, (long long)M, K);
+  if (swiglu != 0 && swiglu != 1) return fail(MOE_ERR_INVALID_ARG, "%s: swiglu=%d", name, swiglu);
+  if (per_tile != 0 && per_tile != 1) return fail(MOE_ERR_INVALID_ARG, "%s: per_tile=%d", name, per_tile);
+  if ((q_t == nullptr) != (s_t == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "%s: q_t and s_t must both be given or both be NULL", name);
+  if (q_t == nullptr) {
+    // row layout only: group sizes, per_tile and m_pad play no part
+    if (M == 0) return MOE_OK;
+    if (M >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: M too large", name);
+    if (!x || !q_row || !s_row) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+    if (!aligned16(x) || !aligned16(q_row)) return fail(MOE_ERR_INVALID_ARG, "%s: x/q_row not 16-byte aligned", name);
+    const int64_t rows_pad = ceil_div(M, kTile) * kTile;
+    if (swiglu)
+      return launch_tile_quant<true>(x, M, K, nullptr, 0, 0, rows_pad, q_row, s_row, nullptr, nullptr, stream, name);
+    return launch_tile_quant<false>(x, M, K, nullptr, 0, 0, rows_pad, q_row, s_row, nullptr, nullptr, stream, name);
+  }
   if (m_pad < 0 || m_pad % kTile != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: m_pad=%lld must be a non-negative multiple of 128", name, (long long)m_pad);
   if (group_sizes == nullptr && m_pad < ceil_div(M, kTile) * kTile)
     return fail(MOE_ERR_INVALID_ARG, "%s: m_pad=%lld < %lld padded rows", name, (long long)m_pad,
                 (long long)(ceil_div(M, kTile) * kTile));
   if (group_sizes != nullptr && (E < 1 || E > 65536)) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d", name, E);
-  if (swiglu != 0 && swiglu != 1) return fail(MOE_ERR_INVALID_ARG, "%s: swiglu=%d", name, swiglu);
-  if (per_tile != 0 && per_tile != 1) return fail(MOE_ERR_INVALID_ARG, "%s: per_tile=%d", name, per_tile);
   if (m_pad >= (int64_t(1) << 31) || M >= (int64_t(1) << 31) || m_pad * static_cast<int64_t>(K) >= (int64_t(1) << 40))
     return fail(MOE_ERR_UNSUPPORTED, "%s: M or m_pad too large", name);
   if (m_pad == 0) return MOE_OK;
-  if (!q_t || !s_t || (M > 0 && (!x || !q_row || !s_row))) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (M > 0 && (!x || !q_row || !s_row)) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
   if ((x && !aligned16(x)) || (q_row && !aligned16(q_row)) || !aligned16(q_t))
     return fail(MOE_ERR_INVALID_ARG, "%s: x/q_row/q_t not 16-byte aligned", name);
   if (swiglu)

@@ -48,11 +48,13 @@ class MoEShape:
 class MoEBuffers:
     """Device buffers for every intermediate of one forward of `shape`."""
 
-    def __init__(self, shape: MoEShape, device, fuse_swiglu: bool = True, fuse_permute: bool = True):
+    def __init__(self, shape: MoEShape, device, fuse_swiglu: bool = True, fuse_permute: bool = True,
+                 fp8_down: bool = False):
         s = shape
         self.shape = s
         self.fuse_swiglu = fuse_swiglu
         self.fuse_permute = fuse_permute
+        self.fp8_down = fp8_down
         bf16 = dict(dtype=torch.bfloat16, device=device)
         self.topk_ids = torch.empty(s.T, s.top_k, dtype=torch.int32, device=device)
         self.topk_weights = torch.empty(s.T, s.top_k, dtype=torch.float32, device=device)
@@ -62,6 +64,10 @@ class MoEBuffers:
         self.gate_up = None if fuse_swiglu else torch.empty(s.numel, 2 * s.F, **bf16)
         self.h = torch.empty(s.numel, s.F, **bf16)
         self.y = torch.empty(s.numel, s.H, **bf16)
+        # e4m3 codes of h and their 1x128-tile scales, for the FP8 down projection
+        self.qa = None if not fp8_down else {
+            "q_row": torch.empty(s.numel, s.F, dtype=torch.uint8, device=device),
+            "s_row": torch.empty(s.numel, s.F // 128, dtype=torch.float32, device=device)}
         self.out = torch.empty(s.T, s.H, **bf16)
         if s.shared_F:
             self.shared_gate_up = None if fuse_swiglu else torch.empty(s.T, 2 * s.shared_F, **bf16)
@@ -77,7 +83,8 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
                        fuse_swiglu: bool = True, buffers: Optional[MoEBuffers] = None,
                        expert_bias: Optional[torch.Tensor] = None, scoring: str = "softmax",
                        renormalize: bool = True, return_parts: bool = False,
-                       shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True):
+                       shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True,
+                       w_down_fp8: Optional[Dict[str, torch.Tensor]] = None):
     """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden)).
 
     With return_parts=True returns (shared_out, routed_out) instead, the split
@@ -86,6 +93,12 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     adds them (after its all-reduce of shared_out when the shared expert is
     tensor-parallel). Otherwise the shared output is added inside the
     unpermute before its single rounding.
+
+    w_down_fp8: the routed down projection in FP8: {"q", "s"} from
+    fp8_block_quant_weights(w_down) (e4m3 codes [E, H, F], one scale per
+    128x128 block); h is quantized to 1x128-tile e4m3 codes (row layout) and
+    grouped_gemm_fp8 replaces the bf16 down GEMM (block_m 128; buffers made
+    with fp8_down=True). The shared expert stays bf16.
 
     fuse_permute: the gate_up GEMM reads each permuted row straight from
     `hidden` (row sorted_pair[r] // top_k) instead of a permuted copy written
@@ -105,9 +118,9 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     shape = MoEShape(T, H, F, E, top_k, padding_m, block_m, shared_F)
     b = buffers
     if b is None:
-        b = MoEBuffers(shape, hidden.device, fuse_swiglu, fuse_permute)
+        b = MoEBuffers(shape, hidden.device, fuse_swiglu, fuse_permute, w_down_fp8 is not None)
     elif (dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu
-          or b.fuse_permute != fuse_permute):
+          or b.fuse_permute != fuse_permute or (w_down_fp8 is not None and b.qa is None)):
         raise ValueError("routed_moe_forward: buffers were made for another shape")
 
     def shared_expert():
@@ -134,7 +147,12 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
         _lib.grouped_gemm_gate_up(b.x_perm, w_gate_up, tb, padding_m, block_m, fuse_swiglu, gu_out)
     if not fuse_swiglu:
         _lib.swiglu(b.gate_up, b.h)
-    _lib.grouped_gemm_down(b.h, w_down, tb, padding_m, block_m, b.y)
+    if w_down_fp8 is None:
+        _lib.grouped_gemm_down(b.h, w_down, tb, padding_m, block_m, b.y)
+    else:
+        _lib.tile_quant_fp8(b.h, out=b.qa, transposed=False)
+        _lib.grouped_gemm_fp8(b.qa["q_row"], b.qa["s_row"], w_down_fp8["q"], w_down_fp8["s"], tb, padding_m,
+                              block_m, b.y)
     addend = None
     if shared_F:
         if side is None:
@@ -169,20 +187,21 @@ class MoEForwardGraph:
                  shared_w_down: Optional[torch.Tensor] = None, fuse_swiglu: bool = True,
                  buffers: Optional[MoEBuffers] = None, expert_bias: Optional[torch.Tensor] = None,
                  scoring: str = "softmax", renormalize: bool = True,
-                 shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True):
+                 shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True,
+                 w_down_fp8: Optional[Dict[str, torch.Tensor]] = None):
         T, H = hidden.shape
         E, twoF, _ = w_gate_up.shape
         shared_F = 0 if shared_w_down is None else shared_w_down.shape[1]
         if buffers is None:
             buffers = MoEBuffers(MoEShape(T, H, twoF // 2, E, top_k, padding_m, block_m, shared_F), hidden.device,
-                                 fuse_swiglu, fuse_permute)
+                                 fuse_swiglu, fuse_permute, w_down_fp8 is not None)
         self.hidden, self.logits, self.buffers = hidden, router_logits, buffers
 
         def run():
             return routed_moe_forward(hidden, router_logits, w_gate_up, w_down, top_k, routed_scaling_factor,
                                       padding_m, block_m, shared_w_gate_up, shared_w_down, fuse_swiglu, buffers,
                                       expert_bias, scoring, renormalize, shared_stream=shared_stream,
-                                      fuse_permute=fuse_permute)
+                                      fuse_permute=fuse_permute, w_down_fp8=w_down_fp8)
 
         # one eager forward first: loads the library and checks every argument
         run()

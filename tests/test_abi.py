@@ -106,14 +106,20 @@ def test_argument_errors_return_before_launch(lib):
     lib.tile_quant_fp8_m_pad_bound.argtypes = [c.c_int64, c.c_int]
     assert lib.tile_quant_fp8_m_pad_bound(385, 5) == 128 * (4 + 5)
     assert lib.tile_quant_fp8_m_pad_bound(-1, 5) == -1
-    assert lib.tile_quant_fp8(None, 4, 100, 0, None, 0, 0, 128, None, None, None, None, None) == -1   # K % 128
-    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 100, None, None, None, None, None) == -1   # m_pad % 128
-    assert lib.tile_quant_fp8(None, 300, 128, 0, None, 0, 0, 256, None, None, None, None, None) == -1  # m_pad < 384
-    assert lib.tile_quant_fp8(None, 4, 128, 2, None, 0, 0, 128, None, None, None, None, None) == -1   # swiglu flag
-    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 3, 128, None, None, None, None, None) == -1   # per_tile flag
-    assert lib.tile_quant_fp8(None, 4, 128, 0, 1, 0, 0, 128, None, None, None, None, None) == -1      # E < 1 with groups
-    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 128, None, None, None, None, None) == -1   # null outputs
-    assert lib.tile_quant_fp8(None, 0, 128, 0, None, 0, 0, 0, None, None, None, None, None) == 0      # nothing to do
+    # (16, 32: stand-in q_t / s_t addresses, never dereferenced: every call below fails its checks first)
+    assert lib.tile_quant_fp8(None, 4, 100, 0, None, 0, 0, 128, None, None, 16, 32, None) == -1   # K % 128
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 100, None, None, 16, 32, None) == -1   # m_pad % 128
+    assert lib.tile_quant_fp8(None, 300, 128, 0, None, 0, 0, 256, None, None, 16, 32, None) == -1  # m_pad < 384
+    assert lib.tile_quant_fp8(None, 4, 128, 2, None, 0, 0, 128, None, None, 16, 32, None) == -1   # swiglu flag
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 3, 128, None, None, 16, 32, None) == -1   # per_tile flag
+    assert lib.tile_quant_fp8(None, 4, 128, 0, 1, 0, 0, 128, None, None, 16, 32, None) == -1      # E < 1 with groups
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 128, None, None, 16, 32, None) == -1   # null x / q_row
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 128, None, None, 16, None, None) == -1  # q_t without s_t
+    assert b"both" in lib.moe_last_error()
+    # row layout only (q_t = s_t = NULL): m_pad and the groups play no part
+    assert lib.tile_quant_fp8(None, 4, 128, 0, None, 0, 0, 0, None, None, None, None, None) == -1    # null x / q_row
+    assert lib.tile_quant_fp8(None, 0, 128, 0, None, 0, 0, 100, None, None, None, None, None) == 0   # nothing to do
+    assert lib.tile_quant_fp8(None, 0, 128, 0, None, 0, 0, 0, None, None, 16, 32, None) == 0         # nothing to do
     # FP8 weight preparation and the block-scaled FP8 grouped GEMM
     lib.fp8_block_quant_weights.argtypes = [P, c.c_int64, c.c_int, P, P, P]
     assert lib.fp8_block_quant_weights(None, 100, 128, None, None, None) == -1     # rows % 128

@@ -744,6 +744,27 @@ def test_tile_quant_ungrouped_equals_swiglu_quant_fp8():
             assert torch.equal(a[k], c[k]), (M, k, "h")
 
 
+@pytest.mark.parametrize("M", [1, 127, 300, 4224])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_tile_quant_row_only(M, swiglu):
+    """q_t = s_t = NULL: the row layout alone, the same bytes as the full call
+    (ungrouped and grouped) and as the oracle."""
+    d = dev()
+    K = 256
+    key = moe_synth.tensor_key(87, M, int(swiglu))
+    x = moe_synth.normal_bf16(key, (M, 2 * K if swiglu else K), 1.0, d)
+    rows = mx.tile_quant_fp8(x, None, swiglu=swiglu, transposed=False)
+    assert set(rows) == {"q_row", "s_row"}
+    full = mx.tile_quant_fp8(x, None, swiglu=swiglu)
+    assert torch.equal(rows["q_row"], full["q_row"]) and torch.equal(rows["s_row"], full["s_row"])
+    sizes = np.random.default_rng(M).multinomial(M, np.ones(5) / 5).astype(np.int32)
+    grouped = mx.tile_quant_fp8(x, _t(sizes, d), swiglu=swiglu)
+    assert torch.equal(rows["q_row"], grouped["q_row"]) and torch.equal(rows["s_row"], grouped["s_row"])
+    h = oracle.swiglu(bits(x), K) if swiglu else bits(x)
+    ref = oracle.quant_fp8(h)
+    assert np.array_equal(host(rows["q_row"]), ref["q_row"]) and np.array_equal(host(rows["s_row"]), ref["s_row"])
+
+
 def test_tile_quant_zero_rows_zero_fills():
     d = dev()
     x = torch.empty(0, 256, dtype=torch.bfloat16, device=d)
@@ -865,6 +886,37 @@ def test_forward_graph_replay(name, side):
     if name == "shared_small":
         exp = oracle_tokens(cfg, inp2, np.arange(cfg.T))
         assert_bf16_close(bits(out), exp["out"], "graph replay, new inputs")
+
+
+@pytest.mark.parametrize("side", [False, True])
+def test_forward_fp8_down(side):
+    """The forward with its routed down projection in FP8 (h quantized to
+    1x128-tile e4m3 codes, block-scaled FP8 grouped GEMM): the same bytes as
+    the stages called one by one (each of them checked against the oracle
+    above), and within e4m3's quantization error of the oracle's bf16
+    forward (relative L2 error under 5%, which the codes' 3-bit mantissa
+    sets; a wrong scale or a dropped block would be far above it)."""
+    d = dev()
+    cfg = SHARED_SMALL
+    inp = inputs(cfg, d)
+    qw = mx.fp8_block_quant_weights(inp["w_down"])
+    stream = torch.cuda.Stream(d) if side else None
+    out = _gpu_forward(cfg, inp, w_down_fp8=qw, shared_stream=stream).clone()
+    # the same stages called one by one
+    ids, w = mx.moe_topk_softmax(inp["logits"], cfg.top_k, scoring=cfg.scoring, renormalize=cfg.renormalize)
+    tb = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
+    h = mx.grouped_gemm_gate_up_gather(inp["hidden"], inp["w_gate_up"], tb, cfg.top_k, cfg.padding_m, cfg.block_m)
+    qa = mx.tile_quant_fp8(h, transposed=False)
+    y = mx.grouped_gemm_fp8(qa["q_row"], qa["s_row"], qw["q"], qw["s"], tb, cfg.padding_m, cfg.block_m)
+    sh = mx.grouped_gemm_down(mx.grouped_gemm_gate_up(inp["hidden"], inp["shared_w_gate_up"], None, 128, 128),
+                              inp["shared_w_down"], None, 128, 128)
+    ref = mx.moe_unpermute(y, tb["pair_to_row"], w, cfg.rsf, sh)
+    assert torch.equal(out, ref)
+    exp = oracle_tokens(cfg, inp, np.arange(cfg.T))["out"]
+    o, e = nm.bf16_to_f64(bits(out)), nm.bf16_to_f64(exp)
+    rel = np.linalg.norm(o - e) / np.linalg.norm(e)
+    say("  fp8-down forward relative L2 error vs the bf16 oracle", rel)
+    assert rel < 0.05
 
 
 # sampled tokens per workload: each one brings up to k experts' weights to the host
