@@ -65,7 +65,7 @@ def parse():
                    help="time only the aligned grouped-GEMM cases (prints their JSON object)")
     p.add_argument("--gemm-cases", default="all",
                    help="aligned grouped-GEMM cases to time: 'all', 'none' or a comma-separated list of names")
-    p.add_argument("--cpu-tokens", type=int, default=2048, help="tokens in the oracle's timed sample (10-15 s)")
+    p.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the oracle's timed sample (the whole T=4096 batch, about 11 s)")
     p.add_argument("--unfused", action="store_true", help="gate_up GEMM then a separate SwiGLU kernel")
     p.add_argument("--permute-copy", action="store_true",
                    help="permute as its own copy kernel instead of inside the gate_up GEMM's loads")
