@@ -231,6 +231,45 @@ def test_gate_up_gather_equals_permute_then_gemm(cfg):
     assert_bf16_close(bits(got), ref_gu, "gather gate_up")
 
 
+def test_gate_up_gather_past_4gib():
+    """Hidden states past 2^32 bytes (T = 300000, H = 7168: 4.3 GB): the
+    256-row kernel addresses gathered rows with 32-bit offsets from the
+    first hidden row, so this launch must take the 128-row kernel; the
+    permuted copy (8.6 GB of x_perm reads and writes) goes through the
+    256-row kernel with per-tile offsets. Sampled rows of both against the
+    oracle, including the last rows of the array."""
+    d = dev()
+    T, H, F, E, k = 300_000, 7168, 128, 4, 1
+    assert T * H * 2 >= 1 << 32
+    say("gather past 4 GiB", T, H)
+    key = moe_synth.tensor_key(88)
+    hid = moe_synth.normal_bf16(key, (T, H), 1.0, d)
+    ids_np = np.random.default_rng(88).integers(0, E, size=(T, k)).astype(np.int32)
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, H), H ** -0.5, d)
+    h_g = mx.grouped_gemm_gate_up_gather(hid, wgu, tb, k, 128, 128)
+    xp = mx.moe_permute(hid, None, k, pair_to_row=tb["pair_to_row"])
+    h_p = mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128)
+    del xp
+    torch.cuda.synchronize()
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    sp = host(tb["sorted_pair"])
+    rows = np.unique(np.concatenate([[0, T - 1], go[1:] - 1, go, np.random.default_rng(1).choice(T, 24)]))
+    rows = rows[(rows >= 0) & (rows < T)]
+    expert = np.searchsorted(np.concatenate([go, [T]]), rows, side="right") - 1
+    for e in range(E):
+        sel = rows[expert == e]
+        if sel.size == 0:
+            continue
+        a = bits(hid[torch.as_tensor(sp[sel] // k, device=d)])
+        ref = oracle.swiglu(oracle.grouped_gemm(a, bits(wgu[e:e + 1]), np.array([sel.size], np.int32),
+                                                np.array([0], np.int32)), F)
+        got_g = bits(h_g[torch.as_tensor(sel, device=d)])
+        got_p = bits(h_p[torch.as_tensor(sel, device=d)])
+        assert_bf16_close(got_g, ref, f"gather, expert {e}")
+        assert_bf16_close(got_p, ref, f"permuted copy, expert {e}")
+
+
 @pytest.mark.parametrize("numel,bm", [(1, 64), (200, 128), (333, 64), (4096, 128)])
 def test_dense_group_gemm(numel, bm):
     d = dev()
