@@ -30,7 +30,9 @@ table's H200 figure beside each case as context. `grouped_quant` times the
 grouped (expand_128x) FP8 quantizer on the pages' single-kernel benchmark
 shapes; `fp8_down` the primary workload's down projection on the FP8 path
 (1x128-tile e4m3 activations, 128x128-block e4m3 weights) beside the bf16 one,
-and the whole forward with that FP8 down projection (`forward_ms`).
+and the whole forward with that FP8 down projection (`forward_ms`); then the
+routed gate_up in FP8 (`gate_up_gemm_ms`) and the forward with both routed
+GEMMs in FP8 (`forward_both_fp8_ms`).
 """
 from __future__ import annotations
 
@@ -397,8 +399,44 @@ def fp8_down(wl, steps, warmup, ev):
     f_ms = sum(a.elapsed_time(b) for a, b in ef) / len(ef)
     flop_fwd = 6.0 * cfg.numel * cfg.H * cfg.F + 6.0 * cfg.T * cfg.H * cfg.shared_F
     del b8
+    # the routed gate_up in FP8 too: the GEMM alone (codes of the hidden states
+    # read through the permutation), then whole forwards with both FP8 GEMMs
+    qg = mx.fp8_block_quant_weights(wl.wgu)
+    qh = mx.tile_quant_fp8(wl.hidden, transposed=False)
+    hg = torch.empty_like(bufs.h)
+    for _ in range(warmup):
+        mx.grouped_gemm_gate_up_fp8(qh["q_row"], qh["s_row"], qg["q"], qg["s"], bufs.tables, cfg.padding_m,
+                                    top_k=cfg.top_k, out=hg)
+    eu = []
+    for _ in range(steps):
+        a = ev()
+        mx.grouped_gemm_gate_up_fp8(qh["q_row"], qh["s_row"], qg["q"], qg["s"], bufs.tables, cfg.padding_m,
+                                    top_k=cfg.top_k, out=hg)
+        eu.append((a, ev()))
+    torch.cuda.synchronize()
+    u_ms = sum(a.elapsed_time(b) for a, b in eu) / len(eu)
+    b88 = mx.MoEBuffers(wl.bufs.shape, wl.hidden.device, wl.fuse, True, fp8_down=True, fp8_gate_up=True)
+
+    def fwd88():
+        mx.routed_moe_forward(wl.hidden, wl.logits, wl.wgu, wl.wd, cfg.top_k, cfg.rsf, cfg.padding_m, cfg.block_m,
+                              wl.swgu, wl.swd, fuse_swiglu=wl.fuse, buffers=b88, expert_bias=wl.bias,
+                              scoring=cfg.scoring, renormalize=cfg.renormalize, w_down_fp8=qw, w_gate_up_fp8=qg)
+    for _ in range(warmup):
+        fwd88()
+    e88 = []
+    for _ in range(steps):
+        a = ev()
+        fwd88()
+        e88.append((a, ev()))
+    torch.cuda.synchronize()
+    f88_ms = sum(a.elapsed_time(b) for a, b in e88) / len(e88)
+    del b88, qg, hg
+    flop_gu = 4.0 * cfg.numel * cfg.H * cfg.F
     return {"gemm_ms": round(g_ms, 4), **pct(g_list), "quant_h_ms": round(q_ms, 4),
             "forward_ms": round(f_ms, 4), "forward_tflops": round(flop_fwd / (f_ms * 1e-3) / 1e12, 2),
+            "gate_up_gemm_ms": round(u_ms, 4), "gate_up_tflops": round(flop_gu / (u_ms * 1e-3) / 1e12, 2),
+            "forward_both_fp8_ms": round(f88_ms, 4),
+            "forward_both_fp8_tflops": round(flop_fwd / (f88_ms * 1e-3) / 1e12, 2),
             "tflops": round(flop / (g_ms * 1e-3) / 1e12, 2),
             "fp8_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
             "bf16_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}

@@ -266,6 +266,32 @@ int grouped_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
                      const int32_t* group_idx_for_bx, int64_t numel, int E, int N, int K, int padding_m,
                      int block_m, uint16_t* y, hipStream_t stream);
 
+/* The block-scaled FP8 grouped GEMM for gate+up: the product of
+ * grouped_gemm_fp8 with w_gate_up's codes, optionally with SwiGLU fused into
+ * its epilogue, and optionally reading the activation codes through the
+ * dispatch permutation (as grouped_gemm_gate_up_gather does for bf16).
+ *   qa, sa       e4m3 activation codes [a_rows, H] and their 1x128-tile
+ *                scales [a_rows, H/128] (tile_quant_fp8's row layout).
+ *                sorted_pair NULL: a_rows == numel, the compact permuted rows;
+ *                otherwise a_rows == T with numel == T*top_k, and compact row
+ *                r is row sorted_pair[r] / top_k (the token's codes, once per
+ *                token instead of once per pair).
+ *   qw, sw       fp8_block_quant_weights(w_gate_up): codes [E, 2F, H] (rows
+ *                0..F-1 gate, F..2F-1 up), scales [E, 2F/128, H/128].
+ *   fuse_swiglu  1: out [numel, F] bf16 = bf16(silu(g) * u) with g and u the
+ *                bf16 roundings of the gate and up products (the bytes of the
+ *                unfused product followed by swiglu()); 0: out [numel, 2F].
+ * Tables as for grouped_gemm_gate_up (NULL tables: one dense group, E = 1,
+ * no sorted_pair). Limits: block_m == 128; H % 128 == 0; F % 128 == 0;
+ * 16-byte aligned qa, qw, out. MOE_ERR_INVALID_ARG for inconsistent sizes or
+ * tables; MOE_ERR_UNSUPPORTED for block_m != 128. */
+int grouped_gemm_gate_up_fp8(const uint8_t* qa, const float* sa, int64_t a_rows, const int32_t* sorted_pair,
+                             int top_k, const uint8_t* qw, const float* sw, const int32_t* group_sizes,
+                             const int32_t* group_offsets, const int32_t* group_padded_offsets,
+                             const int32_t* group_idx_for_bx, int64_t numel, int E, int H, int F,
+                             int padding_m, int block_m, int fuse_swiglu, uint16_t* out,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

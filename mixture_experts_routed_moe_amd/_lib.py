@@ -32,7 +32,7 @@ class MoeError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 SCORING = {"softmax": 0, "sigmoid": 1}
 
 
@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "tile_quant_fp8_m_pad_bound": (I64, [I64, I]),
         "fp8_block_quant_weights": (I, [P, I64, I, P, P, P]),
         "grouped_gemm_fp8": (I, [P, P, P, P, P, P, P, P, I64, I, I, I, I, I, P, P]),
+        "grouped_gemm_gate_up_fp8": (I, [P, P, I64, P, I, P, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -78,7 +79,7 @@ EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_wor
            "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up",
            "grouped_gemm_gate_up_gather", "swiglu",
            "grouped_gemm_down", "moe_unpermute", "swiglu_quant_fp8", "tile_quant_fp8",
-           "tile_quant_fp8_m_pad_bound", "fp8_block_quant_weights", "grouped_gemm_fp8")
+           "tile_quant_fp8_m_pad_bound", "fp8_block_quant_weights", "grouped_gemm_fp8", "grouped_gemm_gate_up_fp8")
 
 
 def lib() -> ctypes.CDLL:
@@ -347,3 +348,31 @@ def grouped_gemm_fp8(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: t
           _ptr(sw, torch.float32, "sw"), *_table_ptrs(tables), numel, E, N, K, padding_m, block_m,
           _ptr(y, torch.bfloat16, "y"), _stream(qa))
     return y
+
+
+def grouped_gemm_gate_up_fp8(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                             tables: Optional[Dict[str, torch.Tensor]], padding_m: int, block_m: int = 128,
+                             fuse_swiglu: bool = True, top_k: Optional[int] = None, out=None) -> torch.Tensor:
+    """Block-scaled FP8 gate_up: qa/sa the e4m3 codes and 1x128 scales of the
+    compact permuted rows, or (top_k given) of the tokens, read through
+    tables["sorted_pair"]; qw/sw = fp8_block_quant_weights(w_gate_up)."""
+    if qw.dim() == 2:
+        qw, sw = qw.unsqueeze(0), sw.unsqueeze(0)
+    E, twoF, H = qw.shape
+    F = twoF // 2
+    a_rows = qa.shape[0]
+    if qa.shape[1] != H:
+        raise ValueError("grouped_gemm_gate_up_fp8: qa width != H")
+    sp = None
+    numel = a_rows
+    if top_k is not None:
+        if tables is None:
+            raise ValueError("grouped_gemm_gate_up_fp8: the gather needs the dispatch tables")
+        sp = tables["sorted_pair"]
+        numel = a_rows * top_k
+    o = _out(out, (numel, F if fuse_swiglu else 2 * F), torch.bfloat16, qa, "out")
+    _call("grouped_gemm_gate_up_fp8", _ptr(qa, torch.uint8, "qa"), _ptr(sa, torch.float32, "sa"), a_rows,
+          _ptr(sp, torch.int32, "sorted_pair"), int(top_k or 1), _ptr(qw, torch.uint8, "qw"),
+          _ptr(sw, torch.float32, "sw"), *_table_ptrs(tables), numel, E, H, F, padding_m, block_m,
+          int(bool(fuse_swiglu)), _ptr(o, torch.bfloat16, "out"), _stream(qa))
+    return o

@@ -26,7 +26,7 @@ int check_launch(const char* what) {
 
 extern "C" const char* moe_last_error(void) { return moe::g_last_error; }
 
-extern "C" int moe_abi_version(void) { return 6; }
+extern "C" int moe_abi_version(void) { return 7; }
 
 extern "C" int64_t moe_num_blocks(int64_t numel, int E, int block_m, int padding_m) {
   if (numel < 0 || E < 0 || block_m <= 0 || padding_m <= 0 || padding_m % block_m != 0) return -1;

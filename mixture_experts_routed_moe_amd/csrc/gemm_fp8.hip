@@ -96,15 +96,22 @@ __global__ __launch_bounds__(256) void block_quant_kernel(const uint16_t* __rest
 }
 
 // One workgroup per (128-row block bx of the padded expert-major row space,
-// 128-column tile nt of y). K advances 128 bytes (one scale block) per step;
+// 128-row weight tile nt). K advances 128 bytes (one scale block) per step;
 // the A rows, the W rows and the 128 A row scales of step kb+1 load
 // (direct-to-LDS) into the other half of a two-stage buffer while step kb
 // computes. A rows past the block's valid rows are read from its last row and
-// never stored.
+// never stored. With a gather table (tb.gather) compact row r of A and of its
+// scales is row gather[r] / gather_k of qa and sa (the token's codes).
+// FUSED (gate_up with SwiGLU): the tile's weight rows are 64 gate rows
+// nt*64.. and the matching 64 up rows up_row + nt*64..; a wave's first
+// 32-row MFMA block is gate, its second the matching up block, so one lane
+// holds both halves of each output and the epilogue stores
+// SwiGLU(bf16(gate), bf16(up)) into the 64 output columns nt*64.. of y.
+template <bool FUSED>
 __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
     const float* __restrict__ sw, moe::Tables tb, int64_t numel, int n_tiles, int N, int K,
-    uint16_t* __restrict__ y) {
+    int up_row, int ldc, uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kF8StageBytes];
   const int bx = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
   int g, rows;
@@ -126,12 +133,21 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
     const int r = wave * 32 + i * 8 + lrow;
     const int rr = min(r, rows - 1);
     const int pos = (lpos ^ f8_swz(r)) * 16;
-    a_src[i] = qa + (m_start + rr) * K + pos;
-    w_src[i] = qw + (static_cast<int64_t>(g) * N + static_cast<int64_t>(nt) * kT + r) * K + pos;
+    a_src[i] = qa + moe::a_row(tb, m_start + rr) * K + pos;
+    // weight row of LDS row r: fused, rows 0-63 gate nt*64 + r, rows 64-127 up
+    const int64_t wr = FUSED ? (r < kT / 2 ? static_cast<int64_t>(nt) * (kT / 2) + r
+                                           : static_cast<int64_t>(up_row) + nt * (kT / 2) + (r - kT / 2))
+                             : static_cast<int64_t>(nt) * kT + r;
+    w_src[i] = qw + (static_cast<int64_t>(g) * N + wr) * K + pos;
   }
   // waves 0 and 1 load the 128 A row scales of a step, 64 rows each
-  const float* sa_src = sa + (m_start + min(wave * 64 + lane, rows - 1)) * nkb;
-  const float* sw_blk = sw + (static_cast<int64_t>(g) * (N / kT) + nt) * nkb;
+  const float* sa_src = sa + moe::a_row(tb, m_start + min(wave * 64 + lane, rows - 1)) * nkb;
+  // the weight scale block of each of the wave's two 32-row MFMA blocks (128-row
+  // blocks: fused, the gate rows nt*64.. sit in block nt/2, the up rows in
+  // block up_row/128 + nt/2; otherwise both in block nt)
+  const float* sw_blk[2];
+  sw_blk[0] = sw + (static_cast<int64_t>(g) * (N / kT) + (FUSED ? nt / 2 : nt)) * nkb;
+  sw_blk[1] = sw + (static_cast<int64_t>(g) * (N / kT) + (FUSED ? up_row / kT + nt / 2 : nt)) * nkb;
 
   auto issue = [&](int kb, int st) __attribute__((always_inline)) {
     uint8_t* base = smem + st * kF8StageBytes;
@@ -155,7 +171,10 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
   // for both operands, which is all the dot products need)
   const int h = lane >> 5;
   const int a_row0 = wm * 64 + (lane & 31);
-  const int w_row0 = wn * 64 + (lane & 31);
+  // LDS row of the wave's MFMA block tn: fused, tn 0 gate rows wn*32.., tn 1
+  // up rows 64 + wn*32..; otherwise rows wn*64 + tn*32..
+  const int w_row0 = (FUSED ? wn * 32 : wn * 64) + (lane & 31);
+  constexpr int kWBlk1 = FUSED ? kT / 2 : 32;
   auto frag = [&](const uint8_t* rows_base, int r, int j) __attribute__((always_inline)) {
     const int c0 = 4 * j + 2 * h;
     const v4i lo = *reinterpret_cast<const v4i*>(rows_base + r * kT + ((c0 ^ f8_swz(r)) << 4));
@@ -170,27 +189,25 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
     if (kb + 1 < nkb) issue(kb + 1, (kb + 1) & 1);
     const uint8_t* st = smem + (kb & 1) * kF8StageBytes;
     const float* s_rows = reinterpret_cast<const float*>(st + 2 * kT * kT);
-    const float w_scale = sw_blk[kb];
+    const float w_scale[2] = {sw_blk[0][kb], sw_blk[1][kb]};
     v8i af[2][2], wf[2][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm) af[tm][j] = frag(st, a_row0 + tm * 32, j);
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) wf[tn][j] = frag(st + kT * kT, w_row0 + tn * 32, j);
+      for (int tn = 0; tn < 2; ++tn) wf[tn][j] = frag(st + kT * kT, w_row0 + tn * kWBlk1, j);
     }
-    float sc[2];
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm) sc[tm] = s_rows[a_row0 + tm * 32] * w_scale;
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn) {
+        const float sc = s_rows[a_row0 + tm * 32] * w_scale[tn];
         floatx16 p = {};
         p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[tn][0], af[tm][0], p, 0, 0, 0, 127, 0, 127);
         p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[tn][1], af[tm][1], p, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tm][tn][r] += p[r] * sc[tm];
+        for (int r = 0; r < 16; ++r) acc[tm][tn][r] += p[r] * sc;
       }
   }
 
@@ -201,16 +218,29 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
   for (int tm = 0; tm < 2; ++tm) {
     const int lr = a_row0 + tm * 32;
     if (lr >= rows) continue;
-    uint16_t* yrow = y + (m_start + lr) * N + static_cast<int64_t>(nt) * kT + wn * 64;
-#pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+    if constexpr (FUSED) {
+      uint16_t* yrow = y + (m_start + lr) * ldc + static_cast<int64_t>(nt) * (kT / 2) + wn * 32;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int n = tn * 32 + 8 * q4 + 4 * h;
-        const uint32_t lo = moe::pack_bf16x2(acc[tm][tn][4 * q4], acc[tm][tn][4 * q4 + 1]);
-        const uint32_t hi = moe::pack_bf16x2(acc[tm][tn][4 * q4 + 2], acc[tm][tn][4 * q4 + 3]);
-        *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
+        uint16_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = moe::swiglu_bf16(moe::f32_to_bf16(acc[tm][0][4 * q4 + e]), moe::f32_to_bf16(acc[tm][1][4 * q4 + e]));
+        *reinterpret_cast<uint2*>(yrow + 8 * q4 + 4 * h) =
+            make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
       }
+    } else {
+      uint16_t* yrow = y + (m_start + lr) * ldc + static_cast<int64_t>(nt) * kT + wn * 64;
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int n = tn * 32 + 8 * q4 + 4 * h;
+          const uint32_t lo = moe::pack_bf16x2(acc[tm][tn][4 * q4], acc[tm][tn][4 * q4 + 1]);
+          const uint32_t hi = moe::pack_bf16x2(acc[tm][tn][4 * q4 + 2], acc[tm][tn][4 * q4 + 3]);
+          *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
+        }
+    }
   }
 }
 
@@ -258,7 +288,52 @@ extern "C" int grouped_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_
   const int64_t blocks = m_blocks * n_tiles;
   if (blocks > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
   const Tables tb{group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx};
-  grouped_gemm_fp8_kernel<<<static_cast<unsigned>(blocks), kF8Threads, 0, stream>>>(qa, sa, qw, sw, tb, numel,
-                                                                                   n_tiles, N, K, y);
+  grouped_gemm_fp8_kernel<false><<<static_cast<unsigned>(blocks), kF8Threads, 0, stream>>>(qa, sa, qw, sw, tb, numel,
+                                                                                          n_tiles, N, K, 0, N, y);
+  return check_launch(name);
+}
+
+extern "C" int grouped_gemm_gate_up_fp8(const uint8_t* qa, const float* sa, int64_t a_rows, const int32_t* sorted_pair,
+                                        int top_k, const uint8_t* qw, const float* sw, const int32_t* group_sizes,
+                                        const int32_t* group_offsets, const int32_t* group_padded_offsets,
+                                        const int32_t* group_idx_for_bx, int64_t numel, int E, int H, int F,
+                                        int padding_m, int block_m, int fuse_swiglu, uint16_t* out,
+                                        hipStream_t stream) {
+  using namespace moe;
+  const char* name = "grouped_gemm_gate_up_fp8";
+  if (numel < 0 || a_rows < 0 || H < kT || H % kT != 0 || F < kT || F % kT != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: numel=%lld a_rows=%lld H=%d F=%d (H, F multiples of 128)", name,
+                (long long)numel, (long long)a_rows, H, F);
+  if (block_m != kT) return fail(MOE_ERR_UNSUPPORTED, "%s: block_m=%d (only 128)", name, block_m);
+  if (fuse_swiglu != 0 && fuse_swiglu != 1) return fail(MOE_ERR_INVALID_ARG, "%s: fuse_swiglu=%d", name, fuse_swiglu);
+  const bool dense = group_sizes == nullptr;
+  if (dense != (group_offsets == nullptr) || dense != (group_padded_offsets == nullptr) ||
+      dense != (group_idx_for_bx == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "%s: tables must be all NULL (dense) or all non-NULL", name);
+  if (dense && (E != 1 || sorted_pair))
+    return fail(MOE_ERR_INVALID_ARG, "%s: dense mode (NULL tables) needs E=1 and no sorted_pair", name);
+  if (!dense && (E < 1 || padding_m <= 0 || padding_m % kT != 0))
+    return fail(MOE_ERR_INVALID_ARG, "%s: E=%d padding_m=%d (a positive multiple of 128)", name, E, padding_m);
+  if (sorted_pair ? (top_k < 1 || numel != a_rows * top_k) : a_rows != numel)
+    return fail(MOE_ERR_INVALID_ARG, "%s: a_rows=%lld must be numel (compact rows) or numel/top_k (gather)", name,
+                (long long)a_rows);
+  if (numel >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: numel >= 2^31", name);
+  if (numel == 0) return MOE_OK;
+  if (!qa || !sa || !qw || !sw || !out) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (!aligned16(qa) || !aligned16(qw) || !aligned16(out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: qa/qw/out not 16-byte aligned", name);
+  const int64_t m_blocks = dense ? ceil_div(numel, kT) : moe_num_blocks(numel, E, kT, padding_m);
+  const int n_tiles = fuse_swiglu ? F / (kT / 2) : (2 * F) / kT;
+  const int64_t blocks = m_blocks * n_tiles;
+  if (blocks > 0x7FFFFFFF) return fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
+  Tables tb{group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx};
+  tb.gather = sorted_pair;
+  tb.gather_k = sorted_pair ? top_k : 1;
+  if (fuse_swiglu)
+    grouped_gemm_fp8_kernel<true><<<static_cast<unsigned>(blocks), kF8Threads, 0, stream>>>(
+        qa, sa, qw, sw, tb, numel, n_tiles, 2 * F, H, F, F, out);
+  else
+    grouped_gemm_fp8_kernel<false><<<static_cast<unsigned>(blocks), kF8Threads, 0, stream>>>(
+        qa, sa, qw, sw, tb, numel, n_tiles, 2 * F, H, 0, 2 * F, out);
   return check_launch(name);
 }

@@ -49,12 +49,13 @@ class MoEBuffers:
     """Device buffers for every intermediate of one forward of `shape`."""
 
     def __init__(self, shape: MoEShape, device, fuse_swiglu: bool = True, fuse_permute: bool = True,
-                 fp8_down: bool = False):
+                 fp8_down: bool = False, fp8_gate_up: bool = False):
         s = shape
         self.shape = s
         self.fuse_swiglu = fuse_swiglu
         self.fuse_permute = fuse_permute
         self.fp8_down = fp8_down
+        self.fp8_gate_up = fp8_gate_up
         bf16 = dict(dtype=torch.bfloat16, device=device)
         self.topk_ids = torch.empty(s.T, s.top_k, dtype=torch.int32, device=device)
         self.topk_weights = torch.empty(s.T, s.top_k, dtype=torch.float32, device=device)
@@ -68,6 +69,10 @@ class MoEBuffers:
         self.qa = None if not fp8_down else {
             "q_row": torch.empty(s.numel, s.F, dtype=torch.uint8, device=device),
             "s_row": torch.empty(s.numel, s.F // 128, dtype=torch.float32, device=device)}
+        # e4m3 codes of the hidden states (one row per token), for the FP8 gate_up
+        self.qh = None if not fp8_gate_up else {
+            "q_row": torch.empty(s.T, s.H, dtype=torch.uint8, device=device),
+            "s_row": torch.empty(s.T, s.H // 128, dtype=torch.float32, device=device)}
         self.out = torch.empty(s.T, s.H, **bf16)
         if s.shared_F:
             self.shared_gate_up = None if fuse_swiglu else torch.empty(s.T, 2 * s.shared_F, **bf16)
@@ -84,7 +89,8 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
                        expert_bias: Optional[torch.Tensor] = None, scoring: str = "softmax",
                        renormalize: bool = True, return_parts: bool = False,
                        shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True,
-                       w_down_fp8: Optional[Dict[str, torch.Tensor]] = None):
+                       w_down_fp8: Optional[Dict[str, torch.Tensor]] = None,
+                       w_gate_up_fp8: Optional[Dict[str, torch.Tensor]] = None):
     """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden)).
 
     With return_parts=True returns (shared_out, routed_out) instead, the split
@@ -99,6 +105,12 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     128x128 block); h is quantized to 1x128-tile e4m3 codes (row layout) and
     grouped_gemm_fp8 replaces the bf16 down GEMM (block_m 128; buffers made
     with fp8_down=True). The shared expert stays bf16.
+
+    w_gate_up_fp8: the routed gate_up in FP8: {"q", "s"} from
+    fp8_block_quant_weights(w_gate_up); the hidden states are quantized once
+    per token to 1x128-tile e4m3 codes and grouped_gemm_gate_up_fp8 reads each
+    pair's row through the dispatch permutation (needs fuse_permute; buffers
+    made with fp8_gate_up=True).
 
     fuse_permute: the gate_up GEMM reads each permuted row straight from
     `hidden` (row sorted_pair[r] // top_k) instead of a permuted copy written
@@ -118,9 +130,11 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     shape = MoEShape(T, H, F, E, top_k, padding_m, block_m, shared_F)
     b = buffers
     if b is None:
-        b = MoEBuffers(shape, hidden.device, fuse_swiglu, fuse_permute, w_down_fp8 is not None)
+        b = MoEBuffers(shape, hidden.device, fuse_swiglu, fuse_permute, w_down_fp8 is not None,
+                       w_gate_up_fp8 is not None)
     elif (dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu
-          or b.fuse_permute != fuse_permute or (w_down_fp8 is not None and b.qa is None)):
+          or b.fuse_permute != fuse_permute or (w_down_fp8 is not None and b.qa is None)
+          or (w_gate_up_fp8 is not None and b.qh is None)):
         raise ValueError("routed_moe_forward: buffers were made for another shape")
 
     def shared_expert():
@@ -140,7 +154,14 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     _lib.moe_topk_softmax(router_logits, top_k, b.topk_ids, b.topk_weights, expert_bias, scoring, renormalize)
     tb = _lib.moe_align(b.topk_ids, E, padding_m, block_m, b.tables)
     gu_out = b.h if fuse_swiglu else b.gate_up
-    if fuse_permute:
+    if w_gate_up_fp8 is not None:
+        if not fuse_permute:
+            raise ValueError("routed_moe_forward: the FP8 gate_up reads its rows through the permutation "
+                             "(fuse_permute=True)")
+        _lib.tile_quant_fp8(hidden, out=b.qh, transposed=False)
+        _lib.grouped_gemm_gate_up_fp8(b.qh["q_row"], b.qh["s_row"], w_gate_up_fp8["q"], w_gate_up_fp8["s"], tb,
+                                      padding_m, block_m, fuse_swiglu, top_k=top_k, out=gu_out)
+    elif fuse_permute:
         _lib.grouped_gemm_gate_up_gather(hidden, w_gate_up, tb, top_k, padding_m, block_m, fuse_swiglu, gu_out)
     else:
         _lib.moe_permute(hidden, tb["sorted_pair"], top_k, b.x_perm, tb["pair_to_row"])
@@ -188,20 +209,22 @@ class MoEForwardGraph:
                  buffers: Optional[MoEBuffers] = None, expert_bias: Optional[torch.Tensor] = None,
                  scoring: str = "softmax", renormalize: bool = True,
                  shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True,
-                 w_down_fp8: Optional[Dict[str, torch.Tensor]] = None):
+                 w_down_fp8: Optional[Dict[str, torch.Tensor]] = None,
+                 w_gate_up_fp8: Optional[Dict[str, torch.Tensor]] = None):
         T, H = hidden.shape
         E, twoF, _ = w_gate_up.shape
         shared_F = 0 if shared_w_down is None else shared_w_down.shape[1]
         if buffers is None:
             buffers = MoEBuffers(MoEShape(T, H, twoF // 2, E, top_k, padding_m, block_m, shared_F), hidden.device,
-                                 fuse_swiglu, fuse_permute, w_down_fp8 is not None)
+                                 fuse_swiglu, fuse_permute, w_down_fp8 is not None, w_gate_up_fp8 is not None)
         self.hidden, self.logits, self.buffers = hidden, router_logits, buffers
 
         def run():
             return routed_moe_forward(hidden, router_logits, w_gate_up, w_down, top_k, routed_scaling_factor,
                                       padding_m, block_m, shared_w_gate_up, shared_w_down, fuse_swiglu, buffers,
                                       expert_bias, scoring, renormalize, shared_stream=shared_stream,
-                                      fuse_permute=fuse_permute, w_down_fp8=w_down_fp8)
+                                      fuse_permute=fuse_permute, w_down_fp8=w_down_fp8,
+                                      w_gate_up_fp8=w_gate_up_fp8)
 
         # one eager forward first: loads the library and checks every argument
         run()

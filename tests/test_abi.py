@@ -61,7 +61,7 @@ def test_num_blocks_matches_worked_example(lib):
     assert lib.moe_num_blocks(100, 3, 64, 128) == 2 + 6
     assert lib.moe_num_blocks(10, 3, 64, 96) == -1
     assert lib.moe_num_blocks(0, 8, 64, 64) == 8
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 def test_workspace_size(lib):
@@ -130,6 +130,17 @@ def test_argument_errors_return_before_launch(lib):
     assert lib.grouped_gemm_fp8(*[None] * 8, 64, 1, 256, 128, 128, 64, None, None) == -2    # block_m != 128
     assert lib.grouped_gemm_fp8(*[None] * 8, 64, 2, 256, 128, 128, 128, None, None) == -1   # dense needs E=1
     assert lib.grouped_gemm_fp8(*[None] * 8, 0, 1, 256, 128, 128, 128, None, None) == 0
+    # FP8 gate_up: a_rows must be numel (compact) or numel / top_k (gather); block_m 128 only
+    lib.grouped_gemm_gate_up_fp8.argtypes = ([P, P, c.c_int64, P, c.c_int, P, P] + [P] * 4 + [c.c_int64] +
+                                             [c.c_int] * 6 + [P, P])
+    assert lib.grouped_gemm_gate_up_fp8(None, None, 8, None, 1, None, None, 1, 1, 1, 1, 16, 2, 256, 256, 128, 128, 1,
+                                        None, None) == -1        # a_rows != numel without sorted_pair
+    assert lib.grouped_gemm_gate_up_fp8(None, None, 8, 16, 2, None, None, 1, 1, 1, 1, 16, 2, 256, 256, 128, 64, 1,
+                                        None, None) == -2        # block_m 64
+    assert lib.grouped_gemm_gate_up_fp8(None, None, 8, 16, 2, None, None, None, None, None, None, 16, 1, 256, 256,
+                                        128, 128, 1, None, None) == -1   # gather without tables
+    assert lib.grouped_gemm_gate_up_fp8(None, None, 0, 16, 2, None, None, 1, 1, 1, 1, 0, 2, 256, 256, 128, 128, 1,
+                                        None, None) == 0         # nothing to do
     # routing limits
     lib.moe_topk_softmax.argtypes = [P, P, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int, P, P, P]
     assert lib.moe_topk_softmax(None, None, 4, 2048, 8, 0, 1, None, None, None) == -2
