@@ -703,7 +703,8 @@ def test_grouped_gemm_gate_up_fp8(F, H, extra_empty):
     assert torch.equal(h, mx.swiglu(gu))
     assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
     # gather: T tokens with two slots each; the compact rows are the tokens' codes in sorted_pair order
-    T, k = 700, 2
+    # (enough rows per expert for the 256 x 256 kernel)
+    T, k = 2000, 2
     rng = np.random.default_rng(F + H)
     ids = np.stack([rng.permutation(len(sizes))[:k] for _ in range(T)]).astype(np.int32)
     tb2 = mx.moe_align(_t(ids, d), len(sizes), 128, 128)
@@ -759,6 +760,39 @@ def test_grouped_gemm_fp8_dsv3_down_sampled_rows():
         ref = oracle.grouped_gemm_fp8(ra["q_row"], ra["s_row"], rw["q"][None], rw["s"][None],
                                       np.array([len(rows)]), np.array([0]))
         assert_bf16_close(bits(y[sel]), ref, f"fp8 down expert {e}")
+
+
+def test_grouped_gemm_gate_up_fp8_dsv3_sampled_rows():
+    """The DeepSeek-V3-shaped routed gate_up in FP8 at full size (T = 4096,
+    top-8, H = 7168, F = 2048, 256 experts, Zipf-biased routing), reading each
+    pair's token codes through sorted_pair, SwiGLU fused: rows of sampled
+    experts against the oracle's FP8 product and SwiGLU on its own codes."""
+    d = dev()
+    cfg = moe_synth.CONFIGS["dsv3_prefill"]
+    say("fp8 gate_up", cfg.name)
+    ids, _ = mx.moe_topk_softmax(moe_synth.router_logits(cfg, d), cfg.top_k, expert_bias=moe_synth.expert_bias(cfg, d))
+    tb = mx.moe_align(ids, cfg.E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    sp = host(tb["sorted_pair"])
+    hid = moe_synth.hidden(cfg, d)
+    wgu = moe_synth.w_gate_up(cfg, d)
+    qh, qg = mx.tile_quant_fp8(hid, transposed=False), mx.fp8_block_quant_weights(wgu)
+    h = mx.grouped_gemm_gate_up_fp8(qh["q_row"], qh["s_row"], qg["q"], qg["s"], tb, 128, top_k=cfg.top_k)
+    active = np.nonzero(gs)[0]
+    rng = np.random.default_rng(4)
+    for e in sorted({int(active[0]), int(active[-1]), int(np.argmax(gs)), *rng.choice(active, 2).tolist()}):
+        o, n = int(go[e]), int(gs[e])
+        rows = sorted({0, n - 1, *rng.choice(n, min(n, 6), replace=False).tolist()})
+        tok = torch.as_tensor(sp[o + np.asarray(rows)] // cfg.top_k, device=d)
+        ra = oracle.quant_fp8(bits(hid[tok]))
+        rw = oracle.block_quant_fp8(bits(wgu[e]))
+        ref = oracle.grouped_gemm_fp8(ra["q_row"], ra["s_row"], rw["q"][None], rw["s"][None],
+                                      np.array([len(rows)]), np.array([0]))
+        sel = torch.as_tensor(o + np.asarray(rows), device=d)
+        got = bits(h[sel])
+        exp = oracle.swiglu(ref, cfg.F)
+        # SwiGLU of the bf16 products: compare against the oracle's SwiGLU of its own product
+        assert_bf16_close(got, exp, f"fp8 gate_up expert {e}")
 
 
 # ------------------------------------------- grouped tile quantizer --
