@@ -1045,6 +1045,152 @@ int launch_gemv(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
   return moe::check_launch(name);
 }
 
+// ---------------------------------------------------------------------------
+// Skinny dense kernel: one group of 5..32 rows (a shared expert at a decode
+// batch). The row-tile kernels give such a launch one workgroup per 256
+// output columns (28 for a 7168-wide down projection), and the few-row kernel
+// re-reads the weights once per 4 rows. Here one 512-thread workgroup takes
+// 32 output columns (fused: 32 gate and the matching 32 up weight rows) and
+// its eight waves split K (wave w takes the 64-wide steps w, w + 8, ...), so a
+// 7168 x 18432 down projection runs 224 workgroups. Operands go from global
+// memory straight to the MFMA registers: lane l reads 64 contiguous bytes
+// (32 k values) of activation row l & 31 and of weight row l & 31 at k
+// offset 32 (l >> 5) of each step, and MFMA i of the step takes the lane's
+// i-th 16 bytes of both, so every k of the step is summed once. Each wave
+// keeps kSkinnyDepth steps of loads in flight; the eight partial sums meet in
+// LDS and are added in wave order (the result does not depend on timing).
+constexpr int kSkinnyCols = 32;
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyDepth = 3;
+#ifndef MOE_SKINNY_MAX_ROWS
+#define MOE_SKINNY_MAX_ROWS 32
+#endif
+
+template <bool FUSED>
+__global__ __launch_bounds__(64 * kSkinnyWaves, 2) void dense_skinny_kernel(const uint16_t* __restrict__ A,
+                                                                            const uint16_t* __restrict__ W, int rows,
+                                                                            int K, int up_row, int ldc,
+                                                                            uint16_t* __restrict__ C) {
+  constexpr int NB = FUSED ? 2 : 1;   // 32-column weight blocks per wave (gate, up)
+  constexpr int D = kSkinnyDepth;
+  __shared__ float red[kSkinnyWaves][NB][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int l32 = lane & 31, h = lane >> 5;
+  const int nt = blockIdx.x;
+  const uint16_t* w0 = W + (static_cast<int64_t>(nt) * kSkinnyCols + l32) * K + h * 32;
+  const uint16_t* w1 = W + (static_cast<int64_t>(FUSED ? up_row : 0) + static_cast<int64_t>(nt) * kSkinnyCols + l32) * K +
+                       h * 32;
+  // activation row l32; rows past the last read the last row (never stored)
+  const uint16_t* ap = A + static_cast<int64_t>(min(l32, rows - 1)) * K + h * 32;
+
+  floatx16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[b][e] = 0.0f;
+  const int nk = K / 64;
+  const int n_my = wave < nk ? (nk - wave + kSkinnyWaves - 1) / kSkinnyWaves : 0;
+  if (n_my > 0) {
+    uint4 bw[D][NB][4], ba[D][4];
+    // loads of this wave's step s into slot d (steps past the last reload it
+    // and add zero); site: a distinct empty asm statement after each call
+    // site's loads keeps the optimizer from merging the prologue's loads
+    // with the loop's into one block
+    auto issue = [&](auto dd, int s, auto site) __attribute__((always_inline)) {
+      constexpr int d = decltype(dd)::value;
+      const int ko = (min(s, n_my - 1) * kSkinnyWaves + wave) * 64;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bw[d][0][j] = *reinterpret_cast<const uint4*>(w0 + ko + j * 8);
+        if (FUSED) bw[d][NB - 1][j] = *reinterpret_cast<const uint4*>(w1 + ko + j * 8);
+        ba[d][j] = *reinterpret_cast<const uint4*>(ap + ko + j * 8);
+      }
+      asm volatile("; skinny loads %0" ::"n"(decltype(site)::value * 8 + d));
+    };
+    auto mfmas = [&](auto dd, bool live) __attribute__((always_inline)) {
+      constexpr int d = decltype(dd)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, live ? ba[d][i] : make_uint4(0u, 0u, 0u, 0u));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw[d][b][i]), acc[b], 0, 0, 0);
+      }
+    };
+    static_assert(D >= 1 && D <= 4, "depth 1..4");
+    issue(Ic<0>{}, 0, Ic<0>{});
+    if constexpr (D > 1) issue(Ic<1>{}, 1, Ic<0>{});
+    if constexpr (D > 2) issue(Ic<2>{}, 2, Ic<0>{});
+    if constexpr (D > 3) issue(Ic<3>{}, 3, Ic<0>{});
+    const int n_pad = (n_my + D - 1) / D * D;
+    int s0 = 0;
+    // whole blocks of D steps, each slot refilled D steps ahead after its
+    // MFMAs; the last block refills nothing
+    for (; s0 + D < n_pad; s0 += D) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(Ic<0>{}, true);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(Ic<0>{}, s0 + D, Ic<1>{});
+      if constexpr (D > 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(Ic<1>{}, true);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(Ic<1>{}, s0 + D + 1, Ic<1>{});
+      }
+      if constexpr (D > 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(Ic<2>{}, true);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(Ic<2>{}, s0 + D + 2, Ic<1>{});
+      }
+      if constexpr (D > 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(Ic<3>{}, true);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(Ic<3>{}, s0 + D + 3, Ic<1>{});
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(Ic<0>{}, s0 < n_my);
+    if constexpr (D > 1) mfmas(Ic<1>{}, s0 + 1 < n_my);
+    if constexpr (D > 2) mfmas(Ic<2>{}, s0 + 2 < n_my);
+    if constexpr (D > 3) mfmas(Ic<3>{}, s0 + 3 < n_my);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[wave][b][e][lane] = acc[b][e];
+  __syncthreads();
+  if (wave != 0) return;
+  // result register e of lane l: activation row (e & 3) + 4h + 8(e >> 2), column l & 31
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = (e & 3) + 4 * h + 8 * (e >> 2);
+    float v[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      v[b] = red[0][b][e][lane];
+#pragma unroll
+      for (int w = 1; w < kSkinnyWaves; ++w) v[b] += red[w][b][e][lane];
+    }
+    if (row >= rows) continue;
+    uint16_t* crow = C + static_cast<int64_t>(row) * ldc + static_cast<int64_t>(nt) * kSkinnyCols + l32;
+    if (FUSED)
+      *crow = moe::swiglu_bf16(moe::f32_to_bf16(v[0]), moe::f32_to_bf16(v[NB - 1]));
+    else
+      *crow = moe::f32_to_bf16(v[0]);
+  }
+}
+
+template <bool FUSED>
+int launch_skinny(const uint16_t* A, const uint16_t* W, int64_t numel, int K, int up_row, int ldc, uint16_t* C,
+                  hipStream_t stream, const char* name) {
+  dense_skinny_kernel<FUSED><<<static_cast<unsigned>(ldc / kSkinnyCols), 64 * kSkinnyWaves, 0, stream>>>(
+      A, W, static_cast<int>(numel), K, up_row, ldc, C);
+  return moe::check_launch(name);
+}
+
 #ifndef MOE_GEMV_MAX_ROWS
 #define MOE_GEMV_MAX_ROWS 4
 #endif
@@ -1072,6 +1218,10 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   const bool few_rows = tb.gs ? numel * 100 <= MOE_GEMV_GROUPED_PCT * static_cast<int64_t>(E) : numel <= MOE_GEMV_MAX_ROWS;
   if (few_rows && K % 64 == 0 && ldc % kGemvCols == 0)
     return launch_gemv<FUSED>(A, W, tb, E, numel, K, w_stride, up_row, ldc, C, stream, name);
+  // one dense group of up to 32 rows: the K-split skinny kernel
+  if (tb.gs == nullptr && tb.gather == nullptr && numel <= MOE_SKINNY_MAX_ROWS && K % 64 == 0 &&
+      ldc % kSkinnyCols == 0)
+    return launch_skinny<FUSED>(A, W, numel, K, up_row, ldc, C, stream, name);
   // the wide kernel addresses a tile's A and W rows with 32-bit byte offsets
   // (with a gather table, A's offsets count from its first row: a_off32)
   const bool wide_fits = (static_cast<int64_t>(up_row) + kWideW) * K * 2 < (int64_t(1) << 32) && a_off32;

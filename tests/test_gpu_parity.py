@@ -313,6 +313,27 @@ def test_few_row_dense_gemm(numel):
         assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd)[None], one, zero), f"down K={K}")
 
 
+@pytest.mark.parametrize("numel", [5, 17, 32])
+def test_skinny_dense_gemm(numel):
+    """One dense group of 5..32 rows (a shared expert at a decode batch): the
+    K-split skinny kernel with K of one step (seven of eight waves idle), of
+    uneven splits (3 and 34 steps over 8 waves) and of 112 steps; gate_up
+    (K = H) fused and unfused and down (K = F) against the oracle."""
+    d = dev()
+    for H, F, Hd in ((64, 64, 256), (2176, 192, 2176), (7168, 2176, 7168)):
+        key = moe_synth.tensor_key(89, numel, H)
+        x = moe_synth.normal_bf16(key, (numel, H), 1.0, d)
+        wgu = moe_synth.normal_bf16(key + 1, (2 * F, H), H ** -0.5, d)
+        wd = moe_synth.normal_bf16(key + 2, (Hd, F), F ** -0.5, d)
+        one, zero = np.array([numel], np.int32), np.array([0], np.int32)
+        gu = mx.grouped_gemm_gate_up(x, wgu, None, 128, 128, fuse_swiglu=False)
+        assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(wgu)[None], one, zero), f"gate_up H={H}")
+        h = mx.grouped_gemm_gate_up(x, wgu, None, 128, 128, fuse_swiglu=True)
+        assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
+        y = mx.grouped_gemm_down(h, wd, None, 128, 128)
+        assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd)[None], one, zero), f"down F={F}")
+
+
 @pytest.mark.parametrize("layout", ["spread", "last"])
 def test_few_row_grouped_gemm(layout):
     """A grouped launch with numel <= E / 10 rows (one decode token's top-k
