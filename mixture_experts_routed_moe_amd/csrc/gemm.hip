@@ -1061,13 +1061,19 @@ int launch_gemv(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
 // LDS and are added in wave order (the result does not depend on timing).
 constexpr int kSkinnyCols = 32;
 constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyDepth = 3;
+#ifndef MOE_SKINNY_DEPTH
+#define MOE_SKINNY_DEPTH 2
+#endif
+#ifndef MOE_SKINNY_OCC
+#define MOE_SKINNY_OCC 2
+#endif
+constexpr int kSkinnyDepth = MOE_SKINNY_DEPTH;
 #ifndef MOE_SKINNY_MAX_ROWS
 #define MOE_SKINNY_MAX_ROWS 32
 #endif
 
 template <bool FUSED>
-__global__ __launch_bounds__(64 * kSkinnyWaves, 2) void dense_skinny_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(64 * kSkinnyWaves, MOE_SKINNY_OCC) void dense_skinny_kernel(const uint16_t* __restrict__ A,
                                                                             const uint16_t* __restrict__ W, int rows,
                                                                             int K, int up_row, int ldc,
                                                                             uint16_t* __restrict__ C) {
