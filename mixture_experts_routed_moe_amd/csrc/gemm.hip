@@ -1231,7 +1231,12 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   // the wide kernel addresses a tile's A and W rows with 32-bit byte offsets
   // (with a gather table, A's offsets count from its first row: a_off32)
   const bool wide_fits = (static_cast<int64_t>(up_row) + kWideW) * K * 2 < (int64_t(1) << 32) && a_off32;
-  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits &&
+#ifndef MOE_WIDE_DENSE_MIN_TILES
+#define MOE_WIDE_DENSE_MIN_TILES 128
+#endif
+  // a dense launch with few 256-row tiles: the 128-row kernel gives it twice the workgroups
+  const bool dense_few = tb.gs == nullptr && moe::ceil_div(numel, kWideRows) * (ldc / pipe_cols) < MOE_WIDE_DENSE_MIN_TILES;
+  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits && !dense_few &&
       numel >= static_cast<int64_t>(MOE_WIDE_MIN_ROWS) * E)
     return launch_wide<FUSED>(A, W, tb, E, numel, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
   if (block_m == kPipeBM && ldc % pipe_cols == 0)
