@@ -1219,8 +1219,9 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
 #ifndef MOE_WIDE_MIN_ROWS
 #define MOE_WIDE_MIN_ROWS 128
 #endif
-  // few rows (at most 4 in one dense group, or at most 2 per expert on
-  // average): the weight-streaming kernel
+  // few rows (at most 4 in one dense group, or numel <= E / 10 over the
+  // experts: one decode token's top-k): the weight-streaming kernel (at 256
+  // rows over 384 experts the row-tile kernels are faster)
   const bool few_rows = tb.gs ? numel * 100 <= MOE_GEMV_GROUPED_PCT * static_cast<int64_t>(E) : numel <= MOE_GEMV_MAX_ROWS;
   if (few_rows && K % 64 == 0 && ldc % kGemvCols == 0)
     return launch_gemv<FUSED>(A, W, tb, E, numel, K, w_stride, up_row, ldc, C, stream, name);
