@@ -125,8 +125,8 @@ int moe_permute(const uint16_t* hidden, const int32_t* sorted_pair, const int32_
 /* Grouped GEMM for gate+up, C[e] = A[e] @ W[e]^T (TileOPs #1580, "Benchmark
  * results" and "Grouped-GEMM kernel"): A is the compact [numel, H] layout;
  * each expert's last, partial row block is masked inside the kernel (rows
- * past the expert read as zero, stores limited to the valid rows) instead of
- * padding A. Row blocks are decoded from the tables as in Tutorial Example 07:
+ * past the expert are read from its last row and their outputs are never
+ * stored) instead of padding A. Row blocks are decoded from the tables as in Tutorial Example 07:
  *     m_start = bx*block_m - group_padded_offsets[g] + group_offsets[g].
  * w_gate_up [E, 2F, H] bf16: rows 0..F-1 gate, rows F..2F-1 up.
  * fuse_swiglu = 0: out [numel, 2F] bf16 = bf16(A @ W^T).
@@ -145,8 +145,10 @@ int grouped_gemm_gate_up(const uint16_t* x_perm, const uint16_t* w_gate_up,
                          int fuse_swiglu, uint16_t* out, hipStream_t stream);
 
 /* grouped_gemm_gate_up with the token permute folded into its A loads: the
- * result is byte-identical to moe_permute followed by grouped_gemm_gate_up
- * on x_perm, with compact row r of A read from
+ * product of moe_permute followed by grouped_gemm_gate_up on x_perm (the
+ * same bytes while T*H*2 < 2^32; past that this call takes the 128-row
+ * kernel, whose fp32 sums may round differently), with compact row r of A
+ * read from
  *     hidden[sorted_pair[r] / top_k, :]
  * (the permute's definition, TileOPs "MoePermuteAlignOp"; the grouped GEMM
  * of TileOPs #1580 "Grouped-GEMM kernel" on the permuted rows), so x_perm is
