@@ -986,26 +986,31 @@ SHARED_SMALL = moe_synth.MoEConfig(85, "shared_small", T=64, H=256, F=128, E=16,
                                    block_m=128, shared_F=384, scoring="sigmoid")
 
 
-@pytest.mark.parametrize("name,side", [("qwen3_decode", False), ("shared_small", False), ("shared_small", True)])
-def test_forward_graph_replay(name, side):
+@pytest.mark.parametrize("name,side,fp8", [("qwen3_decode", False, False), ("shared_small", False, False),
+                                           ("shared_small", True, False), ("shared_small", True, True)])
+def test_forward_graph_replay(name, side, fp8):
     """The forward captured as a HIP graph (with the shared expert forked onto
-    a second stream for side=True): every replay, with eager work of the
-    program between replays, gives the eager forward's bytes; new inputs
-    written into the static tensors give the eager forward of those inputs,
-    which matches the oracle."""
+    a second stream for side=True, both routed GEMMs in FP8 for fp8=True):
+    every replay, with eager work of the program between replays, gives the
+    eager forward's bytes; new inputs written into the static tensors give
+    the eager forward of those inputs (for bf16, matching the oracle)."""
     d = dev()
     cfg = SHARED_SMALL if name == "shared_small" else moe_synth.CONFIGS[name]
-    say("graph", name, side)
+    say("graph", name, side, fp8)
     inp = inputs(cfg, d)
-    ref = _gpu_forward(cfg, inp).clone()
+    kw = {}
+    if fp8:
+        kw = dict(w_down_fp8=mx.fp8_block_quant_weights(inp["w_down"]),
+                  w_gate_up_fp8=mx.fp8_block_quant_weights(inp["w_gate_up"]))
+    ref = _gpu_forward(cfg, inp, **kw).clone()
     stream = torch.cuda.Stream(d) if side else None
     g = mx.MoEForwardGraph(inp["hidden"].clone(), inp["logits"].clone(), inp["w_gate_up"], inp["w_down"], cfg.top_k,
                            cfg.rsf, cfg.padding_m, cfg.block_m, inp.get("shared_w_gate_up"), inp.get("shared_w_down"),
                            expert_bias=inp.get("bias"), scoring=cfg.scoring, renormalize=cfg.renormalize,
-                           shared_stream=stream)
+                           shared_stream=stream, **kw)
     for rep in range(3):
         g.out.zero_()
-        other = _gpu_forward(cfg, inp)          # eager work between replays
+        other = _gpu_forward(cfg, inp, **kw)    # eager work between replays
         out = g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {rep}"
@@ -1018,9 +1023,9 @@ def test_forward_graph_replay(name, side):
     g.logits.copy_(lg2)
     out = g.replay().clone()
     inp2 = dict(inp, hidden=hid2, logits=lg2)
-    ref2 = _gpu_forward(cfg, inp2)
+    ref2 = _gpu_forward(cfg, inp2, **kw)
     assert torch.equal(out, ref2)
-    if name == "shared_small":
+    if name == "shared_small" and not fp8:
         exp = oracle_tokens(cfg, inp2, np.arange(cfg.T))
         assert_bf16_close(bits(out), exp["out"], "graph replay, new inputs")
 
