@@ -32,7 +32,8 @@ shapes; `fp8_down` the primary workload's down projection on the FP8 path
 (1x128-tile e4m3 activations, 128x128-block e4m3 weights) beside the bf16 one,
 and the whole forward with that FP8 down projection (`forward_ms`); then the
 routed gate_up in FP8 (`gate_up_gemm_ms`) and the forward with both routed
-GEMMs in FP8 (`forward_both_fp8_ms`).
+GEMMs in FP8 (`forward_both_fp8_ms`), and with the shared expert's GEMMs in
+FP8 as well (`forward_all_fp8_ms`).
 """
 from __future__ import annotations
 
@@ -430,13 +431,38 @@ def fp8_down(wl, steps, warmup, ev):
         e88.append((a, ev()))
     torch.cuda.synchronize()
     f88_ms = sum(a.elapsed_time(b) for a, b in e88) / len(e88)
-    del b88, qg, hg
+    del b88, hg
+    # and the shared expert's GEMMs in FP8 as well
+    f4_ms = None
+    if cfg.shared_F:
+        qs = {"gate_up": mx.fp8_block_quant_weights(wl.swgu), "down": mx.fp8_block_quant_weights(wl.swd)}
+        b4 = mx.MoEBuffers(wl.bufs.shape, wl.hidden.device, wl.fuse, True, fp8_down=True, fp8_gate_up=True,
+                           fp8_shared=True)
+
+        def fwd4():
+            mx.routed_moe_forward(wl.hidden, wl.logits, wl.wgu, wl.wd, cfg.top_k, cfg.rsf, cfg.padding_m,
+                                  cfg.block_m, wl.swgu, wl.swd, fuse_swiglu=wl.fuse, buffers=b4, expert_bias=wl.bias,
+                                  scoring=cfg.scoring, renormalize=cfg.renormalize, w_down_fp8=qw, w_gate_up_fp8=qg,
+                                  w_shared_fp8=qs)
+        for _ in range(warmup):
+            fwd4()
+        e4 = []
+        for _ in range(steps):
+            a = ev()
+            fwd4()
+            e4.append((a, ev()))
+        torch.cuda.synchronize()
+        f4_ms = sum(a.elapsed_time(b) for a, b in e4) / len(e4)
+        del b4, qs
+    del qg
     flop_gu = 4.0 * cfg.numel * cfg.H * cfg.F
     return {"gemm_ms": round(g_ms, 4), **pct(g_list), "quant_h_ms": round(q_ms, 4),
             "forward_ms": round(f_ms, 4), "forward_tflops": round(flop_fwd / (f_ms * 1e-3) / 1e12, 2),
             "gate_up_gemm_ms": round(u_ms, 4), "gate_up_tflops": round(flop_gu / (u_ms * 1e-3) / 1e12, 2),
             "forward_both_fp8_ms": round(f88_ms, 4),
             "forward_both_fp8_tflops": round(flop_fwd / (f88_ms * 1e-3) / 1e12, 2),
+            "forward_all_fp8_ms": None if f4_ms is None else round(f4_ms, 4),
+            "forward_all_fp8_tflops": None if f4_ms is None else round(flop_fwd / (f4_ms * 1e-3) / 1e12, 2),
             "tflops": round(flop / (g_ms * 1e-3) / 1e12, 2),
             "fp8_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
             "bf16_mfma_frac": round(flop / (g_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}

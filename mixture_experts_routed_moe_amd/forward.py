@@ -49,13 +49,14 @@ class MoEBuffers:
     """Device buffers for every intermediate of one forward of `shape`."""
 
     def __init__(self, shape: MoEShape, device, fuse_swiglu: bool = True, fuse_permute: bool = True,
-                 fp8_down: bool = False, fp8_gate_up: bool = False):
+                 fp8_down: bool = False, fp8_gate_up: bool = False, fp8_shared: bool = False):
         s = shape
         self.shape = s
         self.fuse_swiglu = fuse_swiglu
         self.fuse_permute = fuse_permute
         self.fp8_down = fp8_down
         self.fp8_gate_up = fp8_gate_up
+        self.fp8_shared = fp8_shared
         bf16 = dict(dtype=torch.bfloat16, device=device)
         self.topk_ids = torch.empty(s.T, s.top_k, dtype=torch.int32, device=device)
         self.topk_weights = torch.empty(s.T, s.top_k, dtype=torch.float32, device=device)
@@ -69,11 +70,15 @@ class MoEBuffers:
         self.qa = None if not fp8_down else {
             "q_row": torch.empty(s.numel, s.F, dtype=torch.uint8, device=device),
             "s_row": torch.empty(s.numel, s.F // 128, dtype=torch.float32, device=device)}
-        # e4m3 codes of the hidden states (one row per token), for the FP8 gate_up
-        self.qh = None if not fp8_gate_up else {
+        # e4m3 codes of the hidden states (one row per token), for the FP8 gate_up GEMMs
+        self.qh = None if not (fp8_gate_up or fp8_shared) else {
             "q_row": torch.empty(s.T, s.H, dtype=torch.uint8, device=device),
             "s_row": torch.empty(s.T, s.H // 128, dtype=torch.float32, device=device)}
         self.out = torch.empty(s.T, s.H, **bf16)
+        # e4m3 codes of the shared expert's h, for its FP8 down projection
+        self.qsh = None if not (fp8_shared and s.shared_F) else {
+            "q_row": torch.empty(s.T, s.shared_F, dtype=torch.uint8, device=device),
+            "s_row": torch.empty(s.T, s.shared_F // 128, dtype=torch.float32, device=device)}
         if s.shared_F:
             self.shared_gate_up = None if fuse_swiglu else torch.empty(s.T, 2 * s.shared_F, **bf16)
             self.shared_h = torch.empty(s.T, s.shared_F, **bf16)
@@ -90,7 +95,8 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
                        renormalize: bool = True, return_parts: bool = False,
                        shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True,
                        w_down_fp8: Optional[Dict[str, torch.Tensor]] = None,
-                       w_gate_up_fp8: Optional[Dict[str, torch.Tensor]] = None):
+                       w_gate_up_fp8: Optional[Dict[str, torch.Tensor]] = None,
+                       w_shared_fp8: Optional[Dict[str, Dict[str, torch.Tensor]]] = None):
     """out [T, H] bf16 = rsf * sum_j w_j * expert_j(hidden) (+ shared_expert(hidden)).
 
     With return_parts=True returns (shared_out, routed_out) instead, the split
@@ -112,6 +118,12 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     pair's row through the dispatch permutation (needs fuse_permute; buffers
     made with fp8_gate_up=True).
 
+    w_shared_fp8: the shared expert's two GEMMs in FP8: {"gate_up": ...,
+    "down": ...}, each from fp8_block_quant_weights of the shared weights; its
+    gate_up reads the hidden states' e4m3 codes (one dense group), its h is
+    quantized to 1x128-tile codes for the down projection (buffers made with
+    fp8_shared=True; block_m 128).
+
     fuse_permute: the gate_up GEMM reads each permuted row straight from
     `hidden` (row sorted_pair[r] // top_k) instead of a permuted copy written
     by moe_permute: the same bytes, without the copy's write and re-read.
@@ -131,19 +143,34 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
     b = buffers
     if b is None:
         b = MoEBuffers(shape, hidden.device, fuse_swiglu, fuse_permute, w_down_fp8 is not None,
-                       w_gate_up_fp8 is not None)
+                       w_gate_up_fp8 is not None, w_shared_fp8 is not None)
     elif (dataclasses.astuple(b.shape) != dataclasses.astuple(shape) or b.fuse_swiglu != fuse_swiglu
           or b.fuse_permute != fuse_permute or (w_down_fp8 is not None and b.qa is None)
-          or (w_gate_up_fp8 is not None and b.qh is None)):
+          or (w_gate_up_fp8 is not None and b.qh is None)
+          or (w_shared_fp8 is not None and shared_F and b.qsh is None)):
         raise ValueError("routed_moe_forward: buffers were made for another shape")
 
+    quant_hidden = w_gate_up_fp8 is not None or (w_shared_fp8 is not None and shared_F)
+    if quant_hidden:
+        # the hidden states' e4m3 codes, read by both FP8 gate_up GEMMs
+        _lib.tile_quant_fp8(hidden, out=b.qh, transposed=False)
+
     def shared_expert():
-        if fuse_swiglu:
-            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, True, b.shared_h)
+        sgu = b.shared_h if fuse_swiglu else b.shared_gate_up
+        if w_shared_fp8 is not None:
+            _lib.grouped_gemm_gate_up_fp8(b.qh["q_row"], b.qh["s_row"], w_shared_fp8["gate_up"]["q"],
+                                          w_shared_fp8["gate_up"]["s"], None, padding_m, block_m, fuse_swiglu,
+                                          out=sgu)
         else:
-            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, False, b.shared_gate_up)
+            _lib.grouped_gemm_gate_up(hidden, shared_w_gate_up, None, padding_m, block_m, fuse_swiglu, sgu)
+        if not fuse_swiglu:
             _lib.swiglu(b.shared_gate_up, b.shared_h)
-        _lib.grouped_gemm_down(b.shared_h, shared_w_down, None, padding_m, block_m, b.shared_y)
+        if w_shared_fp8 is not None:
+            _lib.tile_quant_fp8(b.shared_h, out=b.qsh, transposed=False)
+            _lib.grouped_gemm_fp8(b.qsh["q_row"], b.qsh["s_row"], w_shared_fp8["down"]["q"],
+                                  w_shared_fp8["down"]["s"], None, padding_m, block_m, b.shared_y)
+        else:
+            _lib.grouped_gemm_down(b.shared_h, shared_w_down, None, padding_m, block_m, b.shared_y)
 
     main = torch.cuda.current_stream(hidden.device)
     side = shared_stream if shared_F else None
@@ -158,7 +185,6 @@ def routed_moe_forward(hidden: torch.Tensor, router_logits: torch.Tensor, w_gate
         if not fuse_permute:
             raise ValueError("routed_moe_forward: the FP8 gate_up reads its rows through the permutation "
                              "(fuse_permute=True)")
-        _lib.tile_quant_fp8(hidden, out=b.qh, transposed=False)
         _lib.grouped_gemm_gate_up_fp8(b.qh["q_row"], b.qh["s_row"], w_gate_up_fp8["q"], w_gate_up_fp8["s"], tb,
                                       padding_m, block_m, fuse_swiglu, top_k=top_k, out=gu_out)
     elif fuse_permute:
@@ -210,13 +236,15 @@ class MoEForwardGraph:
                  scoring: str = "softmax", renormalize: bool = True,
                  shared_stream: Optional[torch.cuda.Stream] = None, fuse_permute: bool = True,
                  w_down_fp8: Optional[Dict[str, torch.Tensor]] = None,
-                 w_gate_up_fp8: Optional[Dict[str, torch.Tensor]] = None):
+                 w_gate_up_fp8: Optional[Dict[str, torch.Tensor]] = None,
+                 w_shared_fp8: Optional[Dict[str, Dict[str, torch.Tensor]]] = None):
         T, H = hidden.shape
         E, twoF, _ = w_gate_up.shape
         shared_F = 0 if shared_w_down is None else shared_w_down.shape[1]
         if buffers is None:
             buffers = MoEBuffers(MoEShape(T, H, twoF // 2, E, top_k, padding_m, block_m, shared_F), hidden.device,
-                                 fuse_swiglu, fuse_permute, w_down_fp8 is not None, w_gate_up_fp8 is not None)
+                                 fuse_swiglu, fuse_permute, w_down_fp8 is not None, w_gate_up_fp8 is not None,
+                                 w_shared_fp8 is not None)
         self.hidden, self.logits, self.buffers = hidden, router_logits, buffers
 
         def run():
@@ -224,7 +252,7 @@ class MoEForwardGraph:
                                       padding_m, block_m, shared_w_gate_up, shared_w_down, fuse_swiglu, buffers,
                                       expert_bias, scoring, renormalize, shared_stream=shared_stream,
                                       fuse_permute=fuse_permute, w_down_fp8=w_down_fp8,
-                                      w_gate_up_fp8=w_gate_up_fp8)
+                                      w_gate_up_fp8=w_gate_up_fp8, w_shared_fp8=w_shared_fp8)
 
         # one eager forward first: loads the library and checks every argument
         run()

@@ -1030,24 +1030,31 @@ def test_forward_graph_replay(name, side, fp8):
         assert_bf16_close(bits(out), exp["out"], "graph replay, new inputs")
 
 
-@pytest.mark.parametrize("gate_up_fp8,side", [(False, False), (False, True), (True, False), (True, True)])
-def test_forward_fp8(gate_up_fp8, side):
+@pytest.mark.parametrize("gate_up_fp8,side,shared_fp8", [(False, False, False), (False, True, False),
+                                                         (True, False, False), (True, True, False),
+                                                         (True, True, True)])
+def test_forward_fp8(gate_up_fp8, side, shared_fp8):
     """The forward with its routed down projection in FP8 (h quantized to
     1x128-tile e4m3 codes, block-scaled FP8 grouped GEMM) and, with
     gate_up_fp8, its routed gate_up too (the hidden states quantized per
     token, read through the permutation): the same bytes as the stages called
     one by one (each checked against the oracle above), and within e4m3's
     quantization error of the oracle's bf16 forward: relative L2 error under
-    5% with one FP8 GEMM, 8% with two (the codes' 3-bit mantissa sets about
-    2-3% per quantized operand; a wrong scale or a dropped block would be far
-    above it)."""
+    5% with one FP8 GEMM, 8% with two or four (shared_fp8: the shared
+    expert's GEMMs too; the codes' 3-bit mantissa sets about 2-3% per
+    quantized operand; a wrong scale or a dropped block would be far above
+    it)."""
     d = dev()
     cfg = SHARED_SMALL
     inp = inputs(cfg, d)
     qw = mx.fp8_block_quant_weights(inp["w_down"])
     qg = mx.fp8_block_quant_weights(inp["w_gate_up"]) if gate_up_fp8 else None
+    qs = None
+    if shared_fp8:
+        qs = {"gate_up": mx.fp8_block_quant_weights(inp["shared_w_gate_up"]),
+              "down": mx.fp8_block_quant_weights(inp["shared_w_down"])}
     stream = torch.cuda.Stream(d) if side else None
-    out = _gpu_forward(cfg, inp, w_down_fp8=qw, w_gate_up_fp8=qg, shared_stream=stream).clone()
+    out = _gpu_forward(cfg, inp, w_down_fp8=qw, w_gate_up_fp8=qg, w_shared_fp8=qs, shared_stream=stream).clone()
     # the same stages called one by one
     ids, w = mx.moe_topk_softmax(inp["logits"], cfg.top_k, scoring=cfg.scoring, renormalize=cfg.renormalize)
     tb = mx.moe_align(ids, cfg.E, cfg.padding_m, cfg.block_m)
@@ -1060,8 +1067,14 @@ def test_forward_fp8(gate_up_fp8, side):
                                            cfg.block_m)
     qa = mx.tile_quant_fp8(h, transposed=False)
     y = mx.grouped_gemm_fp8(qa["q_row"], qa["s_row"], qw["q"], qw["s"], tb, cfg.padding_m, cfg.block_m)
-    sh = mx.grouped_gemm_down(mx.grouped_gemm_gate_up(inp["hidden"], inp["shared_w_gate_up"], None, 128, 128),
-                              inp["shared_w_down"], None, 128, 128)
+    if shared_fp8:
+        qh = mx.tile_quant_fp8(inp["hidden"], transposed=False)
+        shh = mx.grouped_gemm_gate_up_fp8(qh["q_row"], qh["s_row"], qs["gate_up"]["q"], qs["gate_up"]["s"], None, 128)
+        qsh = mx.tile_quant_fp8(shh, transposed=False)
+        sh = mx.grouped_gemm_fp8(qsh["q_row"], qsh["s_row"], qs["down"]["q"], qs["down"]["s"], None, 128)
+    else:
+        sh = mx.grouped_gemm_down(mx.grouped_gemm_gate_up(inp["hidden"], inp["shared_w_gate_up"], None, 128, 128),
+                                  inp["shared_w_down"], None, 128, 128)
     ref = mx.moe_unpermute(y, tb["pair_to_row"], w, cfg.rsf, sh)
     assert torch.equal(out, ref)
     exp = oracle_tokens(cfg, inp, np.arange(cfg.T))["out"]
