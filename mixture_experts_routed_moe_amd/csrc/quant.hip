@@ -176,7 +176,7 @@ __device__ __forceinline__ bool find_group_block(const int32_t* __restrict__ gs,
 // q_t row of the block) instead of one per 128x128 block. gs == nullptr: one
 // group of M rows (GROUPED = false). Blocks past the groups' padded total
 // write zero codes and scales into their q_t columns.
-template <bool SWIGLU, bool PER_TILE, bool GROUPED, bool TRANS = true>
+template <bool SWIGLU, bool PER_TILE, bool GROUPED, bool TRANS = true, int NB = 1>
 __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                    const int32_t* __restrict__ gs, int E, int m_pad,
                                                                    int n_fb, uint8_t* __restrict__ q_row,
@@ -190,9 +190,11 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
   static_assert(kLds * 4 >= kTile * kTile, "the transposed block fits in the table's space");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = tid & 15, rg = tid >> 4;
-  const int fb = blockIdx.x % n_fb;
-  const int pb = blockIdx.x / n_fb;
-  const int col0 = fb * kTile + cg * 8;
+  // NB adjacent column blocks per workgroup (their loads in flight together)
+  static_assert(NB == 1 || !SWIGLU, "the SiLU table and the transposed codes share LDS: one block");
+  const int n_fbw = n_fb / NB;
+  const int fb0 = (blockIdx.x % n_fbw) * NB;
+  const int pb = blockIdx.x / n_fbw;
   const int n_pb = m_pad / kTile;
 
   int r0, rows;
@@ -210,18 +212,22 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
   }
   if (!live) {
     if constexpr (!TRANS) return;
-    // past the last group: zero codes and scales in this block's q_t columns
+    // past the last group: zero codes and scales in these blocks' q_t columns
 #pragma unroll
-    for (int r = 0; r < (kTile * kTile / 16) / kQuantThreads; ++r) {
-      const int piece = tid + kQuantThreads * r;
-      const int c = piece >> 3, part = piece & 7;
-      *reinterpret_cast<uint4*>(q_t + static_cast<int64_t>(fb * kTile + c) * m_pad + pb * kTile + part * 16) =
-          make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (PER_TILE) {
-      if (tid < kTile) s_t[static_cast<int64_t>(fb * kTile + tid) * n_pb + pb] = 0.0f;
-    } else if (tid == 0) {
-      s_t[static_cast<int64_t>(fb) * n_pb + pb] = 0.0f;
+    for (int cb = 0; cb < NB; ++cb) {
+      const int fb = fb0 + cb;
+#pragma unroll
+      for (int r = 0; r < (kTile * kTile / 16) / kQuantThreads; ++r) {
+        const int piece = tid + kQuantThreads * r;
+        const int c = piece >> 3, part = piece & 7;
+        *reinterpret_cast<uint4*>(q_t + static_cast<int64_t>(fb * kTile + c) * m_pad + pb * kTile + part * 16) =
+            make_uint4(0u, 0u, 0u, 0u);
+      }
+      if (PER_TILE) {
+        if (tid < kTile) s_t[static_cast<int64_t>(fb * kTile + tid) * n_pb + pb] = 0.0f;
+      } else if (tid == 0) {
+        s_t[static_cast<int64_t>(fb) * n_pb + pb] = 0.0f;
+      }
     }
     return;
   }
@@ -229,18 +235,28 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
 
   // all 8 (SWIGLU) or 4 loads first; rows past the block's valid rows read
   // its last row (in bounds) and are masked
-  uint4 g[4], u[4];
+  uint4 gb[NB][4], u[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = r0 + min(lrow0 + i, rows - 1);
     const uint16_t* rp = x + m * (SWIGLU ? 2 : 1) * K;
-    g[i] = *reinterpret_cast<const uint4*>(rp + col0);
-    if (SWIGLU) u[i] = *reinterpret_cast<const uint4*>(rp + K + col0);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) gb[cb][i] = *reinterpret_cast<const uint4*>(rp + (fb0 + cb) * kTile + cg * 8);
+    if (SWIGLU) u[i] = *reinterpret_cast<const uint4*>(rp + K + fb0 * kTile + cg * 8);
   }
   if (SWIGLU) load_silu_table(tab, tid, kQuantThreads);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (SWIGLU) __syncthreads();
 
+  // each block in turn: fb, its first column col0 and its loaded rows g (the
+  // row-layout-only form, which returns at the end of its block, has NB = 1)
+  static_assert(NB == 1 || TRANS, "one block without the transposed layout");
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+  if (cb > 0) __syncthreads();  // the previous block is done with the LDS staging and s_wmax
+  const int fb = fb0 + cb;
+  const uint4 (&g)[4] = gb[cb];
+  const int col0 = fb * kTile + cg * 8;
   uint32_t hp[4][4];  // h as bf16 pairs: hp[i][k] holds columns 2k, 2k+1 of row i
   if constexpr (SWIGLU) {
     // Fast path: every gate of the wave is in the table's range (bf16
@@ -423,6 +439,7 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
     *reinterpret_cast<uint4*>(q_t + static_cast<int64_t>(fb * kTile + c) * m_pad + pb * kTile + part * 16) =
         *reinterpret_cast<const uint4*>(tq + c * kTile + part * 16);
   }
+  }
 }
 
 int launch_silu_table(hipStream_t stream) {
@@ -465,9 +482,27 @@ int launch_tile_quant(const uint16_t* x, int64_t M, int K, const int32_t* gs, in
   }
   const unsigned grid = static_cast<unsigned>(blocks);
   const int Mi = static_cast<int>(M), mp = static_cast<int>(m_pad);
-#define MOE_TQ(PT, GR)                                                                                   \
-  tile_quant_kernel<SWIGLU, PT, GR><<<grid, kQuantThreads, 0, stream>>>(x, Mi, K, gs, E, mp, n_fb, q_row, s_row, \
-                                                                        q_t, s_t)
+#ifndef MOE_TQ_PAIR
+#define MOE_TQ_PAIR 1
+#endif
+#ifndef MOE_TQ_PAIR_MIN_WGS
+#define MOE_TQ_PAIR_MIN_WGS 1024
+#endif
+  // without the SwiGLU a block is 32 KiB of loads: two adjacent column blocks
+  // per workgroup keep as many bytes in flight as the SwiGLU form. A small
+  // launch keeps one block per workgroup, since halving its grid would leave
+  // compute units idle (1024 paired workgroups = 4 per CU).
+  const bool pair = MOE_TQ_PAIR && !SWIGLU && !per_tile && n_fb % 2 == 0 && blocks >= 2 * MOE_TQ_PAIR_MIN_WGS;
+  const unsigned grid2 = static_cast<unsigned>(blocks / 2);
+#define MOE_TQ(PT, GR)                                                                                            \
+  do {                                                                                                            \
+    if (pair)                                                                                                     \
+      tile_quant_kernel<SWIGLU, PT, GR, true, (SWIGLU || PT) ? 1 : 2><<<grid2, kQuantThreads, 0, stream>>>(       \
+          x, Mi, K, gs, E, mp, n_fb, q_row, s_row, q_t, s_t);                                                     \
+    else                                                                                                          \
+      tile_quant_kernel<SWIGLU, PT, GR><<<grid, kQuantThreads, 0, stream>>>(x, Mi, K, gs, E, mp, n_fb, q_row,     \
+                                                                            s_row, q_t, s_t);                     \
+  } while (0)
   if (q_t == nullptr) {
     // row layout only (no transposed outputs): one pass over ceil(M/128) blocks
     tile_quant_kernel<SWIGLU, false, false, false><<<grid, kQuantThreads, 0, stream>>>(

@@ -867,6 +867,28 @@ def test_tile_quant_random_groups_and_overwrite(per_tile):
     _tq_equal(q, ref, f"random groups {sizes.tolist()}")
 
 
+
+def test_tile_quant_paired_blocks_overwrite():
+    """A launch large enough that each workgroup takes two adjacent column
+    blocks (block scales, no SwiGLU, over 2048 blocks): random ragged groups,
+    outputs pre-filled so every byte the contract covers must be written,
+    including the zero columns of the padded tails."""
+    d = dev()
+    rng = np.random.default_rng(95)
+    sizes = rng.choice([0, 1, 5, 127, 128, 129, 300, 513, 1000], size=64).astype(np.int32)
+    M, K = int(sizes.sum()), 2048
+    m_pad = mx.tile_quant_fp8_m_pad_bound(M, len(sizes))
+    assert (m_pad // 128) * (K // 128) >= 2048
+    say("paired tile quant", M, K, m_pad)
+    x = moe_synth.normal_bf16(moe_synth.tensor_key(96, M), (M, K), 1.0, d)
+    out = {"q_row": torch.full((M, K), 0xFF, dtype=torch.uint8, device=d),
+           "s_row": torch.full((M, K // 128), float("nan"), device=d),
+           "q_t": torch.full((K, m_pad), 0xFF, dtype=torch.uint8, device=d),
+           "s_t": torch.full((K // 128, m_pad // 128), float("nan"), device=d)}
+    q = mx.tile_quant_fp8(x, _t(sizes, d), per_tile=False, m_pad=m_pad, out=out)
+    ref = oracle.quant_fp8_grouped(bits(x), sizes, "block", m_pad=m_pad)
+    _tq_equal(q, ref, "paired blocks")
+
 def test_tile_quant_ungrouped_equals_swiglu_quant_fp8():
     """One group, block scales, SwiGLU input: the same bytes as swiglu_quant_fp8
     (and as quantizing the unfused SwiGLU output without it)."""
