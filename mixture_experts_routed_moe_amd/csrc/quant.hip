@@ -492,12 +492,12 @@ int launch_tile_quant(const uint16_t* x, int64_t M, int K, const int32_t* gs, in
   // per workgroup keep as many bytes in flight as the SwiGLU form. A small
   // launch keeps one block per workgroup, since halving its grid would leave
   // compute units idle (1024 paired workgroups = 4 per CU).
-  const bool pair = MOE_TQ_PAIR && !SWIGLU && !per_tile && n_fb % 2 == 0 && blocks >= 2 * MOE_TQ_PAIR_MIN_WGS;
+  const bool pair = MOE_TQ_PAIR && !SWIGLU && n_fb % 2 == 0 && blocks >= 2 * MOE_TQ_PAIR_MIN_WGS;
   const unsigned grid2 = static_cast<unsigned>(blocks / 2);
 #define MOE_TQ(PT, GR)                                                                                            \
   do {                                                                                                            \
     if (pair)                                                                                                     \
-      tile_quant_kernel<SWIGLU, PT, GR, true, (SWIGLU || PT) ? 1 : 2><<<grid2, kQuantThreads, 0, stream>>>(       \
+      tile_quant_kernel<SWIGLU, PT, GR, true, SWIGLU ? 1 : 2><<<grid2, kQuantThreads, 0, stream>>>(              \
           x, Mi, K, gs, E, mp, n_fb, q_row, s_row, q_t, s_t);                                                     \
     else                                                                                                          \
       tile_quant_kernel<SWIGLU, PT, GR><<<grid, kQuantThreads, 0, stream>>>(x, Mi, K, gs, E, mp, n_fb, q_row,     \
