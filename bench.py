@@ -13,7 +13,9 @@ Prints one JSON line. `value` is forward TFLOP/s (6*T*k*H*F routed plus
 6*T*H*Fs shared, per forward, over the timed steps); `ms_per_step` is ms per
 forward. `roofline` is for the dominant kernel (grouped_gemm_gate_up): its
 average duration comes from HIP events recorded on the launch stream around
-every launch inside the timed region; the algorithmic bytes and FLOPs per
+every launch inside the timed region, which carries no other events (the
+other stages' figures under "kernels" come from as many staged forwards, events
+around every stage, after the timed region); the algorithmic bytes and FLOPs per
 launch are counted from the realized routing (active experts' weights once,
 activations in and out once). `cpu_baseline` times the oracle on a bounded
 sample of tokens on the host cores. `other_workloads` times the same number
@@ -147,13 +149,16 @@ class Workload:
                                           renormalize=cfg.renormalize, shared_stream=side,
                                           fuse_permute=self.bufs.fuse_permute)
 
-    def run(self, steps, warmup, ev, whole=False, side=None):
+    def run(self, steps, warmup, ev, whole=False, side=None, live=None):
         """Times `steps` forwards after `warmup` untimed ones. whole=False:
         each forward as its stages with HIP events around every stage (the
-        per-kernel figures come from the timed region itself). whole=True:
-        whole forwards through `routed_moe_forward` (shared expert on `side`
-        when given) with events only around each forward, then the same
-        number of staged forwards, in line, for the per-kernel figures."""
+        per-kernel figures come from the timed region itself); with `live`
+        (a stage name), events only around that stage's launch in the timed
+        region, and the other stages' figures from as many staged forwards
+        after it. whole=True: whole forwards through `routed_moe_forward`
+        (shared expert on `side` when given) with events only around each
+        forward, then the same number of staged forwards, in line, for the
+        per-kernel figures."""
         import torch
         cfg, fuse = self.cfg, self.fuse
         ev_log = {s: [] for s in STAGES}
@@ -176,6 +181,8 @@ class Workload:
             a = ev()
             if whole:
                 self.forward(side)
+            elif live:
+                self.step(lambda name, fn: timed(name, fn) if name == live else fn())
             else:
                 self.step(timed)
             step_ev.append((a, ev()))
@@ -202,8 +209,9 @@ class Workload:
             torch.cuda.synchronize()
             graph_ms = sum(a.elapsed_time(b) for a, b in gev) / len(gev)
             del g
+        if whole or live:
             for _ in range(steps):
-                self.step(timed)
+                self.step(lambda name, fn: fn() if name == live else timed(name, fn))
             torch.cuda.synchronize()
 
         stage_ms = {s: (sum(a.elapsed_time(b) for a, b in v) / len(v)) for s, v in ev_log.items() if v}
@@ -255,7 +263,10 @@ class Workload:
         summary = {
             "ms_per_forward": round(ms_per_step, 4), **{"step_" + k: v for k, v in step_pct.items()},
             "timing": ("whole forwards, shared expert on a second stream" if whole and side is not None and cfg.shared_F
-                       else "whole forwards" if whole else "staged forwards, events around every stage"),
+                       else "whole forwards" if whole
+                       else f"forwards with events around the {live} launch only (the other stages from as many "
+                            "staged forwards after the timed region)" if live
+                       else "staged forwards, events around every stage"),
             "ms_per_forward_graph": None if graph_ms is None else round(graph_ms, 4),
             "tflops_graph": None if graph_ms is None else round(flop_fwd / (graph_ms * 1e-3) / 1e12, 2),
             "tflops": round(flop_fwd / (ms_per_step * 1e-3) / 1e12, 2),
@@ -507,7 +518,7 @@ def main():
         e.record(stream)
         return e
 
-    res = wl.run(args.steps, args.warmup, ev)
+    res = wl.run(args.steps, args.warmup, ev, live="gate_up")
     ms_per_step = res["ms_per_step"]
     stage_ms, kernels = res["stage_ms"], res["kernels"]
     flop_gate_up, bytes_gate_up, flop_down = res["flop_gate_up"], res["bytes_gate_up"], res["flop_down"]
@@ -611,7 +622,7 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "step_ms_p50": step_pct["ms_p50"], "step_ms_min": step_pct["ms_min"],
         "step_ms_p90": step_pct["ms_p90"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded counter-based generator, N(0,1)-shaped inputs, random-init weights)",
+        "timing": res["summary"]["timing"], "dtype": "bf16", "data": "synthetic (seeded counter-based generator, N(0,1)-shaped inputs, random-init weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": H, "F": F, "E": E, "top_k": cfg.top_k,
                    "padding_m": cfg.padding_m, "block_m": cfg.block_m, "routed_scaling_factor": cfg.rsf,
                    "zipf_bias_s": cfg.zipf_s, "shared_F": cfg.shared_F, "fused_swiglu": fuse, "fused_permute": not args.permute_copy,
