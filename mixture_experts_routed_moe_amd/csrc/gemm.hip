@@ -497,6 +497,36 @@ constexpr int kWideWSlots = 2;
 constexpr int kWideWRing = kWideASlots * kWideSlotBytes;  // first W slot
 constexpr int kWideLds = (kWideASlots + kWideWSlots) * kWideSlotBytes;
 
+// SiLU table of the fused gate_up epilogue: entry i is silu_spec of the bf16
+// gate moe::silu_table_entry(i) decodes (|g| in [2^-25, 128), both signs),
+// 32 KiB. gemm_silu_table_kernel writes it before each fused wide launch on
+// the same stream (constants: a concurrent call on another stream writes the
+// same bits).
+__device__ float g_gemm_silu_tab[moe::kSiluTabMid];
+
+__global__ __launch_bounds__(256) void gemm_silu_table_kernel() {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < moe::kSiluTabMid) g_gemm_silu_tab[i] = moe::silu_table_entry(i);
+}
+
+// silu_spec of a bf16 gate (bits gb) from the 8192-entry table, or the
+// closed forms outside its range: g/2 for |g| below 2^-25 and g for g at or
+// above 128 (the same bits as moe::silu_lookup). Negative gates of magnitude
+// at least 128 are not covered (silu_tab_misses); the caller evaluates those
+// directly.
+__device__ __forceinline__ float silu_tab(const float* tab, uint32_t gb) {
+  const uint32_t e = (gb >> 7) & 0xFFu;
+  const uint32_t k = e - static_cast<uint32_t>(moe::kSiluTabE0);  // wraps for e < kSiluTabE0
+  const float t = tab[((gb >> 3) & 0x1000u) | ((k & 31u) << 7) | (gb & 127u)];
+  const float g = __uint_as_float(gb << 16);
+  const float out = e < static_cast<uint32_t>(moe::kSiluTabE0) ? g * 0.5f : g;
+  return k < 32u ? t : out;
+}
+
+__device__ __forceinline__ bool silu_tab_misses(uint32_t gb) {
+  return (gb & 0x8000u) && ((gb >> 7) & 0xFFu) >= static_cast<uint32_t>(moe::kSiluTabE0 + 32);
+}
+
 template <int V>
 struct Ic {
   static constexpr int value = V;
@@ -652,6 +682,20 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     if (kt + 5 < nk) step(Ic<2>{}, Ic<1>{}, kt + 5);
   }
 
+  // FUSED: the SiLU table goes into the ring's last 32 KiB (the second W slot,
+  // above the half-tile exchange) once every wave is past its last fragment
+  // read; it lands while the halves meet
+  constexpr int kTabOff = kWideLds - moe::kSiluTabMid * 4;
+  if constexpr (FUSED) {
+    static_assert(kTabOff >= 128 * 1024, "the table sits above the exchange");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < moe::kSiluTabMid / 4 / (64 * NW); ++i) {
+      const int c = (i * NW + wave) * 64;  // a wave-wide load fills 64 consecutive 16-byte pieces
+      dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab) + c + lane, smem + kTabOff + c * 16);
+    }
+  }
+
   if constexpr (HALF) {
     // the two K halves meet in LDS (the ring is idle: every load has landed
     // at the last step's wait): the odd-sub-step waves hand over their sums
@@ -671,7 +715,8 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
             xch[((tm * 4 + tn) * 4 + q) * 64 + lane] = v;
           }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // (and for this wave's table pieces: after it the table is whole)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kpar) return;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
@@ -691,27 +736,52 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     }
   }
 
+  // FUSED without the halves: wait for the table (every wave's pieces)
+  if constexpr (FUSED && !HALF) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  const float* tab = reinterpret_cast<const float*>(smem + kTabOff);
+  // the SiLUs come from the table unless a gate of this wave needs the direct
+  // evaluation (a negative one of magnitude at least 128): one vote per wave,
+  // and one loop for each case
+  auto store = [&](auto use_tab) __attribute__((always_inline)) {
+    constexpr bool TAB = decltype(use_tab)::value != 0;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
+    for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = row0 + tm * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-      if (row >= rows) continue;
-      uint16_t* crow = C + (m_start + row) * ldc;
-      const int col = lane & 31;
-      if (FUSED) {
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + tm * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+        if (row >= rows) continue;
+        uint16_t* crow = C + (m_start + row) * ldc;
+        const int col = lane & 31;
+        if (FUSED) {
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          const uint16_t gb = moe::f32_to_bf16(acc[tm][tn][r]);
-          const uint16_t ub = moe::f32_to_bf16(acc[tm][tn + 2][r]);
-          crow[nt * (kWideW / 2) + wn * 64 + tn * 32 + col] = moe::swiglu_bf16(gb, ub);
+          for (int tn = 0; tn < 2; ++tn) {
+            const uint16_t gb = moe::f32_to_bf16(acc[tm][tn][r]);
+            const uint16_t ub = moe::f32_to_bf16(acc[tm][tn + 2][r]);
+            crow[nt * (kWideW / 2) + wn * 64 + tn * 32 + col] =
+                TAB ? moe::f32_to_bf16(silu_tab(tab, gb) * moe::bf16_to_f32(ub)) : moe::swiglu_bf16(gb, ub);
+          }
+        } else {
+#pragma unroll
+          for (int tn = 0; tn < 4; ++tn)
+            crow[nt * kWideW + wn * 128 + tn * 32 + col] = moe::f32_to_bf16(acc[tm][tn][r]);
         }
-      } else {
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-          crow[nt * kWideW + wn * 128 + tn * 32 + col] = moe::f32_to_bf16(acc[tm][tn][r]);
       }
     }
+  };
+  if constexpr (FUSED) {
+    bool miss = false;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) miss |= silu_tab_misses(moe::f32_to_bf16(acc[tm][tn][r]));
+    if (__builtin_amdgcn_readfirstlane(static_cast<int>(__ballot(miss) != 0)))
+      store(Ic<0>{});
+    else
+      store(Ic<1>{});
+  } else {
+    store(Ic<0>{});
   }
 }
 
@@ -893,6 +963,11 @@ int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
   const int64_t groups = moe::ceil_div(m_tiles, gm) * (n_tiles / gn);
   const int64_t blocks = eg ? moe::ceil_div(m_tiles, 8) * 8 * n_tiles : moe::ceil_div(groups, 8) * 8 * gm * gn;
   if (blocks > 0x7FFFFFFF || m_tiles > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
+  if (FUSED) {
+    gemm_silu_table_kernel<<<moe::kSiluTabMid / 256, 256, 0, stream>>>();
+    const int rc = moe::check_launch("gemm_silu_table_kernel");
+    if (rc) return rc;
+  }
   grouped_gemm_wide_kernel<FUSED, MOE_WIDE_WAVES><<<static_cast<unsigned>(blocks), 64 * MOE_WIDE_WAVES, 0, stream>>>(
       A, W, tb, E, numel, static_cast<int>(m_tiles), n_tiles, K, w_stride, up_row, ldc, C, gm, gn, eg);
   return moe::check_launch(name);

@@ -231,6 +231,37 @@ def test_gate_up_gather_equals_permute_then_gemm(cfg):
     assert_bf16_close(bits(got), ref_gu, "gather gate_up")
 
 
+
+def test_wide_fused_swiglu_gates_outside_table():
+    """The 256-row kernel's fused SwiGLU takes each SiLU from a table of the
+    bf16 gates with |g| in [2^-25, 128), the closed forms g/2 and g beyond it,
+    and the direct evaluation for a wave holding a gate at or below -128.
+    Gates built to land in each range (a constant-1 input column times a
+    +-1000 weight, or weights scaled by 1e-9): the fused bytes equal the
+    oracle's SwiGLU of the unfused product, and the swiglu kernel's."""
+    d = dev()
+    cfg = WIDE
+    F = cfg.F
+    xp, tb, _, _ = _gemm_setup(cfg, d)
+    xp = xp.clone()
+    xp[:, 0] = 1.0
+    w = moe_synth.w_gate_up(cfg, d).clone()
+    w[1, 0:32, 0] = 1000.0         # expert 1, gate columns 0-31: about +1000 (closed form g, table path)
+    w[2, 64:96, 0] = -1000.0       # expert 2, gate columns 64-95: about -1000 (direct evaluation)
+    w[3, 128:160, :] *= 1e-9       # expert 3, gate columns 128-159: below 2^-25 (closed form g/2)
+    h = mx.grouped_gemm_gate_up(xp, w, tb, cfg.padding_m, cfg.block_m, fuse_swiglu=True)
+    gu = mx.grouped_gemm_gate_up(xp, w, tb, cfg.padding_m, cfg.block_m, fuse_swiglu=False)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    assert gs[1] > 128 and gs[2] > 128 and gs[3] > 128   # the 256-row kernel's tiles
+    g = gu[:, :F].float().cpu().numpy()
+    rows = lambda e: slice(int(go[e]), int(go[e] + gs[e]))
+    assert (g[rows(1), 0:32] >= 128).all()
+    assert (g[rows(2), 64:96] <= -128).all()
+    tiny = np.abs(g[rows(3), 128:160])
+    assert (tiny < 2.0 ** -25).all() and (tiny > 0).any()
+    assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
+    assert torch.equal(h, mx.swiglu(gu))
+
 def test_gate_up_gather_past_4gib():
     """Hidden states past 2^32 bytes (T = 300000, H = 7168: 4.3 GB): the
     256-row kernel addresses gathered rows with 32-bit offsets from the
