@@ -183,15 +183,18 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
                                                                    float* __restrict__ s_row,
                                                                    uint8_t* __restrict__ q_t,
                                                                    float* __restrict__ s_t) {
-  // the SiLU table, and once the SiLUs are done the transposed codes of the block
+  // the SiLU table, and once the SiLUs are done the transposed codes of the
+  // block; with two SwiGLU blocks a workgroup the second block still needs
+  // the table, so the codes get a 16 KiB area of their own
   constexpr int kLds = SWIGLU ? kSiluTabLds : kTile * kTile / 4;
+  constexpr bool kOwnStage = SWIGLU && NB > 1;
   __shared__ __attribute__((aligned(16))) float tab[kLds];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kOwnStage ? kTile * kTile : 16];
   __shared__ uint32_t s_wmax[kQuantThreads / 64][PER_TILE ? kTile / 2 : 1];
   static_assert(kLds * 4 >= kTile * kTile, "the transposed block fits in the table's space");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = tid & 15, rg = tid >> 4;
   // NB adjacent column blocks per workgroup (their loads in flight together)
-  static_assert(NB == 1 || !SWIGLU, "the SiLU table and the transposed codes share LDS: one block");
   const int n_fbw = n_fb / NB;
   const int fb0 = (blockIdx.x % n_fbw) * NB;
   const int pb = blockIdx.x / n_fbw;
@@ -235,14 +238,17 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
 
   // all 8 (SWIGLU) or 4 loads first; rows past the block's valid rows read
   // its last row (in bounds) and are masked
-  uint4 gb[NB][4], u[4];
+  uint4 gb[NB][4], ub[SWIGLU ? NB : 1][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = r0 + min(lrow0 + i, rows - 1);
     const uint16_t* rp = x + m * (SWIGLU ? 2 : 1) * K;
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) gb[cb][i] = *reinterpret_cast<const uint4*>(rp + (fb0 + cb) * kTile + cg * 8);
-    if (SWIGLU) u[i] = *reinterpret_cast<const uint4*>(rp + K + fb0 * kTile + cg * 8);
+    if (SWIGLU) {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) ub[cb][i] = *reinterpret_cast<const uint4*>(rp + K + (fb0 + cb) * kTile + cg * 8);
+    }
   }
   if (SWIGLU) load_silu_table(tab, tid, kQuantThreads);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -256,6 +262,7 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
   if (cb > 0) __syncthreads();  // the previous block is done with the LDS staging and s_wmax
   const int fb = fb0 + cb;
   const uint4 (&g)[4] = gb[cb];
+  const uint4 (&u)[4] = ub[SWIGLU ? cb : 0];
   const int col0 = fb * kTile + cg * 8;
   uint32_t hp[4][4];  // h as bf16 pairs: hp[i][k] holds columns 2k, 2k+1 of row i
   if constexpr (SWIGLU) {
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
   // transposed layout through LDS: the block's column c is 128 bytes (its
   // rows) of q_t row fb*128 + c; this thread's 4 rows of a column are 4 of
   // them. Rows past the valid ones hold code 0, which is the required padding.
-  uint8_t* tq = reinterpret_cast<uint8_t*>(tab);
+  uint8_t* tq = kOwnStage ? stage : reinterpret_cast<uint8_t*>(tab);
 #pragma unroll
   for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(tq + (cg * 8 + j) * kTile + rg * 4) = qt[j];
   __syncthreads();
@@ -488,16 +495,22 @@ int launch_tile_quant(const uint16_t* x, int64_t M, int K, const int32_t* gs, in
 #ifndef MOE_TQ_PAIR_MIN_WGS
 #define MOE_TQ_PAIR_MIN_WGS 1024
 #endif
-  // without the SwiGLU a block is 32 KiB of loads: two adjacent column blocks
-  // per workgroup keep as many bytes in flight as the SwiGLU form. A small
-  // launch keeps one block per workgroup, since halving its grid would leave
-  // compute units idle (1024 paired workgroups = 4 per CU).
-  const bool pair = MOE_TQ_PAIR && !SWIGLU && n_fb % 2 == 0 && blocks >= 2 * MOE_TQ_PAIR_MIN_WGS;
+  // Grouped launches: two adjacent column blocks per workgroup, so half as
+  // many workgroups pay the group-size scan that must finish before a
+  // workgroup's first load (with the SwiGLU the second block's transposed
+  // codes take their own LDS, the table staying for it). Ungrouped launches
+  // have no scan and were slower paired (SwiGLU, M x 2048: 0.094 -> 0.105 ms).
+  // A small launch keeps one block per workgroup, since halving its grid
+  // would leave compute units idle (1024 paired workgroups = 4 per CU).
+  const bool pair = MOE_TQ_PAIR && gs != nullptr && n_fb % 2 == 0 && blocks >= 2 * MOE_TQ_PAIR_MIN_WGS;
   const unsigned grid2 = static_cast<unsigned>(blocks / 2);
+  // (the per-tile SwiGLU form is unpaired: two of its blocks need more than
+  // 128 VGPRs, one workgroup per CU)
 #define MOE_TQ(PT, GR)                                                                                            \
   do {                                                                                                            \
-    if (pair)                                                                                                     \
-      tile_quant_kernel<SWIGLU, PT, GR, true, SWIGLU ? 1 : 2><<<grid2, kQuantThreads, 0, stream>>>(              \
+    constexpr int kNB = (GR && !(SWIGLU && PT)) ? 2 : 1;                                                         \
+    if (pair && kNB == 2)                                                                                         \
+      tile_quant_kernel<SWIGLU, PT, GR, true, kNB><<<grid2, kQuantThreads, 0, stream>>>(                         \
           x, Mi, K, gs, E, mp, n_fb, q_row, s_row, q_t, s_t);                                                     \
     else                                                                                                          \
       tile_quant_kernel<SWIGLU, PT, GR><<<grid, kQuantThreads, 0, stream>>>(x, Mi, K, gs, E, mp, n_fb, q_row,     \

@@ -899,10 +899,11 @@ def test_tile_quant_random_groups_and_overwrite(per_tile):
 
 
 
-@pytest.mark.parametrize("per_tile", [False, True])
-def test_tile_quant_paired_blocks_overwrite(per_tile):
-    """A launch large enough that each workgroup takes two adjacent column
-    blocks (no SwiGLU, over 2048 blocks): random ragged groups,
+@pytest.mark.parametrize("per_tile,swiglu", [(False, False), (True, False), (False, True)])
+def test_tile_quant_paired_blocks_overwrite(per_tile, swiglu):
+    """A grouped launch large enough that each workgroup takes two adjacent
+    column blocks (over 2048 blocks; the per-tile SwiGLU form stays
+    unpaired): random ragged groups,
     outputs pre-filled so every byte the contract covers must be written,
     including the zero columns of the padded tails."""
     d = dev()
@@ -911,15 +912,16 @@ def test_tile_quant_paired_blocks_overwrite(per_tile):
     M, K = int(sizes.sum()), 2048
     m_pad = mx.tile_quant_fp8_m_pad_bound(M, len(sizes))
     assert (m_pad // 128) * (K // 128) >= 2048
-    say("paired tile quant", M, K, m_pad, per_tile)
-    x = moe_synth.normal_bf16(moe_synth.tensor_key(96, M), (M, K), 1.0, d)
+    say("paired tile quant", M, K, m_pad, per_tile, swiglu)
+    x = moe_synth.normal_bf16(moe_synth.tensor_key(96, M, int(swiglu)), (M, 2 * K if swiglu else K), 1.0, d)
     out = {"q_row": torch.full((M, K), 0xFF, dtype=torch.uint8, device=d),
            "s_row": torch.full((M, K // 128), float("nan"), device=d),
            "q_t": torch.full((K, m_pad), 0xFF, dtype=torch.uint8, device=d),
            "s_t": torch.full((K if per_tile else K // 128, m_pad // 128), float("nan"), device=d)}
-    q = mx.tile_quant_fp8(x, _t(sizes, d), per_tile=per_tile, m_pad=m_pad, out=out)
-    ref = oracle.quant_fp8_grouped(bits(x), sizes, "tile" if per_tile else "block", m_pad=m_pad)
-    _tq_equal(q, ref, f"paired blocks per_tile={per_tile}")
+    q = mx.tile_quant_fp8(x, _t(sizes, d), per_tile=per_tile, swiglu=swiglu, m_pad=m_pad, out=out)
+    h = oracle.swiglu(bits(x), K) if swiglu else bits(x)
+    ref = oracle.quant_fp8_grouped(h, sizes, "tile" if per_tile else "block", m_pad=m_pad)
+    _tq_equal(q, ref, f"paired blocks per_tile={per_tile} swiglu={swiglu}")
 
 def test_tile_quant_ungrouped_equals_swiglu_quant_fp8():
     """One group, block scales, SwiGLU input: the same bytes as swiglu_quant_fp8
