@@ -495,13 +495,13 @@ int launch_tile_quant(const uint16_t* x, int64_t M, int K, const int32_t* gs, in
 #ifndef MOE_TQ_PAIR_MIN_WGS
 #define MOE_TQ_PAIR_MIN_WGS 1024
 #endif
-  // Grouped launches: two adjacent column blocks per workgroup, so half as
-  // many workgroups pay the group-size scan that must finish before a
-  // workgroup's first load (with the SwiGLU the second block's transposed
-  // codes take their own LDS, the table staying for it). Ungrouped launches
-  // have no scan and were slower paired (SwiGLU, M x 2048: 0.094 -> 0.105 ms).
-  // A small launch keeps one block per workgroup, since halving its grid
-  // would leave compute units idle (1024 paired workgroups = 4 per CU).
+  // Grouped launches: two adjacent column blocks per workgroup, their loads in
+  // flight together (with the SwiGLU the second block's transposed codes take
+  // their own LDS, the table staying for it): measured faster on every
+  // grouped shape tried. Ungrouped launches were slower paired (SwiGLU,
+  // M x 2048: 0.094 -> 0.105 ms) and keep one block per workgroup, as does a
+  // small launch, where halving the grid would leave compute units idle
+  // (1024 paired workgroups = 4 per CU).
   const bool pair = MOE_TQ_PAIR && gs != nullptr && n_fb % 2 == 0 && blocks >= 2 * MOE_TQ_PAIR_MIN_WGS;
   const unsigned grid2 = static_cast<unsigned>(blocks / 2);
   // (the per-tile SwiGLU form is unpaired: two of its blocks need more than
