@@ -18,6 +18,12 @@
  *     the entry point says otherwise.
  *   - Results are deterministic: the same inputs give the same bytes, run to
  *     run (no atomics whose order reaches an output).
+ *   - Calls that evaluate the SwiGLU (swiglu, swiglu_quant_fp8, tile_quant_fp8
+ *     with swiglu = 1, and the fused gate_up GEMMs on their 256-row path)
+ *     first enqueue a small kernel on `stream` that writes a constant table
+ *     of exact SiLU values into a file-scope device array of the library
+ *     (static storage, not an allocation); concurrent calls on other streams
+ *     write the same bits into it.
  *
  * Page citations name the five source pages by title:
  *   TileOPs #778  "[Feat][MoE] SharedFusedMoE with native shared expert kernel and TP support"
