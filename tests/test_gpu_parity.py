@@ -899,17 +899,19 @@ def test_tile_quant_random_groups_and_overwrite(per_tile):
 
 
 
-@pytest.mark.parametrize("per_tile,swiglu", [(False, False), (True, False), (False, True)])
-def test_tile_quant_paired_blocks_overwrite(per_tile, swiglu):
+@pytest.mark.parametrize("per_tile,swiglu,n_groups,K", [(False, False, 64, 2048), (True, False, 64, 2048),
+                                                        (False, True, 64, 2048), (False, False, 400, 256)])
+def test_tile_quant_paired_blocks_overwrite(per_tile, swiglu, n_groups, K):
     """A grouped launch large enough that each workgroup takes two adjacent
     column blocks (over 2048 blocks; the per-tile SwiGLU form stays
-    unpaired): random ragged groups,
+    unpaired; 400 groups take seven rounds of the group-size scan): random
+    ragged groups,
     outputs pre-filled so every byte the contract covers must be written,
     including the zero columns of the padded tails."""
     d = dev()
-    rng = np.random.default_rng(95)
-    sizes = rng.choice([0, 1, 5, 127, 128, 129, 300, 513, 1000], size=64).astype(np.int32)
-    M, K = int(sizes.sum()), 2048
+    rng = np.random.default_rng(95 + n_groups)
+    sizes = rng.choice([0, 1, 5, 127, 128, 129, 300, 513, 1000], size=n_groups).astype(np.int32)
+    M = int(sizes.sum())
     m_pad = mx.tile_quant_fp8_m_pad_bound(M, len(sizes))
     assert (m_pad // 128) * (K // 128) >= 2048
     say("paired tile quant", M, K, m_pad, per_tile, swiglu)
@@ -921,7 +923,8 @@ def test_tile_quant_paired_blocks_overwrite(per_tile, swiglu):
     q = mx.tile_quant_fp8(x, _t(sizes, d), per_tile=per_tile, swiglu=swiglu, m_pad=m_pad, out=out)
     h = oracle.swiglu(bits(x), K) if swiglu else bits(x)
     ref = oracle.quant_fp8_grouped(h, sizes, "tile" if per_tile else "block", m_pad=m_pad)
-    _tq_equal(q, ref, f"paired blocks per_tile={per_tile} swiglu={swiglu}")
+    _tq_equal(q, ref, f"paired blocks per_tile={per_tile} swiglu={swiglu} groups={n_groups}")
+
 
 def test_tile_quant_ungrouped_equals_swiglu_quant_fp8():
     """One group, block scales, SwiGLU input: the same bytes as swiglu_quant_fp8
