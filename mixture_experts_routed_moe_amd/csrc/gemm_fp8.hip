@@ -113,6 +113,11 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
     const float* __restrict__ sw, moe::Tables tb, int64_t numel, int n_tiles, int N, int K,
     int up_row, int ldc, uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kF8StageBytes];
+  // Row-major tile order. The hardware hands workgroup w to XCD w % 8, so with
+  // n_tiles a multiple of 8 (56 and 32 on the DeepSeek-V3 shapes) column tile
+  // nt of every row block lands on XCD nt % 8: each XCD's L2 holds one eighth
+  // of every expert's weights, which are most of the bytes, while the much
+  // smaller activation codes are read by all eight.
   const int bx = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
   int g, rows;
   int64_t m_start;
