@@ -62,9 +62,22 @@ __global__ __launch_bounds__(kChunk) void align_rank_kernel(
   for (int i = tid; i < kWaves * E; i += kChunk) s_wave_cnt[i / E][i % E] = 0;
 
   // totals and this chunk's prefix, one expert per thread (E <= 1024 = threads)
+  // (eight loads in flight at a time: one at a time, each waited for, the
+  // 32 chunks of a 32768-pair launch cost 32 round trips)
   int total = 0, before = 0;
   if (tid < E) {
-    for (int c = 0; c < nchunks; ++c) {
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8) {
+      int x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = counts[static_cast<int64_t>(c + u) * E + tid];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        before += (c + u < chunk) ? x[u] : 0;
+        total += x[u];
+      }
+    }
+    for (; c < nchunks; ++c) {
       const int x = counts[static_cast<int64_t>(c) * E + tid];
       before += (c < chunk) ? x : 0;
       total += x;
