@@ -227,9 +227,12 @@ class Workload:
         flop_shared = 6.0 * cfg.T * H * cfg.shared_F
         flop_fwd = flop_gate_up + flop_down + flop_shared
         h_cols = F if fuse else 2 * F
-        # activations in: the permuted copy, or with the gather the hidden states once
-        a_in = cfg.T * H * 2 if self.bufs.fuse_permute else numel * H * 2
-        bytes_gate_up = active * 2.0 * F * H * 2 + a_in + numel * h_cols * 2
+        # algorithmic bytes (each pair's activation row counted once, numel*H*2,
+        # as for a permuted copy); with the permute folded into the loads the
+        # kernel's unique reads of the hidden states are T*H*2, reported beside
+        bytes_gate_up = active * 2.0 * F * H * 2 + numel * H * 2 + numel * h_cols * 2
+        bytes_gate_up_gathered = (active * 2.0 * F * H * 2 + (cfg.T if self.bufs.fuse_permute else numel) * H * 2
+                                  + numel * h_cols * 2)
         bytes_down = active * 1.0 * H * F * 2 + numel * F * 2 + numel * H * 2
         bytes_permute = (cfg.T + numel) * H * 2 + 4 * numel
         bytes_unpermute = numel * H * 2 + 8 * cfg.T * cfg.top_k + cfg.T * H * 2 * (2 if cfg.shared_F else 1)
@@ -279,7 +282,35 @@ class Workload:
         }
         return {"ms_per_step": ms_per_step, "step_pct": step_pct, "stage_ms": stage_ms, "kernels": kernels,
                 "flop_gate_up": flop_gate_up, "flop_down": flop_down, "flop_fwd": flop_fwd,
-                "bytes_gate_up": bytes_gate_up, "group_sizes": gs, "summary": summary}
+                "bytes_gate_up": bytes_gate_up, "bytes_gate_up_gathered": bytes_gate_up_gathered,
+                "group_sizes": gs, "summary": summary}
+
+
+def align_scaling(steps, warmup, ev, dev):
+    """moe_align alone at growing pair counts (E = 256, top_k = 8, uniform
+    random ids): its time should grow linearly with the pairs. The largest
+    case, T = 262144 tokens, is the largest aligned-table token count."""
+    import torch
+    import mixture_experts_routed_moe_amd as mx
+    out = {}
+    for T in (4096, 32768, 262144):
+        g = torch.Generator(device=dev).manual_seed(T)
+        ids = torch.argsort(torch.rand(T, 256, device=dev, generator=g), dim=1)[:, :8].to(torch.int32).contiguous()
+        tb = mx.alloc_tables(T * 8, 256, 128, 128, dev)
+        for _ in range(warmup):
+            mx.moe_align(ids, 256, 128, 128, tb)
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            a = ev()
+            mx.moe_align(ids, 256, 128, 128, tb)
+            evs.append((a, ev()))
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in evs]
+        out[f"T{T}_k8_E256"] = {"pairs": T * 8, "ms": round(sum(ms) / len(ms), 4), **pct(ms),
+                                "ns_per_pair": round(sum(ms) / len(ms) * 1e6 / (T * 8), 3)}
+        del ids, tb
+    return out
 
 
 def aligned_gemm_table(names, steps, warmup, ev, dev):
@@ -562,6 +593,7 @@ def main():
     gemm_table = aligned_gemm_table(gemm_names, args.steps, args.warmup, ev, dev) if gemm_names else {}
 
     grouped_quant = {} if args.only_primary else grouped_quant_table(args.steps, args.warmup, ev, dev)
+    align = {} if args.only_primary else align_scaling(args.steps, args.warmup, ev, dev)
 
     # fused SwiGLU + FP8 quantizer on its own workload, HIP events around each launch
     qM, qF = moe_synth.QUANT_CONFIG.M, moe_synth.QUANT_CONFIG.F
@@ -603,6 +635,9 @@ def main():
                 "bound": "hbm" if bytes_gate_up / (HBM_PEAK_GBS * 1e9) >= flop_gate_up / (BF16_PEAK_TFLOPS * 1e12) else "mfma",
                 "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None,
                 "bytes_per_launch": bytes_gate_up, "flop_per_launch": flop_gate_up,
+                "bytes_convention": "active experts' weights + numel*H*2 activations in + numel*F*2 out",
+                "bytes_per_launch_gathered": res["bytes_gate_up_gathered"],
+                "frac_gathered": round(res["bytes_gate_up_gathered"] / gu_s / 1e9 / HBM_PEAK_GBS, 4),
                 "launch_ms": round(stage_ms["gate_up"], 4), "mfma_frac": gu["mfma_frac"], "hbm_frac": gu["hbm_frac"]}
     if roofline["bound"] == "hbm":
         roofline.update(achieved=round(bytes_gate_up / gu_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
@@ -622,7 +657,7 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "step_ms_p50": step_pct["ms_p50"], "step_ms_min": step_pct["ms_min"],
         "step_ms_p90": step_pct["ms_p90"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "timing": res["summary"]["timing"], "dtype": "bf16", "data": "synthetic (seeded counter-based generator, N(0,1)-shaped inputs, random-init weights)",
+        "timing": res["summary"]["timing"], "dtype": "bf16", "data": "synthetic (router logits N(0,1) from numpy PCG64; hidden states and random-init weights from a seeded counter-based generator)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": H, "F": F, "E": E, "top_k": cfg.top_k,
                    "padding_m": cfg.padding_m, "block_m": cfg.block_m, "routed_scaling_factor": cfg.rsf,
                    "zipf_bias_s": cfg.zipf_s, "shared_F": cfg.shared_F, "fused_swiglu": fuse, "fused_permute": not args.permute_copy,
@@ -636,6 +671,7 @@ def main():
         "other_workloads": others,
         "aligned_grouped_gemm": gemm_table,
         "grouped_quant": grouped_quant,
+        "align_scaling": align,
         "fp8_down": fp8,
     }
     print(json.dumps(line), flush=True)

@@ -2,17 +2,25 @@
 // group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx, plus
 // the stable expert-major permutation).
 //
-// Two launches over chunks of 1024 (token, slot) pairs:
-//   1. count: per-chunk expert histogram (LDS atomics; counts are order-free).
-//   2. rank:  every chunk re-reads the small [nchunks, E] histogram to get
-//             the global totals and its own chunk prefix, scans the totals
-//             over experts (wavefront inclusive scans + a cross-wave pass),
-//             and ranks its pairs: lanes with the same expert are found with
-//             ballots over the bits of the expert id, the rank inside a wave
-//             is a popcount below the lane, and waves are ordered through a
-//             per-wave count table. Positions therefore follow pair order,
-//             never the order in which atomics complete.
-// Chunk 0 also writes the E-sized tables and group_idx_for_bx.
+// Three launches over chunks of 1024 (token, slot) pairs, each linear in the
+// number of pairs:
+//   1. count: per-chunk expert histogram counts[c][e] (LDS atomics; counts
+//             are order-free).
+//   2. scan:  per expert, the exclusive prefix of counts over chunks, in
+//             place, and the total (group_sizes). A workgroup takes 64
+//             experts (one per lane, so a chunk's row is one coalesced
+//             256-byte read) and its 16 waves take consecutive ranges of
+//             chunks; the range sums meet in LDS. Every histogram entry is
+//             read twice and written once.
+//   3. rank:  every chunk reads the totals and its own row of prefixes, scans
+//             the totals over experts (wavefront inclusive scans + a
+//             cross-wave pass), and ranks its pairs: lanes with the same
+//             expert are found with ballots over the bits of the expert id,
+//             the rank inside a wave is a popcount below the lane, and waves
+//             are ordered through a per-wave count table. Positions therefore
+//             follow pair order, never the order in which atomics complete.
+// Chunk 0 also writes group_offsets, group_padded_offsets and
+// group_idx_for_bx.
 #include "moe_common.h"
 
 namespace {
@@ -45,9 +53,60 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
+constexpr int kScanWaves = 16;
+
+// counts[c][e] <- sum of counts[c'][e] over c' < c; group_sizes[e] <- the sum
+// over every chunk. Grid: ceil(E / 64) workgroups of kScanWaves waves.
+__global__ __launch_bounds__(64 * kScanWaves) void align_scan_kernel(int32_t* __restrict__ counts, int nchunks, int E,
+                                                                    int32_t* __restrict__ group_sizes) {
+  __shared__ int s_part[kScanWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const bool live = e < E;
+  const int per = (nchunks + kScanWaves - 1) / kScanWaves;
+  const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
+  int32_t* col = counts + e;
+  // this wave's range sum, eight loads in flight at a time
+  int sum = 0;
+  if (live) {
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = col[static_cast<int64_t>(c + u) * E];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += x[u];
+    }
+    for (; c < c1; ++c) sum += col[static_cast<int64_t>(c) * E];
+  }
+  s_part[wave][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += s_part[w][lane];
+  if (wave == kScanWaves - 1 && live) group_sizes[e] = run + sum;
+  if (!live) return;
+  // exclusive prefixes over this wave's range, in place
+  int c = c0;
+  for (; c + 8 <= c1; c += 8) {
+    int x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = col[static_cast<int64_t>(c + u) * E];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      col[static_cast<int64_t>(c + u) * E] = run;
+      run += x[u];
+    }
+  }
+  for (; c < c1; ++c) {
+    const int x = col[static_cast<int64_t>(c) * E];
+    col[static_cast<int64_t>(c) * E] = run;
+    run += x;
+  }
+}
+
 __global__ __launch_bounds__(kChunk) void align_rank_kernel(
     const int32_t* __restrict__ ids, int numel, int E, int id_bits, int padding_m, int block_m,
-    int m_blocks, const int32_t* __restrict__ counts, int nchunks, int32_t* __restrict__ group_sizes,
+    int m_blocks, const int32_t* __restrict__ prefix, const int32_t* __restrict__ group_sizes,
     int32_t* __restrict__ group_offsets, int32_t* __restrict__ group_padded_offsets,
     int32_t* __restrict__ group_idx_for_bx, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_to_row) {
@@ -61,27 +120,12 @@ __global__ __launch_bounds__(kChunk) void align_rank_kernel(
 
   for (int i = tid; i < kWaves * E; i += kChunk) s_wave_cnt[i / E][i % E] = 0;
 
-  // totals and this chunk's prefix, one expert per thread (E <= 1024 = threads)
-  // (eight loads in flight at a time: one at a time, each waited for, the
-  // 32 chunks of a 32768-pair launch cost 32 round trips)
+  // totals and this chunk's prefix (from the scan), one expert per thread
+  // (E <= 1024 = threads)
   int total = 0, before = 0;
   if (tid < E) {
-    int c = 0;
-    for (; c + 8 <= nchunks; c += 8) {
-      int x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = counts[static_cast<int64_t>(c + u) * E + tid];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        before += (c + u < chunk) ? x[u] : 0;
-        total += x[u];
-      }
-    }
-    for (; c < nchunks; ++c) {
-      const int x = counts[static_cast<int64_t>(c) * E + tid];
-      before += (c < chunk) ? x : 0;
-      total += x;
-    }
+    total = group_sizes[tid];
+    before = prefix[static_cast<int64_t>(chunk) * E + tid];
   }
   const int padded = ((total + padding_m - 1) / padding_m) * padding_m;
   // block-wide exclusive scans of total and padded over experts
@@ -103,7 +147,6 @@ __global__ __launch_bounds__(kChunk) void align_rank_kernel(
     s_base[tid] = go + before;
     s_gpo[tid] = gpo;
     if (chunk == 0) {
-      group_sizes[tid] = total;
       group_offsets[tid] = go;
       group_padded_offsets[tid] = gpo;
     }
@@ -191,8 +234,12 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, i
   align_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_ids, static_cast<int>(numel), E, counts);
   int rc = check_launch("moe_align(count)");
   if (rc) return rc;
+  align_scan_kernel<<<static_cast<unsigned>(ceil_div(E, 64)), 64 * kScanWaves, 0, stream>>>(counts, nchunks, E,
+                                                                                          group_sizes);
+  rc = check_launch("moe_align(scan)");
+  if (rc) return rc;
   align_rank_kernel<<<nchunks, kChunk, 0, stream>>>(
       topk_ids, static_cast<int>(numel), E, id_bits, padding_m, block_m, static_cast<int>(m_blocks), counts,
-      nchunks, group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx, sorted_pair, pair_to_row);
+      group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx, sorted_pair, pair_to_row);
   return check_launch("moe_align(rank)");
 }

@@ -207,21 +207,11 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
 // tiles that share A rows or W columns run together behind one L2.
 // Consecutive groups go to different XCDs, which keeps the active (non-empty)
 // blocks spread over all eight.
-#ifndef MOE_PIPE_BK
-#define MOE_PIPE_BK 64
-#endif
-#ifndef MOE_PIPE_STAGES
-#define MOE_PIPE_STAGES 3
-#endif
-#ifndef MOE_PIPE_OCC
-#define MOE_PIPE_OCC 1
-#endif
-#ifndef MOE_PIPE_GROUP
-#define MOE_PIPE_GROUP 16
-#endif
-#ifndef MOE_PIPE_GN_MAX
-#define MOE_PIPE_GN_MAX 8
-#endif
+constexpr int kPipeBK = 64;
+constexpr int kPipeStages = 3;
+constexpr int kPipeOcc = 1;
+constexpr int kPipeGroup = 16;
+constexpr int kPipeGnMax = 8;
 
 constexpr int kPipeBM = 128;
 constexpr int kPipeBNW = 256;
@@ -488,9 +478,6 @@ constexpr int kWideW = 256;
 // serves all of them.
 __device__ __forceinline__ int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-#ifndef MOE_WIDE_SKIP
-#define MOE_WIDE_SKIP 1
-#endif
 constexpr int kWideSlotBytes = kWideRows * 128;
 constexpr int kWideASlots = 3;
 constexpr int kWideWSlots = 2;
@@ -498,16 +485,9 @@ constexpr int kWideWRing = kWideASlots * kWideSlotBytes;  // first W slot
 constexpr int kWideLds = (kWideASlots + kWideWSlots) * kWideSlotBytes;
 
 // SiLU table of the fused gate_up epilogue: entry i is silu_spec of the bf16
-// gate moe::silu_table_entry(i) decodes (|g| in [2^-25, 128), both signs),
-// 32 KiB. gemm_silu_table_kernel writes it before each fused wide launch on
-// the same stream (constants: a concurrent call on another stream writes the
-// same bits).
-__device__ float g_gemm_silu_tab[moe::kSiluTabMid];
-
-__global__ __launch_bounds__(256) void gemm_silu_table_kernel() {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < moe::kSiluTabMid) g_gemm_silu_tab[i] = moe::silu_table_entry(i);
-}
+// gate moe::silu_table_gate(i) (|g| in [2^-25, 128), both signs), 32 KiB,
+// computed at compile time (code-object data: no launch writes it).
+__device__ const moe::SiluTable<moe::kSiluTabMid> g_gemm_silu_tab = moe::make_silu_table<moe::kSiluTabMid>();
 
 // silu_spec of a bf16 gate (bits gb) from the 8192-entry table, or the
 // closed forms outside its range: g/2 for |g| below 2^-25 and g for g at or
@@ -589,11 +569,9 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   // the even sub-steps, the second the odd ones
   const int kpar = HALF ? (wm >= WM / 2) : 0;
   const int row0 = (HALF ? wm % (WM / 2) : wm) * TM * 32;
-#if MOE_WIDE_SKIP
   // 32-row MFMA tiles of this wave that hold valid rows (the others are
   // skipped: with two waves per SIMD the partner wave gets the matrix core)
   const int live_tm = __builtin_amdgcn_readfirstlane(min(TM, max(0, (rows - row0 + 31) / 32)));
-#endif
   const int khalf = lane >> 5;
   // per-lane LDS byte offset of this wave's first A and first W fragment in
   // each sub-step; the other fragments sit at constant offsets from them
@@ -650,9 +628,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
       if (i + 1 < MY_NS) read_frags(i + 1, (i + 1) & 1);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-#if MOE_WIDE_SKIP
         if (tm >= live_tm) break;  // wave-uniform: this and later row tiles hold no valid rows
-#endif
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i & 1][tm], bfr[i & 1][tn], acc[tm][tn], 0, 0, 0);
@@ -692,7 +668,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
 #pragma unroll
     for (int i = 0; i < moe::kSiluTabMid / 4 / (64 * NW); ++i) {
       const int c = (i * NW + wave) * 64;  // a wave-wide load fills 64 consecutive 16-byte pieces
-      dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab) + c + lane, smem + kTabOff + c * 16);
+      dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab.v) + c + lane, smem + kTabOff + c * 16);
     }
   }
 
@@ -812,15 +788,9 @@ __device__ __forceinline__ bool find_wide_tile(const int32_t* __restrict__ gs, i
   return false;
 }
 
-#ifndef MOE_WIDE_GMAX
-#define MOE_WIDE_GMAX 4
-#endif
-#ifndef MOE_WIDE_EG_MIN_COLS
-#define MOE_WIDE_EG_MIN_COLS 16
-#endif
-#ifndef MOE_WIDE_EG_MIN_ROW_TILES
-#define MOE_WIDE_EG_MIN_ROW_TILES 32
-#endif
+constexpr int kWideGmax = 4;
+constexpr int kWideEgMinCols = 16;
+constexpr int kWideEgMinRowTiles = 32;
 
 template <bool FUSED, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
@@ -840,7 +810,7 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
     // Groups of n_tiles tiles, one per 256-row tile of the expert-ordered list
     // (group k runs on XCD k % 8). An expert with mt tiles splits into blocks
     // of gx tiles (gx the largest divisor of n_tiles that is at most
-    // min(mt, MOE_WIDE_GMAX)); each block's gx groups cover its gx row tiles by
+    // min(mt, kWideGmax)); each block's gx groups cover its gx row tiles by
     // n_tiles / gx column tiles, so a group reuses its weight slice gx times and
     // its activation rows n_tiles / gx times from L2; the rows a block leaves
     // over take one group each (one row tile by every column tile).
@@ -858,7 +828,7 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
       mt = (tb.gs[g] + kWideRows - 1) / kWideRows;
     }
     int gx = 1;
-    for (int d = min(mt, MOE_WIDE_GMAX); d > 1; --d)
+    for (int d = min(mt, kWideGmax); d > 1; --d)
       if (n_tiles % d == 0) {
         gx = d;
         break;
@@ -912,15 +882,15 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
 }
 
 // Group shape for the tile order: GN column tiles (a divisor of n_tiles, at
-// most MOE_PIPE_GN_MAX) by GM row blocks, about MOE_PIPE_GROUP tiles.
+// most kPipeGnMax) by GM row blocks, about kPipeGroup tiles.
 void pipe_groups(int n_tiles, int& gm, int& gn) {
   gn = 1;
-  for (int d = MOE_PIPE_GN_MAX; d >= 1; --d)
+  for (int d = kPipeGnMax; d >= 1; --d)
     if (n_tiles % d == 0) {
       gn = d;
       break;
     }
-  gm = MOE_PIPE_GROUP / gn > 0 ? MOE_PIPE_GROUP / gn : 1;
+  gm = kPipeGroup / gn > 0 ? kPipeGroup / gn : 1;
 }
 
 template <bool FUSED>
@@ -931,17 +901,13 @@ int launch_pipe(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, 
   const int64_t groups = moe::ceil_div(m_blocks, gm) * (n_tiles / gn);
   const int64_t blocks = moe::ceil_div(groups, 8) * 8 * gm * gn;
   if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
-  grouped_gemm_pipe_kernel<FUSED, MOE_PIPE_BK, MOE_PIPE_STAGES, MOE_PIPE_OCC><<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
+  grouped_gemm_pipe_kernel<FUSED, kPipeBK, kPipeStages, kPipeOcc><<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
       A, W, tb, numel, static_cast<int>(m_blocks), n_tiles, K, w_stride, up_row, ldc, C, gm, gn);
   return moe::check_launch(name);
 }
 
-#ifndef MOE_WIDE_GROUP
-#define MOE_WIDE_GROUP 16
-#endif
-#ifndef MOE_WIDE_WAVES
-#define MOE_WIDE_WAVES 8
-#endif
+constexpr int kWideGroup = 16;
+constexpr int kWideWaves = 8;
 
 template <bool FUSED>
 int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int n_tiles, int K,
@@ -949,26 +915,21 @@ int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
   // every non-empty expert ends in at most one partial tile
   const int64_t m_tiles = moe::ceil_div(numel, kWideRows) + (tb.gs ? E : 0);
   int gn = 1;
-  for (int d = MOE_PIPE_GN_MAX; d >= 1; --d)
+  for (int d = kPipeGnMax; d >= 1; --d)
     if (n_tiles % d == 0) {
       gn = d;
       break;
     }
-  const int gm = MOE_WIDE_GROUP / gn > 0 ? MOE_WIDE_GROUP / gn : 1;
+  const int gm = kWideGroup / gn > 0 ? kWideGroup / gn : 1;
   // expert-aware groups (see the kernel) when a row tile has many column
   // tiles: on the DeepSeek-V3-shaped routing (16 and 28 column tiles) gate_up
   // 2.46 -> 2.44 ms and down 1.31 -> 1.28 ms (interleaved A/B); with 6 or 8
   // (the Qwen3 shapes) the fixed 16-tile groups are as fast or faster
-  const int eg = n_tiles >= MOE_WIDE_EG_MIN_COLS && m_tiles >= MOE_WIDE_EG_MIN_ROW_TILES;
+  const int eg = n_tiles >= kWideEgMinCols && m_tiles >= kWideEgMinRowTiles;
   const int64_t groups = moe::ceil_div(m_tiles, gm) * (n_tiles / gn);
   const int64_t blocks = eg ? moe::ceil_div(m_tiles, 8) * 8 * n_tiles : moe::ceil_div(groups, 8) * 8 * gm * gn;
   if (blocks > 0x7FFFFFFF || m_tiles > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
-  if (FUSED) {
-    gemm_silu_table_kernel<<<moe::kSiluTabMid / 256, 256, 0, stream>>>();
-    const int rc = moe::check_launch("gemm_silu_table_kernel");
-    if (rc) return rc;
-  }
-  grouped_gemm_wide_kernel<FUSED, MOE_WIDE_WAVES><<<static_cast<unsigned>(blocks), 64 * MOE_WIDE_WAVES, 0, stream>>>(
+  grouped_gemm_wide_kernel<FUSED, kWideWaves><<<static_cast<unsigned>(blocks), 64 * kWideWaves, 0, stream>>>(
       A, W, tb, E, numel, static_cast<int>(m_tiles), n_tiles, K, w_stride, up_row, ldc, C, gm, gn, eg);
   return moe::check_launch(name);
 }
@@ -1136,19 +1097,12 @@ int launch_gemv(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
 // LDS and are added in wave order (the result does not depend on timing).
 constexpr int kSkinnyCols = 32;
 constexpr int kSkinnyWaves = 8;
-#ifndef MOE_SKINNY_DEPTH
-#define MOE_SKINNY_DEPTH 2
-#endif
-#ifndef MOE_SKINNY_OCC
-#define MOE_SKINNY_OCC 2
-#endif
-constexpr int kSkinnyDepth = MOE_SKINNY_DEPTH;
-#ifndef MOE_SKINNY_MAX_ROWS
-#define MOE_SKINNY_MAX_ROWS 32
-#endif
+constexpr int kSkinnyOcc = 2;
+constexpr int kSkinnyDepth = 2;
+constexpr int kSkinnyMaxRows = 32;
 
 template <bool FUSED>
-__global__ __launch_bounds__(64 * kSkinnyWaves, MOE_SKINNY_OCC) void dense_skinny_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(64 * kSkinnyWaves, kSkinnyOcc) void dense_skinny_kernel(const uint16_t* __restrict__ A,
                                                                             const uint16_t* __restrict__ W, int rows,
                                                                             int K, int up_row, int ldc,
                                                                             uint16_t* __restrict__ C) {
@@ -1272,12 +1226,8 @@ int launch_skinny(const uint16_t* A, const uint16_t* W, int64_t numel, int K, in
   return moe::check_launch(name);
 }
 
-#ifndef MOE_GEMV_MAX_ROWS
-#define MOE_GEMV_MAX_ROWS 4
-#endif
-#ifndef MOE_GEMV_GROUPED_PCT
-#define MOE_GEMV_GROUPED_PCT 10
-#endif
+constexpr int kGemvMaxRows = 4;
+constexpr int kGemvGroupedPct = 10;
 
 template <bool FUSED>
 int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E, int block_m, int padding_m,
@@ -1291,29 +1241,25 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   // 256-row tiles pay off once experts average a full 128-row block (at
   // fewer rows per expert nearly every tile is a half tile and the 128-row
   // kernel, with less fixed cost per tile, is faster)
-#ifndef MOE_WIDE_MIN_ROWS
-#define MOE_WIDE_MIN_ROWS 128
-#endif
+  constexpr int kWideMinRows = 128;
   // few rows (at most 4 in one dense group, or numel <= E / 10 over the
   // experts: one decode token's top-k): the weight-streaming kernel (at 256
   // rows over 384 experts the row-tile kernels are faster)
-  const bool few_rows = tb.gs ? numel * 100 <= MOE_GEMV_GROUPED_PCT * static_cast<int64_t>(E) : numel <= MOE_GEMV_MAX_ROWS;
+  const bool few_rows = tb.gs ? numel * 100 <= kGemvGroupedPct * static_cast<int64_t>(E) : numel <= kGemvMaxRows;
   if (few_rows && K % 64 == 0 && ldc % kGemvCols == 0)
     return launch_gemv<FUSED>(A, W, tb, E, numel, K, w_stride, up_row, ldc, C, stream, name);
   // one dense group of up to 32 rows: the K-split skinny kernel
-  if (tb.gs == nullptr && tb.gather == nullptr && numel <= MOE_SKINNY_MAX_ROWS && K % 64 == 0 &&
+  if (tb.gs == nullptr && tb.gather == nullptr && numel <= kSkinnyMaxRows && K % 64 == 0 &&
       ldc % kSkinnyCols == 0)
     return launch_skinny<FUSED>(A, W, numel, K, up_row, ldc, C, stream, name);
   // the wide kernel addresses a tile's A and W rows with 32-bit byte offsets
   // (with a gather table, A's offsets count from its first row: a_off32)
   const bool wide_fits = (static_cast<int64_t>(up_row) + kWideW) * K * 2 < (int64_t(1) << 32) && a_off32;
-#ifndef MOE_WIDE_DENSE_MIN_TILES
-#define MOE_WIDE_DENSE_MIN_TILES 128
-#endif
+  constexpr int kWideDenseMinTiles = 128;
   // a dense launch with few 256-row tiles: the 128-row kernel gives it twice the workgroups
-  const bool dense_few = tb.gs == nullptr && moe::ceil_div(numel, kWideRows) * (ldc / pipe_cols) < MOE_WIDE_DENSE_MIN_TILES;
+  const bool dense_few = tb.gs == nullptr && moe::ceil_div(numel, kWideRows) * (ldc / pipe_cols) < kWideDenseMinTiles;
   if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits && !dense_few &&
-      numel >= static_cast<int64_t>(MOE_WIDE_MIN_ROWS) * E)
+      numel >= static_cast<int64_t>(kWideMinRows) * E)
     return launch_wide<FUSED>(A, W, tb, E, numel, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
   if (block_m == kPipeBM && ldc % pipe_cols == 0)
     return launch_pipe<FUSED>(A, W, tb, numel, m_blocks, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);

@@ -141,21 +141,56 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 //                constant D, which scales exactly with powers of two of g
 //                (the results stay normal), so the [-256, -128) entry times
 //                2^(exponent - 134) is exact.
-// Every entry is computed with silu_spec itself, so a lookup returns the same
-// bits as the direct evaluation.
+// Every entry is silu_spec's value, computed at compile time (below), so a
+// lookup returns the same bits as the direct evaluation.
 constexpr int kSiluTabE0 = 102;                          // bf16 exponent field of 2^-25
 constexpr int kSiluTabMid = 2 * 32 * 128;
 constexpr int kSiluTabSize = kSiluTabMid + 128;
 
-// Entry i of the table.
-__device__ __forceinline__ float silu_table_entry(int i) {
-  uint32_t b;
-  if (i < kSiluTabMid)
-    b = (static_cast<uint32_t>(i >> 12) << 15) | (static_cast<uint32_t>(((i >> 7) & 31) + kSiluTabE0) << 7) |
-        static_cast<uint32_t>(i & 127);
-  else
-    b = 0x8000u | (134u << 7) | static_cast<uint32_t>(i - kSiluTabMid);
-  return silu_spec(bf16_to_f32(static_cast<uint16_t>(b)));
+// The bf16 gate (bits) of table entry i.
+constexpr uint32_t silu_table_gate(int i) {
+  return i < kSiluTabMid ? (static_cast<uint32_t>(i >> 12) << 15) |
+                               (static_cast<uint32_t>(((i >> 7) & 31) + kSiluTabE0) << 7) |
+                               static_cast<uint32_t>(i & 127)
+                         : 0x8000u | (134u << 7) | static_cast<uint32_t>(i - kSiluTabMid);
+}
+
+// exp_spec and silu_spec for constant evaluation: the same IEEE binary32
+// operations in the same order (a constant expression rounds every
+// operation to nearest-even and never contracts), with rint written as the
+// 1.5 * 2^23 shift (exact round-half-even for |v| < 2^22; here |v| < 128).
+constexpr float exp_spec_cx(float x) {
+  x = x < -86.0f ? -86.0f : (x > 88.0f ? 88.0f : x);
+  const float v = x * 0x1.715476p+0f;
+  const float n = (v + 0x1.8p23f) - 0x1.8p23f;
+  const float r = (x - n * 0x1.62e4p-1f) - n * 0x1.7f7d1cp-20f;
+  float p = 0x1.a01a02p-13f;
+  p = 0x1.6c16c2p-10f + r * p;
+  p = 0x1.111112p-7f + r * p;
+  p = 0x1.555556p-5f + r * p;
+  p = 0x1.555556p-3f + r * p;
+  p = 0.5f + r * p;
+  p = 1.0f + r * p;
+  p = 1.0f + r * p;
+  return p * __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<int>(n) + 127) << 23);
+}
+
+constexpr float silu_spec_cx(float g) { return g / (1.0f + exp_spec_cx(-g)); }
+
+// The first N entries of the table, as a compile-time constant: a kernel
+// reads it from its code object's data (no kernel writes it, so concurrent
+// calls on any streams share it without ordering).
+template <int N>
+struct SiluTable {
+  float v[N];
+};
+
+template <int N>
+constexpr SiluTable<N> make_silu_table() {
+  static_assert(N <= kSiluTabSize, "table size");
+  SiluTable<N> t{};
+  for (int i = 0; i < N; ++i) t.v[i] = silu_spec_cx(__builtin_bit_cast(float, silu_table_gate(i) << 16));
+  return t;
 }
 
 // silu_spec of a bf16 gate (bits in the low 16 bits of gb), from the table.

@@ -2,12 +2,10 @@
 //
 // Both take every SiLU from a lookup table in LDS (a lookup and a few selects
 // instead of an exp polynomial and a divide), which moves them from ALU-bound
-// towards the HBM bound. Each call first runs silu_table_kernel, which writes
-// the 8320 exact silu_spec values of moe_common.h's table into the
-// file-scope array g_silu_tab; the kernels that follow on the same stream copy
-// it into LDS. The array holds constants: a call on another stream that
-// rewrites it concurrently writes the same bits, so no ordering between
-// streams is needed.
+// towards the HBM bound. The 8320 exact silu_spec values of moe_common.h's
+// table are computed at compile time into the constant array g_silu_tab (part
+// of the code object: no launch writes it), and each workgroup copies it into
+// LDS.
 //
 // swiglu_quant_fp8: one 512-thread workgroup per 128x128 block of
 // h = SiLU(gate) * up. Thread (rg, cg) of 32x16 owns rows rg*4..rg*4+3 and
@@ -69,13 +67,8 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return static_cast<uint32_t>(moe::f32_to_bf16(lo)) | (static_cast<uint32_t>(moe::f32_to_bf16(hi)) << 16);
 }
 
-__device__ float g_silu_tab[moe::kSiluTabSize];
-
-__global__ __launch_bounds__(256) void silu_table_kernel() {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= moe::kSiluTabSize) return;
-  g_silu_tab[i] = moe::silu_table_entry(i);
-}
+// The 8320 silu_spec values, evaluated at compile time (code-object data).
+__device__ const moe::SiluTable<moe::kSiluTabSize> g_silu_tab = moe::make_silu_table<moe::kSiluTabSize>();
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -91,7 +84,7 @@ __device__ __forceinline__ void load_silu_table(float* tab, int t, int n) {
   const int lane = t & 63;
   for (int c = (t >> 6) * 64; c < kSiluTabPieces; c += n) {
     const int src = min(c + lane, kSiluTabPieces - 1);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const float4*>(g_silu_tab) + src,
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const float4*>(g_silu_tab.v) + src,
                                      (lds_void_t*)(reinterpret_cast<float4*>(tab) + c), 16, 0, 0);
   }
 }
@@ -449,11 +442,6 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
   }
 }
 
-int launch_silu_table(hipStream_t stream) {
-  silu_table_kernel<<<(moe::kSiluTabSize + 255) / 256, 256, 0, stream>>>();
-  return moe::check_launch("silu_table_kernel");
-}
-
 }  // namespace
 
 extern "C" int swiglu(const uint16_t* gate_up, int64_t M, int F, uint16_t* h, hipStream_t stream) {
@@ -465,8 +453,6 @@ extern "C" int swiglu(const uint16_t* gate_up, int64_t M, int F, uint16_t* h, hi
   if (total >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "swiglu: M*F too large");
   if (!gate_up || !h) return fail(MOE_ERR_INVALID_ARG, "swiglu: null pointer");
   if (!aligned16(gate_up) || !aligned16(h)) return fail(MOE_ERR_INVALID_ARG, "swiglu: pointers not 16-byte aligned");
-  int rc = launch_silu_table(stream);
-  if (rc) return rc;
   const int64_t blocks = ceil_div(total, 256 * kSwigluChunks);
   swiglu_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(reinterpret_cast<const uint4*>(gate_up),
                                                                    static_cast<uint32_t>(total),
@@ -483,18 +469,9 @@ int launch_tile_quant(const uint16_t* x, int64_t M, int K, const int32_t* gs, in
   const int n_fb = K / kTile;
   const int64_t blocks = (m_pad / kTile) * n_fb;
   if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: too many blocks", name);
-  if (SWIGLU) {
-    int rc = launch_silu_table(stream);
-    if (rc) return rc;
-  }
   const unsigned grid = static_cast<unsigned>(blocks);
   const int Mi = static_cast<int>(M), mp = static_cast<int>(m_pad);
-#ifndef MOE_TQ_PAIR
-#define MOE_TQ_PAIR 1
-#endif
-#ifndef MOE_TQ_PAIR_MIN_WGS
-#define MOE_TQ_PAIR_MIN_WGS 1024
-#endif
+  constexpr int kTqPairMinWgs = 1024;
   // Grouped launches: two adjacent column blocks per workgroup, their loads in
   // flight together (with the SwiGLU the second block's transposed codes take
   // their own LDS, the table staying for it): measured faster on every
@@ -502,7 +479,7 @@ int launch_tile_quant(const uint16_t* x, int64_t M, int K, const int32_t* gs, in
   // M x 2048: 0.094 -> 0.105 ms) and keep one block per workgroup, as does a
   // small launch, where halving the grid would leave compute units idle
   // (1024 paired workgroups = 4 per CU).
-  const bool pair = MOE_TQ_PAIR && gs != nullptr && n_fb % 2 == 0 && blocks >= 2 * MOE_TQ_PAIR_MIN_WGS;
+  const bool pair = gs != nullptr && n_fb % 2 == 0 && blocks >= 2 * kTqPairMinWgs;
   const unsigned grid2 = static_cast<unsigned>(blocks / 2);
   // (the per-tile SwiGLU form is unpaired: two of its blocks need more than
   // 128 VGPRs, one workgroup per CU)

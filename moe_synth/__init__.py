@@ -22,6 +22,10 @@ float32 multiply is correctly rounded on any IEEE device. bf16 tensors are
 that float32 value rounded to nearest-even by torch. The arithmetic is written
 in torch int64 ops, so CPU and GPU produce the same bits, and any index range
 of a tensor (one expert's weights, one token's row) can be regenerated alone.
+
+The router logits are the exception: they are drawn from a true normal on the
+host (see router_logits), because the tails decide which experts a biased
+routing reaches.
 """
 from __future__ import annotations
 
@@ -295,8 +299,22 @@ def hidden(cfg: MoEConfig, device="cpu", rows: Optional[slice] = None) -> torch.
 
 
 def router_logits(cfg: MoEConfig, device="cpu", rows: Optional[slice] = None) -> torch.Tensor:
+    """Router logits [T, E] float32 from a true N(0, 1) (rows r0..r1-1 of them).
+
+    Unlike the hashed Irwin-Hall stream of the other tensors, the logits keep a
+    normal's tails: with a per-expert bias, which experts get any tokens at all
+    depends on the rare large logits, and a sum of four uniforms (cut at
+    +-3.46 sigma) would starve the experts the bias ranks low. numpy's PCG64
+    generator, seeded with SeedSequence([workload id, tensor tag]), draws them
+    on the host with `standard_normal(dtype=float32)` (ziggurat), and the bytes
+    are uploaded.
+    The stream is drawn row-major from its start, so the first T rows are the
+    same for every T (a row range is a slice of the rows up to its end).
+    """
     r0, r1 = (0, cfg.T) if rows is None else (rows.start, rows.stop)
-    return normal_f32(tensor_key(cfg.cid, TAG_LOGITS), (r1 - r0, cfg.E), 1.0, device, start=r0 * cfg.E)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.cid, TAG_LOGITS])))
+    z = rng.standard_normal(r1 * cfg.E, dtype=np.float32).reshape(r1, cfg.E)[r0:r1]
+    return torch.from_numpy(np.ascontiguousarray(z)).to(device)
 
 
 def expert_bias(cfg: MoEConfig, device="cpu") -> Optional[torch.Tensor]:

@@ -135,6 +135,31 @@ def test_align_deterministic():
         assert torch.equal(a[key], b[key])
 
 
+@pytest.mark.parametrize("T,k,E,skew", [(262145, 8, 256, True), (300001, 7, 1000, False), (2100000, 1, 3, False)])
+def test_align_large_bit_exact(T, k, E, skew):
+    """Past 2^21 pairs (2049-2051 chunks of 1024 pairs, the last one ragged),
+    against the oracle's tables: the scan over chunks runs in ranges across
+    16 waves, whose boundaries fall inside the chunk sequence."""
+    d = dev()
+    say("align large", T, k, E, skew)
+    rng = np.random.default_rng(T)
+    if skew:
+        # Zipf-like expert popularity: some experts empty, a few very large
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p[rng.choice(E, E // 8, replace=False)] = 0.0
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(64)]).astype(np.int32)
+        ids = ids[rng.integers(0, 64, T)]
+    else:
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32) if E <= 8 else \
+            np.stack([rng.permutation(E)[:k] for _ in range(97)]).astype(np.int32)[rng.integers(0, 97, T)]
+    tb = mx.moe_align(_t(ids, d), E, 128, 128)
+    ref = oracle.dispatch_tables(ids, E, 128, 128)
+    for key in ("group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx",
+                "sorted_pair", "pair_to_row"):
+        assert np.array_equal(host(tb[key]), ref[key]), key
+
+
 # ------------------------------------------------------------- permute --
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3_prefill", "dsv3_prefill"])
@@ -1143,11 +1168,15 @@ def test_forward_fp8(gate_up_fp8, side, shared_fp8):
     assert rel < (0.08 if gate_up_fp8 else 0.05), rel
 
 
-# sampled tokens per workload: each one brings up to k experts' weights to the host
-SAMPLED_TOKENS = {"qwen3_prefill": 21, "dsv3_prefill": 21, "kimi_k2_t32": 3, "kimi_k2_t512": 3, "kimi_k2_t4096": 3}
+# sampled tokens per workload: each one brings up to k experts' weights to the
+# host; None: every token (the whole batch against the oracle's forward)
+SAMPLED_TOKENS = {"qwen3_prefill": None, "dsv3_prefill": None, "kimi_k2_t32": 3, "kimi_k2_t512": 3,
+                  "kimi_k2_t2048": 3, "kimi_k2_t4096": 3}
 
 
-@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_prefill", "kimi_k2_t32", "kimi_k2_t512", "kimi_k2_t4096"])
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_prefill", "kimi_k2_t32", "kimi_k2_t512", "kimi_k2_t2048",
+                                  "kimi_k2_t4096"])
 def test_forward_full_size_sampled_tokens(name):
     d = dev()
     cfg = moe_synth.CONFIGS[name]
@@ -1167,11 +1196,15 @@ def test_forward_full_size_sampled_tokens(name):
                 "pair_to_row"):
         assert np.array_equal(host(bufs.tables[key]), ref_tab[key]), key
     say("  active experts", int((ref_tab["group_sizes"] > 0).sum()), "max rows", int(ref_tab["group_sizes"].max()))
-    tokens = np.unique(np.concatenate([[0, 1, cfg.T - 1],
-                                       np.random.default_rng(cfg.cid).choice(cfg.T, SAMPLED_TOKENS[name])]))
+    if SAMPLED_TOKENS[name] is None:
+        tokens = np.arange(cfg.T)
+    else:
+        tokens = np.unique(np.concatenate([[0, 1, cfg.T - 1],
+                                           np.random.default_rng(cfg.cid).choice(cfg.T, SAMPLED_TOKENS[name])]))
+    say("  oracle on", tokens.size, "tokens")
     ref = oracle_tokens(cfg, inp, tokens)
-    err = assert_bf16_close(bits(out[torch.as_tensor(tokens, device=d)]), ref["out"], f"{name} sampled out")
-    say("  sampled out max abs err", err)
+    err = assert_bf16_close(bits(out[torch.as_tensor(tokens, device=d)]), ref["out"], f"{name} out")
+    say("  out max abs err over", tokens.size, "tokens", err)
     if cfg.shared_F:
         assert_bf16_close(bits(bufs.shared_y[torch.as_tensor(tokens, device=d)]), ref["shared"], "shared")
     # determinism: a second forward gives the same bytes
