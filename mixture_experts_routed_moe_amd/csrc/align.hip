@@ -205,32 +205,18 @@ extern "C" size_t moe_align_workspace_bytes(int64_t numel, int E) {
   return static_cast<size_t>(nchunks) * static_cast<size_t>(E) * sizeof(int32_t);
 }
 
-extern "C" int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_m, int block_m,
-                         int32_t* group_sizes, int32_t* group_offsets, int32_t* group_padded_offsets,
-                         int32_t* group_idx_for_bx, int32_t* sorted_pair, int32_t* pair_to_row,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The three launches on `counts` (nchunks x E int32, fully written by the
+// count kernel before the scan reads it). Arguments checked by the caller.
+int align_launch(const int32_t* topk_ids, int64_t numel, int E, int padding_m, int block_m, int32_t* group_sizes,
+                 int32_t* group_offsets, int32_t* group_padded_offsets, int32_t* group_idx_for_bx,
+                 int32_t* sorted_pair, int32_t* pair_to_row, int32_t* counts, hipStream_t stream) {
   using namespace moe;
-  if (T < 0 || top_k < 1) return fail(MOE_ERR_INVALID_ARG, "moe_align: T=%lld top_k=%d", (long long)T, top_k);
-  if (E < 1 || E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "moe_align: E=%d not in [1,%d]", E, kMaxE);
-  if (block_m <= 0 || padding_m <= 0 || padding_m % block_m != 0)
-    return fail(MOE_ERR_INVALID_ARG, "moe_align: padding_m=%d must be a positive multiple of block_m=%d",
-                padding_m, block_m);
-  const int64_t numel = T * top_k;
-  if (numel >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "moe_align: T*top_k >= 2^31");
   const int64_t m_blocks = moe_num_blocks(numel, E, block_m, padding_m);
-  if (m_blocks * static_cast<int64_t>(block_m) >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "moe_align: padded row space >= 2^31");
-  if (!group_sizes || !group_offsets || !group_padded_offsets || !group_idx_for_bx || !workspace)
-    return fail(MOE_ERR_INVALID_ARG, "moe_align: null pointer");
-  if (numel > 0 && (!topk_ids || !sorted_pair || !pair_to_row))
-    return fail(MOE_ERR_INVALID_ARG, "moe_align: null pointer");
-  if (workspace_bytes < moe_align_workspace_bytes(numel, E))
-    return fail(MOE_ERR_INVALID_ARG, "moe_align: workspace %zu < %zu bytes", workspace_bytes,
-                moe_align_workspace_bytes(numel, E));
   const int nchunks = numel > 0 ? static_cast<int>(ceil_div(numel, kChunk)) : 1;
   int id_bits = 1;
   while ((1 << id_bits) < E) ++id_bits;
-  int32_t* counts = static_cast<int32_t*>(workspace);
   align_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_ids, static_cast<int>(numel), E, counts);
   int rc = check_launch("moe_align(count)");
   if (rc) return rc;
@@ -242,4 +228,45 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, i
       topk_ids, static_cast<int>(numel), E, id_bits, padding_m, block_m, static_cast<int>(m_blocks), counts,
       group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx, sorted_pair, pair_to_row);
   return check_launch("moe_align(rank)");
+}
+
+// Argument checks shared by both entry points (nothing is enqueued on failure).
+int align_check(const char* name, const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_m, int block_m,
+                int32_t* group_sizes, int32_t* group_offsets, int32_t* group_padded_offsets,
+                int32_t* group_idx_for_bx, int32_t* sorted_pair, int32_t* pair_to_row) {
+  using namespace moe;
+  if (T < 0 || top_k < 1) return fail(MOE_ERR_INVALID_ARG, "%s: T=%lld top_k=%d", name, (long long)T, top_k);
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d not in [1,%d]", name, E, kMaxE);
+  if (block_m <= 0 || padding_m <= 0 || padding_m % block_m != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: padding_m=%d must be a positive multiple of block_m=%d", name, padding_m,
+                block_m);
+  const int64_t numel = T * top_k;
+  if (numel >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: T*top_k >= 2^31", name);
+  const int64_t m_blocks = moe_num_blocks(numel, E, block_m, padding_m);
+  if (m_blocks * static_cast<int64_t>(block_m) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: padded row space >= 2^31", name);
+  if (!group_sizes || !group_offsets || !group_padded_offsets || !group_idx_for_bx)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (numel > 0 && (!topk_ids || !sorted_pair || !pair_to_row))
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_m, int block_m,
+                         int32_t* group_sizes, int32_t* group_offsets, int32_t* group_padded_offsets,
+                         int32_t* group_idx_for_bx, int32_t* sorted_pair, int32_t* pair_to_row,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace moe;
+  int rc = align_check("moe_align", topk_ids, T, top_k, E, padding_m, block_m, group_sizes, group_offsets,
+                       group_padded_offsets, group_idx_for_bx, sorted_pair, pair_to_row);
+  if (rc) return rc;
+  const int64_t numel = T * top_k;
+  if (!workspace) return fail(MOE_ERR_INVALID_ARG, "moe_align: null workspace");
+  if (workspace_bytes < moe_align_workspace_bytes(numel, E))
+    return fail(MOE_ERR_INVALID_ARG, "moe_align: workspace %zu < %zu bytes", workspace_bytes,
+                moe_align_workspace_bytes(numel, E));
+  return align_launch(topk_ids, numel, E, padding_m, block_m, group_sizes, group_offsets, group_padded_offsets,
+                      group_idx_for_bx, sorted_pair, pair_to_row, static_cast<int32_t*>(workspace), stream);
 }
