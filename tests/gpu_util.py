@@ -86,4 +86,12 @@ def oracle_tokens(cfg, inp, tokens):
         shared = oracle.shared_expert(hid, bits(inp["shared_w_gate_up"]), bits(inp["shared_w_down"]))
     out = oracle.unpermute(y, tab["pair_to_row"], w, cfg.top_k, cfg.rsf, shared)
     routed = oracle.unpermute(y, tab["pair_to_row"], w, cfg.top_k, cfg.rsf, None)
-    return {"topk_ids": ids, "topk_weights": w, "out": out, "shared": shared, "routed": routed}
+    return {"topk_ids": ids, "topk_weights": w, "out": out, "shared": shared, "routed": routed, "h": h, "y": y,
+            "tables": tab, "w_down_used": wd}
+
+
+def bf16_ulp(bits_arr: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at each element (2^(e-7) in binade [2^e, 2^(e+1)), 2^-133 below 2^-126)."""
+    v = np.abs(nm.bf16_to_f64(bits_arr))
+    _, e = np.frexp(v)
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
