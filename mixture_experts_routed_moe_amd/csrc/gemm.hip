@@ -441,15 +441,14 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
 // ms with four 128 x 128 waves). A wave whose rows are all past the tile's
 // valid rows skips its MFMAs.
 //
-// An expert's last tile often has 128 rows or fewer (an odd block count).
-// Such a "half" tile loads only 128 A rows and splits K between the wave
-// rows: wave rows wm and wm + 2 cover the same 64 rows, the first over the
-// even 16-wide sub-steps, the second over the odd ones, and the two partial
-// sums meet in LDS at the end. A half tile therefore costs about half a full
-// one, and the padding overhead stays that of 128-row blocks.
+// An expert's only or last tile often has 128 rows or fewer (most experts of
+// a skewed routing have a few rows): such a tile loads only 64 or 128 A rows
+// and runs the ring of wide_stage_tile, whose deeper stages keep more of the
+// weight stream in flight; the padding overhead stays that of 64- or
+// 128-row blocks.
 //
 // Loads, fragments and barriers work as in grouped_gemm_pipe_kernel, over
-// the ring described at wide_ring_tile.
+// the rings described at wide_ring_tile and wide_stage_tile.
 constexpr int kWideRows = 256;
 constexpr int kWideW = 256;
 
@@ -512,19 +511,19 @@ struct Ic {
   static constexpr int value = V;
 };
 
-template <bool FUSED, bool HALF, int NW>
+template <bool FUSED, int NW>
 __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ Wb, int64_t m_start, int rows, int nt,
                                                int K, int up_row, int ldc, uint16_t* __restrict__ C,
                                                const int32_t* __restrict__ gather, int gather_k) {
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
-  constexpr int AROWS = HALF ? kWideRows / 2 : kWideRows;
+  constexpr int AROWS = kWideRows;
   constexpr int WM = NW / 2;                         // wave rows (two wave columns)
   constexpr int TM = kWideRows / WM / 32;            // 32-row MFMA tiles per wave
   constexpr int A_LOADS = AROWS / (NW * RPL);        // per wave per step
   constexpr int B_LOADS = kWideW / (NW * RPL);
   constexpr int NS = BK / 16;
-  constexpr int MY_NS = HALF ? NS / 2 : NS;
+  constexpr int MY_NS = NS;
   constexpr int L = A_LOADS + B_LOADS;               // loads issued per step
   constexpr int PER = (L + MY_NS - 1) / MY_NS;
   static_assert(kWideSlotBytes == kWideW * ROWB, "a slot holds one 256-row part");
@@ -565,10 +564,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  // half tiles: wave rows wm and wm + WM/2 cover the same rows, the first
-  // the even sub-steps, the second the odd ones
-  const int kpar = HALF ? (wm >= WM / 2) : 0;
-  const int row0 = (HALF ? wm % (WM / 2) : wm) * TM * 32;
+  const int row0 = wm * TM * 32;
   // 32-row MFMA tiles of this wave that hold valid rows (the others are
   // skipped: with two waves per SIMD the partner wave gets the matrix core)
   const int live_tm = __builtin_amdgcn_readfirstlane(min(TM, max(0, (rows - row0 + 31) / 32)));
@@ -580,7 +576,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   uint32_t a_rd[MY_NS], b_rd[MY_NS];
 #pragma unroll
   for (int i = 0; i < MY_NS; ++i) {
-    const int chunk = (HALF ? 2 * i + kpar : i) * 2 + khalf;
+    const int chunk = i * 2 + khalf;
     a_rd[i] = static_cast<uint32_t>(a_r0 * ROWB + ((chunk ^ wide_swz(a_r0)) << 4));
     b_rd[i] = static_cast<uint32_t>(kWideWRing + b_r0 * ROWB + ((chunk ^ wide_swz(b_r0)) << 4));
     asm volatile("" : "+v"(a_rd[i]), "+v"(b_rd[i]));
@@ -658,12 +654,10 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     if (kt + 5 < nk) step(Ic<2>{}, Ic<1>{}, kt + 5);
   }
 
-  // FUSED: the SiLU table goes into the ring's last 32 KiB (the second W slot,
-  // above the half-tile exchange) once every wave is past its last fragment
-  // read; it lands while the halves meet
+  // FUSED: the SiLU table goes into the ring's last 32 KiB (the second W slot)
+  // once every wave is past its last fragment read
   constexpr int kTabOff = kWideLds - moe::kSiluTabMid * 4;
   if constexpr (FUSED) {
-    static_assert(kTabOff >= 128 * 1024, "the table sits above the exchange");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
     for (int i = 0; i < moe::kSiluTabMid / 4 / (64 * NW); ++i) {
@@ -672,48 +666,8 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     }
   }
 
-  if constexpr (HALF) {
-    // the two K halves meet in LDS (the ring is idle: every load has landed
-    // at the last step's wait): the odd-sub-step waves hand over their sums
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    typedef float floatx4 __attribute__((ext_vector_type(4)));
-    constexpr int XCH = TM * 4 * 4 * 64;                 // floatx4 per wave
-    static_assert(NW / 2 * XCH * 16 <= kWideLds, "exchange fits the ring");
-    floatx4* xch = reinterpret_cast<floatx4*>(smem) + ((wm % (WM / 2)) * 2 + wn) * XCH;
-    if (kpar) {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            floatx4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2], acc[tm][tn][4 * q + 3]};
-            xch[((tm * 4 + tn) * 4 + q) * 64 + lane] = v;
-          }
-    }
-    // (and for this wave's table pieces: after it the table is whole)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kpar) return;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      // one row tile's partial sums at a time, added here (not sunk into the
-      // conditional stores below, which would keep every read live at once)
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const floatx4 v = xch[((tm * 4 + tn) * 4 + q) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[tm][tn][4 * q + e] += v[e];
-        }
-        asm volatile("" : "+v"(acc[tm][tn]));
-      }
-    }
-  }
-
-  // FUSED without the halves: wait for the table (every wave's pieces)
-  if constexpr (FUSED && !HALF) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  // FUSED: wait for the table (every wave's pieces)
+  if constexpr (FUSED) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   const float* tab = reinterpret_cast<const float*>(smem + kTabOff);
   // the SiLUs come from the table unless a gate of this wave needs the direct
   // evaluation (a negative one of magnitude at least 128): one vote per wave,
@@ -750,6 +704,259 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) miss |= silu_tab_misses(moe::f32_to_bf16(acc[tm][tn][r]));
+    if (__builtin_amdgcn_readfirstlane(static_cast<int>(__ballot(miss) != 0)))
+      store(Ic<0>{});
+    else
+      store(Ic<1>{});
+  } else {
+    store(Ic<0>{});
+  }
+}
+
+// Tiles of at most AR = 64 or 128 valid rows (an expert's only or last
+// tile; most experts of a skewed routing have a few rows). What such a tile
+// waits for is its weight slice (256 rows x K) streaming in from HBM: with
+// the full tile's ring (one W step of 32 KiB in flight) a CU pulls about 21
+// GB/s of weights. Here the ring is S equal stages, each the step's AR A
+// rows and its 256 W rows (AR = 64: 40 KiB, four stages; AR = 128: 48 KiB,
+// three stages), and the loads of step kt + S - 1 go into the slot step
+// kt - 1 used, so up to S - 1 steps of weights are in flight.
+//
+// Waves: AR = 64, 2 x 4 (32 rows x 64 W rows each: one MFMA row tile, two
+// column tiles); AR = 128, 2 x 2 waves of 64 rows x 128 W rows, with K split
+// between wave groups (the even and the odd 16-wide sub-steps) and the two
+// partial sums added through LDS at the end (as the full tile's half case
+// did), which halves the fragment reads per MFMA. Fused: a wave's column
+// tiles are gate tiles and the matching up tiles.
+template <int AR>
+struct StageShape;
+template <>
+struct StageShape<64> {
+  static constexpr int TMW = 1, WR = 2, TNW = 2, WC = 4, KS = 1;
+};
+template <>
+struct StageShape<128> {
+  static constexpr int TMW = 2, WR = 2, TNW = 4, WC = 2, KS = 2;
+};
+
+template <bool FUSED, int AR, int NW>
+__device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* __restrict__ A,
+                                                const uint16_t* __restrict__ Wb, int64_t m_start, int rows, int nt,
+                                                int K, int up_row, int ldc, uint16_t* __restrict__ C,
+                                                const int32_t* __restrict__ gather, int gather_k) {
+  using SS = StageShape<AR>;
+  constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
+  constexpr int TMW = SS::TMW, TNW = SS::TNW, WR = SS::WR, WC = SS::WC, KS = SS::KS;
+  constexpr int A_BYTES = AR * ROWB;
+  constexpr int STAGE = A_BYTES + kWideW * ROWB;
+  constexpr int S = kWideLds / STAGE;
+  constexpr int A_LOADS = AR / (NW * RPL);           // per wave per step
+  constexpr int B_LOADS = kWideW / (NW * RPL);
+  constexpr int L = A_LOADS + B_LOADS;
+  constexpr int NS = BK / 16;
+  constexpr int MY_NS = NS / KS;
+  constexpr int PER = (L + MY_NS - 1) / MY_NS;
+  static_assert(WR * WC * KS == NW && WR * TMW * 32 == AR && WC * TNW * 32 == kWideW, "wave layout");
+  static_assert(S >= 3 && S <= 4 && (S - 2) * L <= 63, "ring");
+  static_assert(A_LOADS >= 1 && AR % (NW * RPL) == 0, "A loads");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wc = wave % WC;
+  const int wr = (wave / WC) % WR;
+  const int kpar = wave / (WC * WR);
+  const int lrow = lane / CPR;
+  const int lpos = lane % CPR;
+
+  const char* a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
+  const char* w_base = reinterpret_cast<const char*>(Wb + static_cast<int64_t>(nt) * (FUSED ? kWideW / 2 : kWideW) * K);
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int r = (wave * A_LOADS + i) * RPL + lrow;
+    const int rr = min(r, rows - 1);
+    const uint32_t ar = gather ? static_cast<uint32_t>(gather[m_start + rr] / gather_k) : static_cast<uint32_t>(rr);
+    a_off[i] = ar * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int r = (wave * B_LOADS + i) * RPL + lrow;
+    const int lr = (FUSED && r >= kWideW / 2) ? up_row + (r - kWideW / 2) : r;
+    b_off[i] = static_cast<uint32_t>(lr) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
+  }
+  const int a_lds0 = wave * A_LOADS * RPL * ROWB;
+  const int b_lds0 = A_BYTES + wave * B_LOADS * RPL * ROWB;
+
+  floatx16 acc[TMW][TNW];
+#pragma unroll
+  for (int a = 0; a < TMW; ++a)
+#pragma unroll
+    for (int b = 0; b < TNW; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  const int row0 = wr * TMW * 32;
+  // 32-row MFMA tiles of this wave that hold valid rows (the others are skipped)
+  const int live_tm = __builtin_amdgcn_readfirstlane(min(TMW, max(0, (rows - row0 + 31) / 32)));
+  const int khalf = lane >> 5;
+  const int a_r0 = row0 + (lane & 31);
+  const int b_r0 = wc * (FUSED ? TNW / 2 : TNW) * 32 + (lane & 31);
+  uint32_t a_rd[MY_NS], b_rd[MY_NS];
+#pragma unroll
+  for (int i = 0; i < MY_NS; ++i) {
+    const int chunk = (KS == 2 ? 2 * i + kpar : i) * 2 + khalf;
+    a_rd[i] = static_cast<uint32_t>(a_r0 * ROWB + ((chunk ^ wide_swz(a_r0)) << 4));
+    b_rd[i] = static_cast<uint32_t>(A_BYTES + b_r0 * ROWB + ((chunk ^ wide_swz(b_r0)) << 4));
+    asm volatile("" : "+v"(a_rd[i]), "+v"(b_rd[i]));
+  }
+  // W fragment tn: rows b_r0 + b_frag_row(tn) (fused: the gate tiles, then the matching up tiles)
+  auto b_frag_row = [](int tn) constexpr {
+    return FUSED ? (tn < TNW / 2 ? tn * 32 : kWideW / 2 + (tn - TNW / 2) * 32) : tn * 32;
+  };
+
+  const int nk = K / BK;
+  auto issue = [&](int kt, int slot_base, int first, int count) __attribute__((always_inline)) {
+    const int ko = kt * BK * 2;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      if (j < first || j >= first + count) continue;
+      if (j < B_LOADS)
+        dma16(w_base + ko + b_off[j], smem + slot_base + b_lds0 + j * RPL * ROWB);
+      else
+        dma16(a_base + ko + a_off[j - B_LOADS], smem + slot_base + a_lds0 + (j - B_LOADS) * RPL * ROWB);
+    }
+  };
+  // prologue: steps 0 .. S-2
+  issue(0, 0, 0, L);
+  if (nk > 1) issue(1, STAGE, 0, L);
+  if constexpr (S > 3) {
+    if (nk > 2) issue(2, 2 * STAGE, 0, L);
+  }
+
+  bf16x8_t af[2][TMW], bfr[2][TNW];
+  auto step = [&](auto slot_c, int kt) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr int SL_NEXT = (SL + S - 1) % S;  // step kt + S - 1 reuses the slot of step kt - 1
+    // steps kt+1 .. kt+S-2 (those that exist) may still be in flight
+    const int later = nk - 1 - kt;
+    if (later >= S - 2) wait_dma_barrier<(S - 2) * L>();
+    else wait_dma_barrier_dyn<L, S - 3>(later);
+    auto read_frags = [&](int i, int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tm = 0; tm < TMW; ++tm)
+        af[buf][tm] = *reinterpret_cast<const bf16x8_t*>(smem + a_rd[i] + SL * STAGE + tm * 32 * ROWB);
+#pragma unroll
+      for (int tn = 0; tn < TNW; ++tn)
+        bfr[buf][tn] = *reinterpret_cast<const bf16x8_t*>(smem + b_rd[i] + SL * STAGE + b_frag_row(tn) * ROWB);
+    };
+    const bool ahead = kt + S - 1 < nk;
+    read_frags(0, 0);
+#pragma unroll
+    for (int i = 0; i < MY_NS; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < MY_NS) read_frags(i + 1, (i + 1) & 1);
+#pragma unroll
+      for (int tm = 0; tm < TMW; ++tm) {
+        if (tm >= live_tm) break;  // wave-uniform: this and later row tiles hold no valid rows
+#pragma unroll
+        for (int tn = 0; tn < TNW; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i & 1][tm], bfr[i & 1][tn], acc[tm][tn], 0, 0, 0);
+      }
+      if (ahead) issue(kt + S - 1, SL_NEXT * STAGE, i * PER, PER);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += S) {
+    step(Ic<0>{}, kt);
+    if (kt + 1 < nk) step(Ic<1>{}, kt + 1);
+    if (kt + 2 < nk) step(Ic<2>{}, kt + 2);
+    if constexpr (S > 3) {
+      if (kt + 3 < nk) step(Ic<3>{}, kt + 3);
+    }
+  }
+
+  // FUSED: the SiLU table goes into the ring's last 32 KiB once every wave is
+  // past its last fragment read (above the K-split exchange)
+  constexpr int kTabOff = kWideLds - moe::kSiluTabMid * 4;
+  if constexpr (FUSED) {
+    static_assert(KS == 1 || kTabOff >= 128 * 1024, "the table sits above the exchange");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < moe::kSiluTabMid / 4 / (64 * NW); ++i) {
+      const int c = (i * NW + wave) * 64;
+      dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab.v) + c + lane, smem + kTabOff + c * 16);
+    }
+  }
+  if constexpr (KS == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    typedef float floatx4 __attribute__((ext_vector_type(4)));
+    constexpr int XCH = TMW * TNW * 4 * 64;          // floatx4 per wave
+    static_assert(NW / 2 * XCH * 16 <= 128 * 1024, "exchange fits below the table");
+    floatx4* xch = reinterpret_cast<floatx4*>(smem) + (wr * WC + wc) * XCH;
+    if (kpar) {
+#pragma unroll
+      for (int tm = 0; tm < TMW; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TNW; ++tn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            floatx4 v = {acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2], acc[tm][tn][4 * q + 3]};
+            xch[((tm * TNW + tn) * 4 + q) * 64 + lane] = v;
+          }
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kpar) return;
+#pragma unroll
+    for (int tm = 0; tm < TMW; ++tm) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int tn = 0; tn < TNW; ++tn) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const floatx4 v = xch[((tm * TNW + tn) * 4 + q) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[tm][tn][4 * q + e] += v[e];
+        }
+        asm volatile("" : "+v"(acc[tm][tn]));
+      }
+    }
+  } else if constexpr (FUSED) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  const float* tab = reinterpret_cast<const float*>(smem + kTabOff);
+  auto store = [&](auto use_tab) __attribute__((always_inline)) {
+    constexpr bool TAB = decltype(use_tab)::value != 0;
+#pragma unroll
+    for (int tm = 0; tm < TMW; ++tm) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + tm * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+        if (row >= rows) continue;
+        uint16_t* crow = C + (m_start + row) * ldc;
+        const int col = lane & 31;
+        if (FUSED) {
+#pragma unroll
+          for (int tn = 0; tn < TNW / 2; ++tn) {
+            const uint16_t gb = moe::f32_to_bf16(acc[tm][tn][r]);
+            const uint16_t ub = moe::f32_to_bf16(acc[tm][tn + TNW / 2][r]);
+            crow[nt * (kWideW / 2) + wc * (TNW / 2) * 32 + tn * 32 + col] =
+                TAB ? moe::f32_to_bf16(silu_tab(tab, gb) * moe::bf16_to_f32(ub)) : moe::swiglu_bf16(gb, ub);
+          }
+        } else {
+#pragma unroll
+          for (int tn = 0; tn < TNW; ++tn)
+            crow[nt * kWideW + wc * TNW * 32 + tn * 32 + col] = moe::f32_to_bf16(acc[tm][tn][r]);
+        }
+      }
+    }
+  };
+  if constexpr (FUSED) {
+    bool miss = false;
+#pragma unroll
+    for (int tm = 0; tm < TMW; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TNW / 2; ++tn)
 #pragma unroll
         for (int r = 0; r < 16; ++r) miss |= silu_tab_misses(moe::f32_to_bf16(acc[tm][tn][r]));
     if (__builtin_amdgcn_readfirstlane(static_cast<int>(__ballot(miss) != 0)))
@@ -875,10 +1082,12 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
   if (r <= 0) return;
   const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
-  if (rows <= kWideRows / 2)
-    wide_ring_tile<FUSED, true, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+  if (rows <= 64)
+    wide_stage_tile<FUSED, 64, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+  else if (rows <= kWideRows / 2)
+    wide_stage_tile<FUSED, 128, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
   else
-    wide_ring_tile<FUSED, false, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+    wide_ring_tile<FUSED, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
 }
 
 // Group shape for the tile order: GN column tiles (a divisor of n_tiles, at
@@ -1238,10 +1447,11 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
   // ldc is the output width: F for the fused gate_up, 2F or H otherwise
   const int pipe_cols = FUSED ? kPipeBNW / 2 : kPipeBNW;
-  // 256-row tiles pay off once experts average a full 128-row block (at
-  // fewer rows per expert nearly every tile is a half tile and the 128-row
-  // kernel, with less fixed cost per tile, is faster)
-  constexpr int kWideMinRows = 128;
+  // Grouped launches take the 256-row kernel whatever the rows per expert:
+  // an expert's tile of at most 64 or 128 rows runs a ring of deeper stages
+  // (wide_stage_tile), which beat the 128-row kernel on the decode-like
+  // shapes too (interleaved: Kimi-K2 T = 512 gate_up 3.64 -> 3.59 ms, down
+  // 2.09 -> 1.97 ms; Qwen3 decode 0.201 -> 0.189 / 0.094 -> 0.089 ms)
   // few rows (at most 4 in one dense group, or numel <= E / 10 over the
   // experts: one decode token's top-k): the weight-streaming kernel (at 256
   // rows over 384 experts the row-tile kernels are faster)
@@ -1258,8 +1468,7 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   constexpr int kWideDenseMinTiles = 128;
   // a dense launch with few 256-row tiles: the 128-row kernel gives it twice the workgroups
   const bool dense_few = tb.gs == nullptr && moe::ceil_div(numel, kWideRows) * (ldc / pipe_cols) < kWideDenseMinTiles;
-  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits && !dense_few &&
-      numel >= static_cast<int64_t>(kWideMinRows) * E)
+  if (block_m == kPipeBM && ldc % pipe_cols == 0 && K % 64 == 0 && wide_fits && !dense_few)
     return launch_wide<FUSED>(A, W, tb, E, numel, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
   if (block_m == kPipeBM && ldc % pipe_cols == 0)
     return launch_pipe<FUSED>(A, W, tb, numel, m_blocks, ldc / pipe_cols, K, w_stride, up_row, ldc, C, stream, name);
