@@ -86,8 +86,8 @@ def oracle_tokens(cfg, inp, tokens):
         shared = oracle.shared_expert(hid, bits(inp["shared_w_gate_up"]), bits(inp["shared_w_down"]))
     out = oracle.unpermute(y, tab["pair_to_row"], w, cfg.top_k, cfg.rsf, shared)
     routed = oracle.unpermute(y, tab["pair_to_row"], w, cfg.top_k, cfg.rsf, None)
-    return {"topk_ids": ids, "topk_weights": w, "out": out, "shared": shared, "routed": routed, "h": h, "y": y,
-            "tables": tab, "w_down_used": wd}
+    return {"topk_ids": ids, "topk_weights": w, "out": out, "shared": shared, "routed": routed, "gate_up": gu,
+            "h": h, "y": y, "tables": tab, "w_down_used": wd}
 
 
 def bf16_ulp(bits_arr: np.ndarray) -> np.ndarray:

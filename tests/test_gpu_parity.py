@@ -1169,29 +1169,39 @@ def test_forward_fp8(gate_up_fp8, side, shared_fp8):
     assert rel < (0.08 if gate_up_fp8 else 0.05), rel
 
 
-def _full_batch_checks(cfg, bufs, out, ref):
+def _full_batch_checks(cfg, inp, bufs, out, ref):
     """The whole batch against the oracle: each stage on the GPU's own input to
-    that stage (every element within atol = rtol = 1e-2), then the output
-    against the oracle's independent forward.
+    that stage (bf16 results within atol = rtol = 1e-2 on every element, the
+    SwiGLU byte for byte), then the output against the oracle's independent
+    forward.
 
     With every token present, the oracle's compact rows (its experts are the
     reached ones, in ascending id) are the GPU's rows. End to end, the two
-    sides round three bf16 tensors (g and u, h, y) from differently ordered
-    sums (fp32 on the GPU, fp64 in the oracle), so a value that lands within
-    an accumulation error of a bf16 rounding boundary rounds to neighbouring
-    bf16 values on the two sides; the unpermute scales a y difference by
-    rsf * w (up to 2.827 here) before the output's own rounding. So an output
-    element may leave atol + rtol*|ref| only by what the unpermute's
-    linearity gives for the y differences, rsf * sum_j w_j |dy_j|, plus one
-    ulp of the output for its rounding; the y differences themselves are
-    bounded by the down-projection stage check.
+    sides round g and u, h and y to bf16 from differently ordered sums (fp32
+    on the GPU, fp64 in the oracle), so a value within an accumulation error
+    of a bf16 rounding boundary rounds to neighbouring bf16 values on the two
+    sides, and a later stage scales the difference (the SwiGLU by silu(g) or
+    u, the unpermute by rsf * w, rsf up to 2.827 here). So an output element
+    may leave atol + rtol*|ref| only by what the unpermute's linearity gives
+    for the y and weight differences, rsf * sum_j (w_j |dy_j| + |dw_j| |y_j|)
+    plus the shared output's difference, plus one ulp of the output for its
+    rounding; the y differences themselves are bounded by the stage checks.
     """
     h_gpu, y_gpu = bits(bufs.h), bits(bufs.y)
     assert h_gpu.shape == ref["h"].shape and y_gpu.shape == ref["y"].shape
     tab = ref["tables"]
-    # stage: gate_up + SwiGLU from the hidden states (no GPU input)
-    err = assert_bf16_close(h_gpu, ref["h"], f"{cfg.name} h")
-    say("  h max abs err", err)
+    d = bufs.h.device
+    # stage: the gate_up GEMM (unfused, gathering the hidden states) against the oracle's
+    gu = mx.grouped_gemm_gate_up_gather(inp["hidden"], inp["w_gate_up"], bufs.tables, cfg.top_k, cfg.padding_m,
+                                        cfg.block_m, False)
+    gu_gpu = bits(gu)
+    del gu
+    err = assert_bf16_close(gu_gpu, ref["gate_up"], f"{cfg.name} gate_up")
+    say("  gate_up max abs err", err)
+    # stage: the SwiGLU fused into the forward's gate_up, byte for byte on the GPU's g|u
+    h_spec = oracle.swiglu(gu_gpu, cfg.F)
+    assert np.array_equal(h_gpu, h_spec), f"{cfg.name}: {int((h_gpu != h_spec).sum())} h values differ"
+    del gu_gpu, h_spec
     # stage: down projection of the GPU's h
     y_from_h = oracle.grouped_gemm(h_gpu, ref["w_down_used"], tab["group_sizes"], tab["group_offsets"])
     err = assert_bf16_close(y_gpu, y_from_h, f"{cfg.name} y from the GPU's h")
@@ -1205,23 +1215,33 @@ def _full_batch_checks(cfg, bufs, out, ref):
     err = assert_bf16_close(out_gpu, out_from_y, f"{cfg.name} out from the GPU's y")
     say("  out (from the GPU's y) max abs err", err)
     # end to end, against the oracle's own forward
-    g, r = nm.bf16_to_f64(out_gpu), nm.bf16_to_f64(ref["out"])
+    _assert_within_propagated(cfg, out_gpu, ref["out"], y_gpu, ref, w, tab, shared_gpu, "out")
+
+
+def _assert_within_propagated(cfg, got_bits, ref_bits, y_gpu, ref, w, tab, shared_gpu, what):
+    """got against the oracle's forward output: within atol + rtol*|ref| on all
+    but at most 1e-5 of the elements, and every element within that plus the
+    unpermute's propagation of the y and weight differences (plus the shared
+    output's difference when it joined) plus one output ulp."""
+    g, r = nm.bf16_to_f64(got_bits), nm.bf16_to_f64(ref_bits)
     diff = np.abs(g - r)
     tol = BF16_ATOL + BF16_RTOL * np.abs(r)
     outside = diff > tol
     rows = np.asarray(tab["pair_to_row"], np.int64).reshape(cfg.T, cfg.top_k)
     prop = np.zeros_like(g)
     rsf = float(np.float32(cfg.rsf))
+    dw = np.abs(w.astype(np.float64) - ref["topk_weights"].astype(np.float64))
     for j in range(cfg.top_k):
-        dy = np.abs(nm.bf16_to_f64(y_gpu[rows[:, j]]) - nm.bf16_to_f64(ref["y"][rows[:, j]]))
-        prop += rsf * w[:, j:j + 1].astype(np.float64) * dy
-    if cfg.shared_F:
+        yg = nm.bf16_to_f64(y_gpu[rows[:, j]])
+        dy = np.abs(yg - nm.bf16_to_f64(ref["y"][rows[:, j]]))
+        prop += rsf * (w[:, j:j + 1].astype(np.float64) * dy + dw[:, j:j + 1] * np.abs(yg))
+    if shared_gpu is not None:
         prop += np.abs(nm.bf16_to_f64(shared_gpu) - nm.bf16_to_f64(ref["shared"]))
-    bound = tol + prop + bf16_ulp(ref["out"])
+    bound = tol + prop + bf16_ulp(ref_bits)
     bad = diff > bound
-    say("  out vs the oracle's forward: max abs err", float(diff.max()), "outside atol/rtol:", int(outside.sum()),
-        "of", diff.size, "(all within the propagated bound)" if not bad.any() else "")
-    assert not bad.any(), (f"{int(bad.sum())} outputs beyond the propagated bound; first "
+    say(f"  {what} vs the oracle's forward: max abs err", float(diff.max()), "outside atol/rtol:",
+        int(outside.sum()), "of", diff.size, "(all within the propagated bound)" if not bad.any() else "")
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond the propagated bound; first "
                            f"{np.argwhere(bad)[:5].tolist()}")
     assert outside.sum() <= 1e-5 * diff.size, int(outside.sum())
 
@@ -1262,7 +1282,7 @@ def test_forward_full_size_sampled_tokens(name):
     say("  oracle on", tokens.size, "tokens")
     ref = oracle_tokens(cfg, inp, tokens)
     if SAMPLED_TOKENS[name] is None:
-        _full_batch_checks(cfg, bufs, out, ref)
+        _full_batch_checks(cfg, inp, bufs, out, ref)
     else:
         err = assert_bf16_close(bits(out[torch.as_tensor(tokens, device=d)]), ref["out"], f"{name} out")
         say("  out max abs err over", tokens.size, "tokens", err)
@@ -1285,5 +1305,9 @@ def test_forward_full_size_sampled_tokens(name):
         # the split of the partial-output contract: shared part and routed part, added by the caller
         shared, routed = _gpu_forward(cfg, inp, return_parts=True)
         assert torch.equal(shared, bufs.shared_y)
-        sel = torch.as_tensor(tokens, device=d)
-        assert_bf16_close(bits(routed[sel]), ref["routed"], f"{name} routed part")
+        if SAMPLED_TOKENS[name] is None:
+            _assert_within_propagated(cfg, bits(routed), ref["routed"], bits(bufs.y), ref, host(bufs.topk_weights),
+                                      ref["tables"], None, "routed part")
+        else:
+            sel = torch.as_tensor(tokens, device=d)
+            assert_bf16_close(bits(routed[sel]), ref["routed"], f"{name} routed part")
