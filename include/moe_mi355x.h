@@ -116,6 +116,27 @@ int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_
               int32_t* group_idx_for_bx, int32_t* sorted_pair, int32_t* pair_to_row,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* moe_align for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same tables, bytes and launches as moe_align, with the chunk histogram in
+ * a static per-device array of the library (moe_align_noalloc_max_scratch_bytes()
+ * bytes, 4 MiB, held on each GPU the library runs on until the process
+ * ends) instead of a caller workspace. It calls no allocating routine; its
+ * first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress). Every call on one GPU shares the array: calls that
+ * overlap on one GPU (two streams, two threads) race and give wrong tables.
+ * The stream must belong to the current device (MOE_ERR_INVALID_ARG
+ * otherwise). Pair counts whose histogram, moe_align_workspace_bytes(T*top_k,
+ * E), exceeds the array are refused with MOE_ERR_UNSUPPORTED before anything
+ * is enqueued (at E = 256 up to 4,194,304 pairs). Other limits and errors as
+ * moe_align. */
+int moe_align_noalloc(const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_m, int block_m,
+                      int32_t* group_sizes, int32_t* group_offsets, int32_t* group_padded_offsets,
+                      int32_t* group_idx_for_bx, int32_t* sorted_pair, int32_t* pair_to_row, hipStream_t stream);
+
+/* Size in bytes of moe_align_noalloc's static scratch array. */
+size_t moe_align_noalloc_max_scratch_bytes(void);
+
 /* Token permute into the compact expert-major layout (TileOPs "MoePermuteAlignOp":
  * token routing for the grouped GEMM):
  *     x_perm[r, :] = hidden[sorted_pair[r] / top_k, :]

@@ -32,7 +32,7 @@ class MoeError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 SCORING = {"softmax": 0, "sigmoid": 1}
 
 
@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
         "moe_align_workspace_bytes": (SZ, [I64, I]),
         "moe_topk_softmax": (I, [P, P, I64, I, I, I, I, P, P, P]),
         "moe_align": (I, [P, I64, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
+        "moe_align_noalloc": (I, [P, I64, I, I, I, I, P, P, P, P, P, P, P]),
+        "moe_align_noalloc_max_scratch_bytes": (SZ, []),
         "moe_permute": (I, [P, P, P, I64, I, I, P, P]),
         "grouped_gemm_gate_up": (I, [P, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
         "grouped_gemm_gate_up_gather": (I, [P, I64, P, I, P, P, P, P, P, I64, I, I, I, I, I, I, P, P]),
@@ -79,7 +81,8 @@ EXPORTS = ("moe_last_error", "moe_abi_version", "moe_num_blocks", "moe_align_wor
            "moe_topk_softmax", "moe_align", "moe_permute", "grouped_gemm_gate_up",
            "grouped_gemm_gate_up_gather", "swiglu",
            "grouped_gemm_down", "moe_unpermute", "swiglu_quant_fp8", "tile_quant_fp8",
-           "tile_quant_fp8_m_pad_bound", "fp8_block_quant_weights", "grouped_gemm_fp8", "grouped_gemm_gate_up_fp8")
+           "tile_quant_fp8_m_pad_bound", "fp8_block_quant_weights", "grouped_gemm_fp8", "grouped_gemm_gate_up_fp8",
+           "moe_align_noalloc", "moe_align_noalloc_max_scratch_bytes")
 
 
 def lib() -> ctypes.CDLL:
@@ -177,6 +180,27 @@ def moe_align(topk_ids: torch.Tensor, E: int, padding_m: int, block_m: int,
           _ptr(tb["group_idx_for_bx"], i32, "group_idx_for_bx"), _ptr(tb["sorted_pair"], i32, "sorted_pair"),
           _ptr(tb["pair_to_row"], i32, "pair_to_row"), ws.data_ptr(), ws.numel(), _stream(topk_ids))
     return tb
+
+
+def moe_align_noalloc(topk_ids: torch.Tensor, E: int, padding_m: int, block_m: int,
+                      tables: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """moe_align without a workspace: the library's static per-device scratch
+    holds the chunk histogram (calls that overlap on one GPU race; pair counts
+    whose histogram exceeds moe_align_noalloc_max_scratch_bytes() are refused).
+    With `tables` given, nothing is allocated."""
+    T, k = topk_ids.shape
+    tb = tables if tables is not None else alloc_tables(T * k, E, padding_m, block_m, topk_ids.device)
+    i32 = torch.int32
+    _call("moe_align_noalloc", _ptr(topk_ids, i32, "topk_ids"), T, k, E, padding_m, block_m,
+          _ptr(tb["group_sizes"], i32, "group_sizes"), _ptr(tb["group_offsets"], i32, "group_offsets"),
+          _ptr(tb["group_padded_offsets"], i32, "group_padded_offsets"),
+          _ptr(tb["group_idx_for_bx"], i32, "group_idx_for_bx"), _ptr(tb["sorted_pair"], i32, "sorted_pair"),
+          _ptr(tb["pair_to_row"], i32, "pair_to_row"), _stream(topk_ids))
+    return tb
+
+
+def moe_align_noalloc_max_scratch_bytes() -> int:
+    return int(lib().moe_align_noalloc_max_scratch_bytes())
 
 
 def moe_permute(hidden: torch.Tensor, sorted_pair: Optional[torch.Tensor], top_k: int, out=None,

@@ -21,6 +21,8 @@
 //             follow pair order, never the order in which atomics complete.
 // Chunk 0 also writes group_offsets, group_padded_offsets and
 // group_idx_for_bx.
+#include <mutex>
+
 #include "moe_common.h"
 
 namespace {
@@ -269,4 +271,75 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t T, int top_k, int E, i
                 moe_align_workspace_bytes(numel, E));
   return align_launch(topk_ids, numel, E, padding_m, block_m, group_sizes, group_offsets, group_padded_offsets,
                       group_idx_for_bx, sorted_pair, pair_to_row, static_cast<int32_t*>(workspace), stream);
+}
+
+// ---------------------------------------------------------------------------
+// moe_align_noalloc: moe_align with its histogram in a file-scope device
+// array instead of a caller workspace, for callers that cannot allocate.
+// Every GPU holds its own copy of the array (for as long as the process
+// runs); host code reaches it only through the address hipGetSymbolAddress
+// returns for that device, looked up once per device on its first call (the
+// array's name in host code is a host-side stand-in, not a device address).
+// The count launch writes every entry the later launches read, so nothing
+// needs clearing between calls; concurrent calls on one GPU share the array
+// and race.
+namespace {
+
+constexpr size_t kAlignScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) int32_t scratch[kAlignScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the stream's device (the current device).
+int scratch_for_stream(hipStream_t stream, int32_t** out) {
+  using namespace moe;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "moe_align_noalloc: hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "moe_align_noalloc: device %d", dev);
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess)
+      return fail(MOE_ERR_INVALID_ARG, "moe_align_noalloc: hipStreamGetDevice failed");
+    if (sdev != dev)
+      return fail(MOE_ERR_INVALID_ARG, "moe_align_noalloc: the stream is on device %d, the current device is %d",
+                  static_cast<int>(sdev), dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_HIP, "moe_align_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" size_t moe_align_noalloc_max_scratch_bytes(void) { return kAlignScratchBytes; }
+
+extern "C" int moe_align_noalloc(const int32_t* topk_ids, int64_t T, int top_k, int E, int padding_m, int block_m,
+                                 int32_t* group_sizes, int32_t* group_offsets, int32_t* group_padded_offsets,
+                                 int32_t* group_idx_for_bx, int32_t* sorted_pair, int32_t* pair_to_row,
+                                 hipStream_t stream) {
+  using namespace moe;
+  int rc = align_check("moe_align_noalloc", topk_ids, T, top_k, E, padding_m, block_m, group_sizes, group_offsets,
+                       group_padded_offsets, group_idx_for_bx, sorted_pair, pair_to_row);
+  if (rc) return rc;
+  const int64_t numel = T * top_k;
+  const size_t need = moe_align_workspace_bytes(numel, E);
+  if (need > kAlignScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_align_noalloc: T*top_k=%lld pairs over E=%d experts need %zu bytes of scratch, the static "
+                "array holds %zu (use moe_align with a workspace)",
+                static_cast<long long>(numel), E, need, kAlignScratchBytes);
+  int32_t* counts = nullptr;
+  rc = scratch_for_stream(stream, &counts);
+  if (rc) return rc;
+  return align_launch(topk_ids, numel, E, padding_m, block_m, group_sizes, group_offsets, group_padded_offsets,
+                      group_idx_for_bx, sorted_pair, pair_to_row, counts, stream);
 }
