@@ -454,10 +454,11 @@ constexpr int kWideW = 256;
 
 // The wide tile's K loop, K step 64 (whole 128-byte rows, so every L1 -> L2
 // request moves a full line). The A part and the W part of a step are 32 KiB
-// each; A(kt) goes to A slot kt % 3 and W(kt) to W slot kt % 2 (LDS: three A
-// slots, then two W slots, 160 KiB). During step kt the loads of W(kt+1) and
-// A(kt+2) go into the slots steps kt-1 used, and the wait at the top of step
-// kt+1 leaves A(kt+2) in flight: between one and three 32 KiB parts are in
+// each; the operand with three slots (the weights, see kWideWDeep) is loaded
+// two steps ahead and the other, with two slots, one step ahead (LDS: the A
+// slots, then the W slots, 160 KiB). During step kt the loads of A(kt+1) and
+// W(kt+2) go into the slots steps kt-1 used, and the wait at the top of step
+// kt+1 leaves W(kt+2) in flight: between one and three 32 KiB parts are in
 // flight at any time and the ring never drains.
 //
 // The loop is unrolled over the six steps after which both slot sequences
@@ -478,8 +479,13 @@ constexpr int kWideW = 256;
 __device__ __forceinline__ int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 constexpr int kWideSlotBytes = kWideRows * 128;
-constexpr int kWideASlots = 3;
-constexpr int kWideWSlots = 2;
+// The operand with three slots is loaded two steps ahead, the other one step:
+// the weights, the stream that comes from HBM (interleaved against three A
+// slots: routed gate_up 2.828 -> 2.770 ms on the DeepSeek-V3 routing, Qwen3
+// prefill 0.343 -> 0.336 ms, aligned GLM-5 shapes 1-2% faster; same bytes).
+constexpr bool kWideWDeep = true;
+constexpr int kWideASlots = kWideWDeep ? 2 : 3;
+constexpr int kWideWSlots = kWideWDeep ? 3 : 2;
 constexpr int kWideWRing = kWideASlots * kWideSlotBytes;  // first W slot
 constexpr int kWideLds = (kWideASlots + kWideWSlots) * kWideSlotBytes;
 
@@ -585,23 +591,37 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   constexpr int kBFragRow[4] = {0, 32, FUSED ? kWideW / 2 : 64, FUSED ? kWideW / 2 + 32 : 96};
 
   const int nk = K / BK;
-  // prologue: A(0), W(0), A(1)
+  // the operand with three slots runs two steps ahead (its loads are issued
+  // last in a step), the other one step ahead
+  constexpr int FIRST = kWideWDeep ? A_LOADS : B_LOADS;   // loads of the one-ahead operand
+  constexpr int LAST = kWideWDeep ? B_LOADS : A_LOADS;    // loads of the two-ahead operand
+  auto load_a = [&](int kt, int slot, int i) __attribute__((always_inline)) {
+    dma16(a_base + kt * BK * 2 + a_off[i], smem + a_lds0 + slot * kWideSlotBytes + i * RPL * ROWB);
+  };
+  auto load_w = [&](int kt, int slot, int i) __attribute__((always_inline)) {
+    dma16(w_base + kt * BK * 2 + b_off[i], smem + b_lds0 + slot * kWideSlotBytes + i * RPL * ROWB);
+  };
+  // prologue: A(0), W(0), then step 1 of the two-ahead operand
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) dma16(a_base + a_off[i], smem + a_lds0 + i * RPL * ROWB);
+  for (int i = 0; i < A_LOADS; ++i) load_a(0, 0, i);
 #pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) dma16(w_base + b_off[i], smem + b_lds0 + i * RPL * ROWB);
+  for (int i = 0; i < B_LOADS; ++i) load_w(0, 0, i);
   if (nk > 1) {
+    if constexpr (kWideWDeep) {
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      dma16(a_base + BK * 2 + a_off[i], smem + kWideSlotBytes + a_lds0 + i * RPL * ROWB);
+      for (int i = 0; i < B_LOADS; ++i) load_w(1, 1, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) load_a(1, 1, i);
+    }
   }
 
   bf16x8_t af[2][TM], bfr[2][4];
   auto step = [&](auto sa, auto sw, int kt) __attribute__((always_inline)) {
     constexpr int SA = decltype(sa)::value, SW = decltype(sw)::value;
-    constexpr int A_NEXT = (SA + 2) % kWideASlots, W_NEXT = (SW + 1) % kWideWSlots;
-    // every load except A(kt+1) (the last issued) must have landed
-    if (kt + 1 < nk) wait_dma_barrier<A_LOADS>();
+    constexpr int A_NEXT = (SA + kWideASlots - 1) % kWideASlots, W_NEXT = (SW + kWideWSlots - 1) % kWideWSlots;
+    // every load except step kt+1 of the two-ahead operand (the last issued) must have landed
+    if (kt + 1 < nk) wait_dma_barrier<LAST>();
     else wait_dma_barrier<0>();
     auto read_frags = [&](int i, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -612,8 +632,6 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
         bfr[buf][tn] =
             *reinterpret_cast<const bf16x8_t*>(smem + b_rd[i] + SW * kWideSlotBytes + kBFragRow[tn] * ROWB);
     };
-    const char* w_src = w_base + (kt + 1) * BK * 2;
-    const char* a_src = a_base + (kt + 2) * BK * 2;
     read_frags(0, 0);
 #pragma unroll
     for (int i = 0; i < MY_NS; ++i) {
@@ -629,16 +647,20 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
         for (int tn = 0; tn < 4; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i & 1][tm], bfr[i & 1][tn], acc[tm][tn], 0, 0, 0);
       }
-      // this sub-step's share of the loads for W(kt+1), then A(kt+2)
+      // this sub-step's share of the loads: step kt+1 of the one-ahead
+      // operand, then step kt+2 of the two-ahead one
 #pragma unroll
       for (int j = i * PER; j < i * PER + PER && j < L; ++j) {
-        if (j < B_LOADS) {
-          if (kt + 1 < nk)
-            dma16(w_src + b_off[j], smem + b_lds0 + W_NEXT * kWideSlotBytes + j * RPL * ROWB);
+        if (j < FIRST) {
+          if (kt + 1 < nk) {
+            if constexpr (kWideWDeep) load_a(kt + 1, A_NEXT, j);
+            else load_w(kt + 1, W_NEXT, j);
+          }
         } else {
-          if (kt + 2 < nk)
-            dma16(a_src + a_off[j - B_LOADS],
-                  smem + a_lds0 + A_NEXT * kWideSlotBytes + (j - B_LOADS) * RPL * ROWB);
+          if (kt + 2 < nk) {
+            if constexpr (kWideWDeep) load_w(kt + 2, W_NEXT, j - FIRST);
+            else load_a(kt + 2, A_NEXT, j - FIRST);
+          }
         }
       }
     }
@@ -647,14 +669,14 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   // guarded, so the loop has a single exit
   for (int kt = 0; kt < nk; kt += 6) {
     step(Ic<0>{}, Ic<0>{}, kt);
-    if (kt + 1 < nk) step(Ic<1>{}, Ic<1>{}, kt + 1);
-    if (kt + 2 < nk) step(Ic<2>{}, Ic<0>{}, kt + 2);
-    if (kt + 3 < nk) step(Ic<0>{}, Ic<1>{}, kt + 3);
-    if (kt + 4 < nk) step(Ic<1>{}, Ic<0>{}, kt + 4);
-    if (kt + 5 < nk) step(Ic<2>{}, Ic<1>{}, kt + 5);
+    if (kt + 1 < nk) step(Ic<1 % kWideASlots>{}, Ic<1 % kWideWSlots>{}, kt + 1);
+    if (kt + 2 < nk) step(Ic<2 % kWideASlots>{}, Ic<2 % kWideWSlots>{}, kt + 2);
+    if (kt + 3 < nk) step(Ic<3 % kWideASlots>{}, Ic<3 % kWideWSlots>{}, kt + 3);
+    if (kt + 4 < nk) step(Ic<4 % kWideASlots>{}, Ic<4 % kWideWSlots>{}, kt + 4);
+    if (kt + 5 < nk) step(Ic<5 % kWideASlots>{}, Ic<5 % kWideWSlots>{}, kt + 5);
   }
 
-  // FUSED: the SiLU table goes into the ring's last 32 KiB (the second W slot)
+  // FUSED: the SiLU table goes into the ring's last 32 KiB (the last W slot)
   // once every wave is past its last fragment read
   constexpr int kTabOff = kWideLds - moe::kSiluTabMid * 4;
   if constexpr (FUSED) {

@@ -21,7 +21,6 @@ namespace {
 
 constexpr int kT = 128;                                  // tile edge and scale block
 constexpr int kF8Threads = 256;                          // four waves, 2 x 2, each 64 x 64
-constexpr int kF8StageBytes = 2 * kT * kT + kT * 4;      // A rows, W rows, A row scales
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -97,56 +96,75 @@ __global__ __launch_bounds__(256) void block_quant_kernel(const uint16_t* __rest
 
 // One workgroup per (128-row block bx of the padded expert-major row space,
 // 128-row weight tile nt). K advances 128 bytes (one scale block) per step;
-// the A rows, the W rows and the 128 A row scales of step kb+1 load
-// (direct-to-LDS) into the other half of a two-stage buffer while step kb
-// computes. A rows past the block's valid rows are read from its last row and
-// never stored. With a gather table (tb.gather) compact row r of A and of its
-// scales is row gather[r] / gather_k of qa and sa (the token's codes).
+// the A rows, the W rows and the A row scales of a step load direct-to-LDS
+// into a ring of S stages. A block with more than 64 valid rows (AR = 128)
+// has two stages of 33 KiB: step kb+1 loads while step kb computes. A block
+// of at most 64 rows (an expert's only or last block; most experts of a
+// skewed routing have a few rows) only streams its weights, so it takes the
+// ring for 64 A rows: three stages of 24 KiB, two steps of weights in flight
+// (two workgroups per CU: 73 KiB of LDS each). A rows past the block's valid
+// rows are read from its last row and never stored. With a gather table
+// (tb.gather) compact row r of A and of its scales is row gather[r] /
+// gather_k of qa and sa (the token's codes).
 // FUSED (gate_up with SwiGLU): the tile's weight rows are 64 gate rows
 // nt*64.. and the matching 64 up rows up_row + nt*64..; a wave's first
 // 32-row MFMA block is gate, its second the matching up block, so one lane
 // holds both halves of each output and the epilogue stores
 // SwiGLU(bf16(gate), bf16(up)) into the 64 output columns nt*64.. of y.
-template <bool FUSED>
-__global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
-    const float* __restrict__ sw, moe::Tables tb, int64_t numel, int n_tiles, int N, int K,
-    int up_row, int ldc, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kF8StageBytes];
-  // Row-major tile order. The hardware hands workgroup w to XCD w % 8, so with
-  // n_tiles a multiple of 8 (56 and 32 on the DeepSeek-V3 shapes) column tile
-  // nt of every row block lands on XCD nt % 8: each XCD's L2 holds one eighth
-  // of every expert's weights, which are most of the bytes, while the much
-  // smaller activation codes are read by all eight.
-  const int bx = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
-  int g, rows;
-  int64_t m_start;
-  moe::decode_block(tb, bx, kT, numel, g, m_start, rows);
-  if (rows == 0) return;
+template <int AR>
+struct F8Ring {
+  static constexpr int S = AR == 128 ? 2 : 3;                      // stages
+  static constexpr int A_BYTES = AR * kT;
+  static constexpr int STAGE = A_BYTES + kT * kT + AR * 4;         // A rows, W rows, A row scales
+};
+// every wave issues one 4-byte scale load per step (so every wave's count of
+// loads per step is the same); the waves past the scales load a copy of the
+// first scales into a scratch area of their own
+constexpr int kF8Scratch = 4 * 64 * 4;
+constexpr int kF8Lds = (2 * F8Ring<128>::STAGE > 3 * F8Ring<64>::STAGE ? 2 * F8Ring<128>::STAGE
+                                                                        : 3 * F8Ring<64>::STAGE) + kF8Scratch;
+static_assert(2 * kF8Lds <= 160 * 1024, "two workgroups per CU");
 
+template <bool FUSED, int AR>
+__device__ __forceinline__ void fp8_tile(uint8_t* smem, const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                         const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+                                         const moe::Tables& tb, int g, int64_t m_start, int rows, int nt, int N,
+                                         int K, int up_row, int ldc, uint16_t* __restrict__ y) {
+  using R = F8Ring<AR>;
+  constexpr int S = R::S, STAGE = R::STAGE;
+  constexpr int A_LD = AR / 32;          // A loads (8 rows each) per wave and step
+  constexpr int TM = AR / 64;            // 32-row MFMA blocks per wave
+  constexpr int L = A_LD + 4 + 1;        // loads per wave and step: A, W, one scale load
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int nkb = K / kT;
   const int lrow = lane >> 3, lpos = lane & 7;
 
-  // this wave's 32 A rows and 32 W rows of every step: four 8-row loads each
-  const uint8_t* a_src[4];
+  // this wave's A rows (A_LD x 8) and 32 W rows of every step
+  const uint8_t* a_src[A_LD];
   const uint8_t* w_src[4];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int r = wave * (AR / 4) + i * 8 + lrow;
+    const int rr = min(r, rows - 1);
+    a_src[i] = qa + moe::a_row(tb, m_start + rr) * K + (lpos ^ f8_swz(r)) * 16;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + i * 8 + lrow;
-    const int rr = min(r, rows - 1);
-    const int pos = (lpos ^ f8_swz(r)) * 16;
-    a_src[i] = qa + moe::a_row(tb, m_start + rr) * K + pos;
     // weight row of LDS row r: fused, rows 0-63 gate nt*64 + r, rows 64-127 up
     const int64_t wr = FUSED ? (r < kT / 2 ? static_cast<int64_t>(nt) * (kT / 2) + r
                                            : static_cast<int64_t>(up_row) + nt * (kT / 2) + (r - kT / 2))
                              : static_cast<int64_t>(nt) * kT + r;
-    w_src[i] = qw + (static_cast<int64_t>(g) * N + wr) * K + pos;
+    w_src[i] = qw + (static_cast<int64_t>(g) * N + wr) * K + (lpos ^ f8_swz(r)) * 16;
   }
-  // waves 0 and 1 load the 128 A row scales of a step, 64 rows each
-  const float* sa_src = sa + moe::a_row(tb, m_start + min(wave * 64 + lane, rows - 1)) * nkb;
+  // the AR A row scales of a step, 64 a wave: waves past them reload the
+  // first 64 into their own scratch slot
+  const bool real_scale = wave * 64 < AR;
+  const float* sa_src = sa + moe::a_row(tb, m_start + min((real_scale ? wave * 64 : 0) + lane, rows - 1)) * nkb;
+  const int sa_dst = real_scale ? R::A_BYTES + kT * kT + wave * 64 * 4 : -1;
+  uint8_t* const scratch = smem + kF8Lds - kF8Scratch + wave * 64 * 4;
   // the weight scale block of each of the wave's two 32-row MFMA blocks (128-row
   // blocks: fused, the gate rows nt*64.. sit in block nt/2, the up rows in
   // block up_row/128 + nt/2; otherwise both in block nt)
@@ -155,17 +173,17 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
   sw_blk[1] = sw + (static_cast<int64_t>(g) * (N / kT) + (FUSED ? up_row / kT + nt / 2 : nt)) * nkb;
 
   auto issue = [&](int kb, int st) __attribute__((always_inline)) {
-    uint8_t* base = smem + st * kF8StageBytes;
+    uint8_t* base = smem + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(a_src[i] + kb * kT, base + (wave * 32 + i * 8) * kT);
+    for (int i = 0; i < A_LD; ++i) dma16(a_src[i] + kb * kT, base + (wave * (AR / 4) + i * 8) * kT);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(w_src[i] + kb * kT, base + kT * kT + (wave * 32 + i * 8) * kT);
-    if (wave < 2) dma4(sa_src + kb, base + 2 * kT * kT + wave * 64 * 4);
+    for (int i = 0; i < 4; ++i) dma16(w_src[i] + kb * kT, base + R::A_BYTES + (wave * 32 + i * 8) * kT);
+    dma4(sa_src + kb, sa_dst >= 0 ? base + sa_dst : scratch);
   };
 
-  floatx16 acc[2][2];
+  floatx16 acc[TM][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -175,7 +193,9 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
   // half h of half j takes chunks 4j + 2h and 4j + 2h + 1 (the same mapping
   // for both operands, which is all the dot products need)
   const int h = lane >> 5;
-  const int a_row0 = wm * 64 + (lane & 31);
+  const int a_row0 = wm * (AR / 2) + (lane & 31);
+  // 32-row MFMA blocks of this wave that hold valid rows (the others skip their MFMAs)
+  const int live_tm = __builtin_amdgcn_readfirstlane(min(TM, max(0, (rows - wm * (AR / 2) + 31) / 32)));
   // LDS row of the wave's MFMA block tn: fused, tn 0 gate rows wn*32.., tn 1
   // up rows 64 + wn*32..; otherwise rows wn*64 + tn*32..
   const int w_row0 = (FUSED ? wn * 32 : wn * 64) + (lane & 31);
@@ -187,24 +207,33 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
 
+  // prologue: steps 0 .. S-2
   issue(0, 0);
+  if (S > 2 && nkb > 1) issue(1, 1);
   for (int kb = 0; kb < nkb; ++kb) {
-    // stage kb has landed for every wave, and every wave is done with stage kb-1
-    wait_vm_barrier<0>();
-    if (kb + 1 < nkb) issue(kb + 1, (kb + 1) & 1);
-    const uint8_t* st = smem + (kb & 1) * kF8StageBytes;
-    const float* s_rows = reinterpret_cast<const float*>(st + 2 * kT * kT);
+    // stage kb has landed for every wave (the S-2 later steps may still be in
+    // flight), and every wave is done with stage kb-1, whose slot takes step kb+S-1
+    if constexpr (S == 2) {
+      wait_vm_barrier<0>();
+    } else {
+      if (kb + 1 < nkb) wait_vm_barrier<L>();
+      else wait_vm_barrier<0>();
+    }
+    if (kb + S - 1 < nkb) issue(kb + S - 1, (kb + S - 1) % S);
+    const uint8_t* st = smem + (kb % S) * STAGE;
+    const float* s_rows = reinterpret_cast<const float*>(st + R::A_BYTES + kT * kT);
     const float w_scale[2] = {sw_blk[0][kb], sw_blk[1][kb]};
-    v8i af[2][2], wf[2][2];
+    v8i af[TM][2], wf[2][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int tm = 0; tm < 2; ++tm) af[tm][j] = frag(st, a_row0 + tm * 32, j);
+      for (int tm = 0; tm < TM; ++tm) af[tm][j] = frag(st, a_row0 + tm * 32, j);
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) wf[tn][j] = frag(st + kT * kT, w_row0 + tn * kWBlk1, j);
+      for (int tn = 0; tn < 2; ++tn) wf[tn][j] = frag(st + R::A_BYTES, w_row0 + tn * kWBlk1, j);
     }
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
+    for (int tm = 0; tm < TM; ++tm) {
+      if (tm >= live_tm) break;  // wave-uniform: no valid rows from here on
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn) {
         const float sc = s_rows[a_row0 + tm * 32] * w_scale[tn];
@@ -214,13 +243,14 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[tm][tn][r] += p[r] * sc;
       }
+    }
   }
 
   // lane (h, c): activation row a_row0 + tm*32; result element r is weight
   // row w_row0-relative (r & 3) + 4h + 8(r >> 2), four consecutive columns per
   // quad of registers
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
+  for (int tm = 0; tm < TM; ++tm) {
     const int lr = a_row0 + tm * 32;
     if (lr >= rows) continue;
     if constexpr (FUSED) {
@@ -247,6 +277,28 @@ __global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
         }
     }
   }
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kF8Threads, 2) void grouped_gemm_fp8_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
+    const float* __restrict__ sw, moe::Tables tb, int64_t numel, int n_tiles, int N, int K,
+    int up_row, int ldc, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kF8Lds];
+  // Row-major tile order. The hardware hands workgroup w to XCD w % 8, so with
+  // n_tiles a multiple of 8 (56 and 32 on the DeepSeek-V3 shapes) column tile
+  // nt of every row block lands on XCD nt % 8: each XCD's L2 holds one eighth
+  // of every expert's weights, which are most of the bytes, while the much
+  // smaller activation codes are read by all eight.
+  const int bx = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
+  int g, rows;
+  int64_t m_start;
+  moe::decode_block(tb, bx, kT, numel, g, m_start, rows);
+  if (rows == 0) return;
+  if (rows <= 64)
+    fp8_tile<FUSED, 64>(smem, qa, sa, qw, sw, tb, g, m_start, rows, nt, N, K, up_row, ldc, y);
+  else
+    fp8_tile<FUSED, 128>(smem, qa, sa, qw, sw, tb, g, m_start, rows, nt, N, K, up_row, ldc, y);
 }
 
 }  // namespace
