@@ -512,6 +512,34 @@ __device__ __forceinline__ bool silu_tab_misses(uint32_t gb) {
   return (gb & 0x8000u) && ((gb >> 7) & 0xFFu) >= static_cast<uint32_t>(moe::kSiluTabE0 + 32);
 }
 
+// Per-lane A byte offsets of a wide tile's direct-to-LDS loads: row r of
+// the tile (clamped to the last valid row) is A row gather[m_start + r] /
+// gather_k, or m_start + r without a gather table (then counted from the
+// tile's first row). The gather entries are loaded together, so the
+// prologue waits for them once.
+template <int A_LOADS, int NW, int RPL>
+__device__ __forceinline__ void wide_a_offsets(uint32_t* a_off, const int32_t* __restrict__ gather, int gather_k,
+                                               int64_t m_start, int rows, int K, int wave, int lrow, int lpos) {
+  if (gather) {
+    int32_t gv[A_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) gv[i] = gather[m_start + min((wave * A_LOADS + i) * RPL + lrow, rows - 1)];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int r = (wave * A_LOADS + i) * RPL + lrow;
+      a_off[i] = static_cast<uint32_t>(gv[i] / gather_k) * static_cast<uint32_t>(K) * 2u +
+                 static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int r = (wave * A_LOADS + i) * RPL + lrow;
+      a_off[i] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) * 2u +
+                 static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
+    }
+  }
+}
+
 template <int V>
 struct Ic {
   static constexpr int value = V;
@@ -519,7 +547,8 @@ struct Ic {
 
 template <bool FUSED, int NW>
 __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __restrict__ A,
-                                               const uint16_t* __restrict__ Wb, int64_t m_start, int rows, int nt,
+                                               const uint16_t* __restrict__ Wb, const int32_t* __restrict__ go_g,
+                                               int64_t m_off, int rows, int nt,
                                                int K, int up_row, int ldc, uint16_t* __restrict__ C,
                                                const int32_t* __restrict__ gather, int gather_k) {
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
@@ -543,16 +572,8 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   // direct-to-LDS sources: a uniform base per step plus fixed per-lane
   // offsets (with a gather table, from the start of A: the host checks that
   // A's rows fit 32-bit byte offsets)
-  const char* a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
   const char* w_base = reinterpret_cast<const char*>(Wb + static_cast<int64_t>(nt) * (FUSED ? kWideW / 2 : kWideW) * K);
   uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int r = (wave * A_LOADS + i) * RPL + lrow;
-    const int rr = min(r, rows - 1);
-    const uint32_t ar = gather ? static_cast<uint32_t>(gather[m_start + rr] / gather_k) : static_cast<uint32_t>(rr);
-    a_off[i] = ar * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
-  }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int r = (wave * B_LOADS + i) * RPL + lrow;
@@ -591,6 +612,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   constexpr int kBFragRow[4] = {0, 32, FUSED ? kWideW / 2 : 64, FUSED ? kWideW / 2 + 32 : 96};
 
   const int nk = K / BK;
+  const char* a_base = nullptr;  // set once the row offset is known (after W(0) is out)
   // the operand with three slots runs two steps ahead (its loads are issued
   // last in a step), the other one step ahead
   constexpr int FIRST = kWideWDeep ? A_LOADS : B_LOADS;   // loads of the one-ahead operand
@@ -601,11 +623,26 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   auto load_w = [&](int kt, int slot, int i) __attribute__((always_inline)) {
     dma16(w_base + kt * BK * 2 + b_off[i], smem + b_lds0 + slot * kWideSlotBytes + i * RPL * ROWB);
   };
-  // prologue: A(0), W(0), then step 1 of the two-ahead operand
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) load_a(0, 0, i);
+  // FUSED: the SiLU table (32 KiB, one slot) takes the place of W(nk) in the
+  // W slot that step would have used, loaded during step nk - 2 like a W part
+  // (same count per wave, so the waits are unchanged); the wait of the last
+  // step lands it
+  static_assert(moe::kSiluTabMid * 4 == kWideSlotBytes && moe::kSiluTabMid / 4 / (64 * NW) == B_LOADS,
+                "the table loads like one W step");
+  auto load_tab = [&](int slot, int i) __attribute__((always_inline)) {
+    const int c = (i * NW + wave) * 64;  // a wave-wide load fills 64 consecutive 16-byte pieces
+    dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab.v) + c + lane, smem + kWideWRing + slot * kWideSlotBytes + c * 16);
+  };
+  // prologue: W(0), which needs only the expert and the column tile, goes out
+  // before the loads the A rows depend on (the group offset, then the
+  // gather entries); then A(0), then step 1 of the two-ahead operand
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) load_w(0, 0, i);
+  const int64_t m_start = (go_g ? static_cast<int64_t>(*go_g) : 0) + m_off;
+  a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
+  wide_a_offsets<A_LOADS, NW, RPL>(a_off, gather, gather_k, m_start, rows, K, wave, lrow, lpos);
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) load_a(0, 0, i);
   if (nk > 1) {
     if constexpr (kWideWDeep) {
 #pragma unroll
@@ -660,6 +697,8 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
           if (kt + 2 < nk) {
             if constexpr (kWideWDeep) load_w(kt + 2, W_NEXT, j - FIRST);
             else load_a(kt + 2, A_NEXT, j - FIRST);
+          } else if constexpr (FUSED && kWideWDeep) {
+            if (kt + 2 == nk) load_tab(W_NEXT, j - FIRST);
           }
         }
       }
@@ -676,21 +715,18 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     if (kt + 5 < nk) step(Ic<5 % kWideASlots>{}, Ic<5 % kWideWSlots>{}, kt + 5);
   }
 
-  // FUSED: the SiLU table goes into the ring's last 32 KiB (the last W slot)
-  // once every wave is past its last fragment read
-  constexpr int kTabOff = kWideLds - moe::kSiluTabMid * 4;
+  // FUSED with a single K step (no step nk - 2): the table goes into the last
+  // W slot once every wave is past its last fragment read
+  const int tab_slot = nk >= 2 ? nk % kWideWSlots : kWideWSlots - 1;
   if constexpr (FUSED) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (nk < 2) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < moe::kSiluTabMid / 4 / (64 * NW); ++i) {
-      const int c = (i * NW + wave) * 64;  // a wave-wide load fills 64 consecutive 16-byte pieces
-      dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab.v) + c + lane, smem + kTabOff + c * 16);
+      for (int i = 0; i < B_LOADS; ++i) load_tab(tab_slot, i);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
   }
-
-  // FUSED: wait for the table (every wave's pieces)
-  if constexpr (FUSED) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  const float* tab = reinterpret_cast<const float*>(smem + kTabOff);
+  const float* tab = reinterpret_cast<const float*>(smem + kWideWRing + tab_slot * kWideSlotBytes);
   // the SiLUs come from the table unless a gate of this wave needs the direct
   // evaluation (a negative one of magnitude at least 128): one vote per wave,
   // and one loop for each case
@@ -765,7 +801,8 @@ struct StageShape<128> {
 
 template <bool FUSED, int AR, int NW>
 __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* __restrict__ A,
-                                                const uint16_t* __restrict__ Wb, int64_t m_start, int rows, int nt,
+                                                const uint16_t* __restrict__ Wb, const int32_t* __restrict__ go_g,
+                                                int64_t m_off, int rows, int nt,
                                                 int K, int up_row, int ldc, uint16_t* __restrict__ C,
                                                 const int32_t* __restrict__ gather, int gather_k) {
   using SS = StageShape<AR>;
@@ -792,16 +829,9 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   const int lrow = lane / CPR;
   const int lpos = lane % CPR;
 
-  const char* a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
+  const char* a_base = nullptr;  // set once the row offset is known (after W(0) is out)
   const char* w_base = reinterpret_cast<const char*>(Wb + static_cast<int64_t>(nt) * (FUSED ? kWideW / 2 : kWideW) * K);
   uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int r = (wave * A_LOADS + i) * RPL + lrow;
-    const int rr = min(r, rows - 1);
-    const uint32_t ar = gather ? static_cast<uint32_t>(gather[m_start + rr] / gather_k) : static_cast<uint32_t>(rr);
-    a_off[i] = ar * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>((lpos ^ wide_swz(r)) << 4);
-  }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int r = (wave * B_LOADS + i) * RPL + lrow;
@@ -850,8 +880,15 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
         dma16(a_base + ko + a_off[j - B_LOADS], smem + slot_base + a_lds0 + (j - B_LOADS) * RPL * ROWB);
     }
   };
-  // prologue: steps 0 .. S-2
-  issue(0, 0, 0, L);
+  // prologue: steps 0 .. S-2, W(0) first: it needs only the expert and the
+  // column tile, and goes out before the loads the A rows depend on (the
+  // group offset, then the gather entries); the order of the DMA loads is
+  // that of issue(), so the waits are unchanged
+  issue(0, 0, 0, B_LOADS);
+  const int64_t m_start = (go_g ? static_cast<int64_t>(*go_g) : 0) + m_off;
+  a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
+  wide_a_offsets<A_LOADS, NW, RPL>(a_off, gather, gather_k, m_start, rows, K, wave, lrow, lpos);
+  issue(0, 0, B_LOADS, A_LOADS);
   if (nk > 1) issue(1, STAGE, 0, L);
   if constexpr (S > 3) {
     if (nk > 2) issue(2, 2 * STAGE, 0, L);
@@ -990,29 +1027,51 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   }
 }
 
-// Expert g and tile q inside it of the p-th 256-row tile, counting
-// ceil(gs[e] / 256) tiles per expert in expert order (a wave-wide scan over
-// the group sizes, 64 experts at a time). Returns false past the last tile.
-__device__ __forceinline__ bool find_wide_tile(const int32_t* __restrict__ gs, int E, int p, int& g, int& q) {
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2,
+// 4 and 8 (lanes shifted in from outside a 16-lane row add 0), then lane 15
+// of each row added to the next row and lane 31 to the upper two rows.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  int v = x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Expert g, tile q inside it and the expert's row count n of the p-th 256-row
+// tile, counting ceil(gs[e] / 256) tiles per expert in expert order. The
+// group sizes of up to kFindBatch * 64 experts are loaded at once (one load
+// latency before the search, which every workgroup pays before its first
+// weight load), then scanned 64 at a time. Returns false past the last tile.
+constexpr int kFindBatch = 8;
+__device__ __forceinline__ bool find_wide_tile(const int32_t* __restrict__ gs, int E, int p, int& g, int& q, int& n) {
   const int lane = threadIdx.x & 63;
   int before = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    const int pc = e < E ? (gs[e] + (kWideRows - 1)) / kWideRows : 0;
-    int incl = pc;
+  for (int base0 = 0; base0 < E; base0 += 64 * kFindBatch) {
+    int cnt[kFindBatch];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
+    for (int b = 0; b < kFindBatch; ++b) {
+      const int e = base0 + b * 64 + lane;
+      cnt[b] = e < E ? gs[e] : 0;
     }
-    const int total = __shfl(incl, 63);
-    if (p < before + total) {
-      const int j = __builtin_ctzll(__ballot(before + incl > p));
-      g = __builtin_amdgcn_readfirstlane(base + j);
-      q = __builtin_amdgcn_readfirstlane(p - before - (__shfl(incl, j) - __shfl(pc, j)));
-      return true;
+#pragma unroll
+    for (int b = 0; b < kFindBatch; ++b) {
+      if (base0 + b * 64 >= E) break;
+      const int pc = (cnt[b] + (kWideRows - 1)) / kWideRows;
+      const int incl = wave_incl_sum(pc);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (p < before + total) {
+        const int j = __builtin_ctzll(__ballot(before + incl > p));
+        g = base0 + b * 64 + j;
+        q = p - before - (__builtin_amdgcn_readlane(incl, j) - __builtin_amdgcn_readlane(pc, j));
+        n = __builtin_amdgcn_readlane(cnt[b], j);
+        return true;
+      }
+      before += total;
     }
-    before += total;
   }
   return false;
 }
@@ -1034,7 +1093,7 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
   const int w = blockIdx.x;
   const int xcd = w & 7, j = w >> 3;
   int g, nt;
-  int64_t m_start, r;
+  int64_t m_off, r;  // the tile's first row inside its group, rows left from there
   if (expert_groups) {
     // Groups of n_tiles tiles, one per 256-row tile of the expert-ordered list
     // (group k runs on XCD k % 8). An expert with mt tiles splits into blocks
@@ -1047,14 +1106,14 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
     const int t = j - jg * n_tiles;
     const int k = jg * 8 + xcd;
     if (k >= m_tiles) return;
-    int q, mt;
+    int q, mt, n = 0;
     if (tb.gs == nullptr) {
       g = 0;
       q = k;
       mt = static_cast<int>((numel + kWideRows - 1) / kWideRows);
     } else {
-      if (!find_wide_tile(tb.gs, E, k, g, q)) return;
-      mt = (tb.gs[g] + kWideRows - 1) / kWideRows;
+      if (!find_wide_tile(tb.gs, E, k, g, q, n)) return;
+      mt = (n + kWideRows - 1) / kWideRows;
     }
     int gx = 1;
     for (int d = min(mt, kWideGmax); d > 1; --d)
@@ -1071,13 +1130,8 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
       mq = q;
       nt = t;
     }
-    if (tb.gs == nullptr) {
-      m_start = static_cast<int64_t>(mq) * kWideRows;
-      r = numel - m_start;
-    } else {
-      m_start = static_cast<int64_t>(tb.go[g]) + static_cast<int64_t>(mq) * kWideRows;
-      r = static_cast<int64_t>(tb.gs[g]) - static_cast<int64_t>(mq) * kWideRows;
-    }
+    m_off = static_cast<int64_t>(mq) * kWideRows;
+    r = (tb.gs == nullptr ? numel : static_cast<int64_t>(n)) - m_off;
   } else {
     const int gsz = gm * gn;
     const int jg = j / gsz;
@@ -1092,24 +1146,26 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
     if (p >= m_tiles) return;
     if (tb.gs == nullptr) {
       g = 0;
-      m_start = static_cast<int64_t>(p) * kWideRows;
-      r = numel - m_start;
+      m_off = static_cast<int64_t>(p) * kWideRows;
+      r = numel - m_off;
     } else {
-      int q;
-      if (!find_wide_tile(tb.gs, E, p, g, q)) return;
-      m_start = static_cast<int64_t>(tb.go[g]) + static_cast<int64_t>(q) * kWideRows;
-      r = static_cast<int64_t>(tb.gs[g]) - static_cast<int64_t>(q) * kWideRows;
+      int q, n;
+      if (!find_wide_tile(tb.gs, E, p, g, q, n)) return;
+      m_off = static_cast<int64_t>(q) * kWideRows;
+      r = static_cast<int64_t>(n) - m_off;
     }
   }
   if (r <= 0) return;
   const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
+  // the group's offset is read by the tile after its first weight loads are out
+  const int32_t* go_g = tb.gs == nullptr ? nullptr : tb.go + g;
   if (rows <= 64)
-    wide_stage_tile<FUSED, 64, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+    wide_stage_tile<FUSED, 64, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
   else if (rows <= kWideRows / 2)
-    wide_stage_tile<FUSED, 128, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+    wide_stage_tile<FUSED, 128, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
   else
-    wide_ring_tile<FUSED, NW>(smem, A, Wb, m_start, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+    wide_ring_tile<FUSED, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
 }
 
 // Group shape for the tile order: GN column tiles (a divisor of n_tiles, at
