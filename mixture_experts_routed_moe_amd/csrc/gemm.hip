@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "moe_common.h"
+#include "wide_sched.h"
 
 namespace {
 
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
 //
 // Loads, fragments and barriers work as in grouped_gemm_pipe_kernel, over
 // the rings described at wide_ring_tile and wide_stage_tile.
-constexpr int kWideRows = 256;
+using moe::kWideRows;
 constexpr int kWideW = 256;
 
 // The wide tile's K loop, K step 64 (whole 128-byte rows, so every L1 -> L2
@@ -1027,135 +1028,18 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   }
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2,
-// 4 and 8 (lanes shifted in from outside a 16-lane row add 0), then lane 15
-// of each row added to the next row and lane 31 to the upper two rows.
-__device__ __forceinline__ int wave_incl_sum(int x) {
-  int v = x;
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
-  return v;
-}
-
-// Expert g, tile q inside it and the expert's row count n of the p-th 256-row
-// tile, counting ceil(gs[e] / 256) tiles per expert in expert order. The
-// group sizes of up to kFindBatch * 64 experts are loaded at once (one load
-// latency before the search, which every workgroup pays before its first
-// weight load), then scanned 64 at a time. Returns false past the last tile.
-constexpr int kFindBatch = 8;
-__device__ __forceinline__ bool find_wide_tile(const int32_t* __restrict__ gs, int E, int p, int& g, int& q, int& n) {
-  const int lane = threadIdx.x & 63;
-  int before = 0;
-  for (int base0 = 0; base0 < E; base0 += 64 * kFindBatch) {
-    int cnt[kFindBatch];
-#pragma unroll
-    for (int b = 0; b < kFindBatch; ++b) {
-      const int e = base0 + b * 64 + lane;
-      cnt[b] = e < E ? gs[e] : 0;
-    }
-#pragma unroll
-    for (int b = 0; b < kFindBatch; ++b) {
-      if (base0 + b * 64 >= E) break;
-      const int pc = (cnt[b] + (kWideRows - 1)) / kWideRows;
-      const int incl = wave_incl_sum(pc);
-      const int total = __builtin_amdgcn_readlane(incl, 63);
-      if (p < before + total) {
-        const int j = __builtin_ctzll(__ballot(before + incl > p));
-        g = base0 + b * 64 + j;
-        q = p - before - (__builtin_amdgcn_readlane(incl, j) - __builtin_amdgcn_readlane(pc, j));
-        n = __builtin_amdgcn_readlane(cnt[b], j);
-        return true;
-      }
-      before += total;
-    }
-  }
-  return false;
-}
-
-constexpr int kWideGmax = 4;
-constexpr int kWideEgMinCols = 16;
-constexpr int kWideEgMinRowTiles = 32;
-
 template <bool FUSED, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel, int m_tiles,
-    int n_tiles, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int gm, int gn,
-    int expert_groups) {
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel,
+    moe::WideGrid wg, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C) {
   constexpr int SMEM = kWideLds;
   static_assert(SMEM <= 160 * 1024, "LDS ring too large");
   static_assert(SMEM >= 128 * 1024, "the half-tile exchange needs 128 KiB");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
 
-  const int w = blockIdx.x;
-  const int xcd = w & 7, j = w >> 3;
   int g, nt;
   int64_t m_off, r;  // the tile's first row inside its group, rows left from there
-  if (expert_groups) {
-    // Groups of n_tiles tiles, one per 256-row tile of the expert-ordered list
-    // (group k runs on XCD k % 8). An expert with mt tiles splits into blocks
-    // of gx tiles (gx the largest divisor of n_tiles that is at most
-    // min(mt, kWideGmax)); each block's gx groups cover its gx row tiles by
-    // n_tiles / gx column tiles, so a group reuses its weight slice gx times and
-    // its activation rows n_tiles / gx times from L2; the rows a block leaves
-    // over take one group each (one row tile by every column tile).
-    const int jg = j / n_tiles;
-    const int t = j - jg * n_tiles;
-    const int k = jg * 8 + xcd;
-    if (k >= m_tiles) return;
-    int q, mt, n = 0;
-    if (tb.gs == nullptr) {
-      g = 0;
-      q = k;
-      mt = static_cast<int>((numel + kWideRows - 1) / kWideRows);
-    } else {
-      if (!find_wide_tile(tb.gs, E, k, g, q, n)) return;
-      mt = (n + kWideRows - 1) / kWideRows;
-    }
-    int gx = 1;
-    for (int d = min(mt, kWideGmax); d > 1; --d)
-      if (n_tiles % d == 0) {
-        gx = d;
-        break;
-      }
-    int mq;
-    if (q < (mt / gx) * gx) {
-      const int gi = q % gx;
-      mq = q - gi + t % gx;
-      nt = gi * (n_tiles / gx) + t / gx;
-    } else {
-      mq = q;
-      nt = t;
-    }
-    m_off = static_cast<int64_t>(mq) * kWideRows;
-    r = (tb.gs == nullptr ? numel : static_cast<int64_t>(n)) - m_off;
-  } else {
-    const int gsz = gm * gn;
-    const int jg = j / gsz;
-    const int t = j - jg * gsz;
-    const int group = jg * 8 + xcd;
-    const int super_cols = n_tiles / gn;
-    const int sr = group / super_cols;
-    const int sc = group - sr * super_cols;
-    const int tm_ = t % gm;
-    const int p = sr * gm + tm_;  // 256-row tile index
-    nt = sc * gn + (t - tm_) / gm;
-    if (p >= m_tiles) return;
-    if (tb.gs == nullptr) {
-      g = 0;
-      m_off = static_cast<int64_t>(p) * kWideRows;
-      r = numel - m_off;
-    } else {
-      int q, n;
-      if (!find_wide_tile(tb.gs, E, p, g, q, n)) return;
-      m_off = static_cast<int64_t>(q) * kWideRows;
-      r = static_cast<int64_t>(n) - m_off;
-    }
-  }
-  if (r <= 0) return;
+  if (!moe::wide_tile_at(tb, E, numel, wg, blockIdx.x, g, nt, m_off, r)) return;
   const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
   // the group's offset is read by the tile after its first weight loads are out
@@ -1193,31 +1077,17 @@ int launch_pipe(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, 
   return moe::check_launch(name);
 }
 
-constexpr int kWideGroup = 16;
 constexpr int kWideWaves = 8;
 
 template <bool FUSED>
 int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int n_tiles, int K,
                 int64_t w_stride, int up_row, int ldc, uint16_t* C, hipStream_t stream, const char* name) {
-  // every non-empty expert ends in at most one partial tile
-  const int64_t m_tiles = moe::ceil_div(numel, kWideRows) + (tb.gs ? E : 0);
-  int gn = 1;
-  for (int d = kPipeGnMax; d >= 1; --d)
-    if (n_tiles % d == 0) {
-      gn = d;
-      break;
-    }
-  const int gm = kWideGroup / gn > 0 ? kWideGroup / gn : 1;
-  // expert-aware groups (see the kernel) when a row tile has many column
-  // tiles: on the DeepSeek-V3-shaped routing (16 and 28 column tiles) gate_up
-  // 2.46 -> 2.44 ms and down 1.31 -> 1.28 ms (interleaved A/B); with 6 or 8
-  // (the Qwen3 shapes) the fixed 16-tile groups are as fast or faster
-  const int eg = n_tiles >= kWideEgMinCols && m_tiles >= kWideEgMinRowTiles;
-  const int64_t groups = moe::ceil_div(m_tiles, gm) * (n_tiles / gn);
-  const int64_t blocks = eg ? moe::ceil_div(m_tiles, 8) * 8 * n_tiles : moe::ceil_div(groups, 8) * 8 * gm * gn;
-  if (blocks > 0x7FFFFFFF || m_tiles > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
+  moe::WideGrid wg;
+  int64_t blocks;
+  if (!moe::wide_grid(numel, E, tb.gs != nullptr, n_tiles, wg, blocks))
+    return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
   grouped_gemm_wide_kernel<FUSED, kWideWaves><<<static_cast<unsigned>(blocks), 64 * kWideWaves, 0, stream>>>(
-      A, W, tb, E, numel, static_cast<int>(m_tiles), n_tiles, K, w_stride, up_row, ldc, C, gm, gn, eg);
+      A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C);
   return moe::check_launch(name);
 }
 
