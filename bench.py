@@ -679,10 +679,11 @@ def main():
 
 def gemm_source_sha() -> str:
     """First 16 hex digits of the sha256 over the GEMM kernels' sources
-    (gemm.hip, then moe_common.h): the revision a traffic figure belongs to."""
+    (gemm.hip, then wide_sched.h, then moe_common.h): the revision a traffic
+    figure belongs to."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("gemm.hip", "moe_common.h"):
+    for name in ("gemm.hip", "wide_sched.h", "moe_common.h"):
         with open(os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
