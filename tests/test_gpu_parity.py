@@ -449,6 +449,39 @@ def test_grouped_gemm_wide_expert_groups(fused):
         assert_bf16_close(bits(y), oracle.grouped_gemm(bits(xp), bits(wd), gs, go), "down (16 col tiles)")
 
 
+@pytest.mark.parametrize("n_out", [4096, 256])
+def test_grouped_gemm_more_than_512_experts(n_out):
+    """700 experts: the tile search loads the group sizes 512 at a time, so the
+    experts past 512 (among them experts of 1..9 row tiles) are found in its
+    second pass. n_out = 4096 takes the expert-aware tile order (16 column
+    tiles), 256 the fixed groups; gate_up (fused and not) and down against the
+    oracle."""
+    d = dev()
+    say("more than 512 experts", n_out)
+    rng = np.random.default_rng(12)
+    E = 700
+    sizes = (rng.integers(1, 200, E) * (rng.random(E) < 0.35)).astype(np.int64)
+    for e, n in ((3, 600), (513, 1), (515, 257), (600, 2300), (650, 700), (699, 129)):
+        sizes[e] = n
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    ids_np = ids_np[rng.permutation(ids_np.size)][:, None]
+    T, K = ids_np.shape[0], 64
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    assert list(gs) == list(sizes)
+    key = moe_synth.tensor_key(87, n_out)
+    x = moe_synth.normal_bf16(key, (T, K), 1.0, d)
+    F = n_out // 2
+    wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, K), K ** -0.5, d)
+    gu = mx.grouped_gemm_gate_up(x, wgu, tb, 128, 128, fuse_swiglu=False)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(wgu), gs, go), f"gate_up E=700 2F={2 * F}")
+    h = mx.grouped_gemm_gate_up(x, wgu, tb, 128, 128, fuse_swiglu=True)
+    assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
+    wd = moe_synth.normal_bf16(key + 2, (E, n_out, K), K ** -0.5, d)
+    y = mx.grouped_gemm_down(x, wd, tb, 128, 128)
+    assert_bf16_close(bits(y), oracle.grouped_gemm(bits(x), bits(wd), gs, go), f"down E=700 H={n_out}")
+
+
 @pytest.mark.parametrize("K", [64, 192, 448])
 def test_grouped_gemm_small_expert_tiles(K):
     """Tiles of at most 32 valid rows inside a 256-row-kernel launch (experts
