@@ -66,6 +66,7 @@ def parse():
                             "kimi_k2_t512", "kimi_k2_t2048", "kimi_k2_t4096"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-primary", action="store_true", help="skip the other forward workloads")
+    p.add_argument("--fp8", action="store_true", help="with --only-primary: still run the FP8 leg (fp8_down)")
     p.add_argument("--gemm-table-only", action="store_true",
                    help="time only the aligned grouped-GEMM cases (prints their JSON object)")
     p.add_argument("--gemm-cases", default="all",
@@ -558,7 +559,7 @@ def main():
     H, F, E = cfg.H, cfg.F, cfg.E
     hidden, logits, bias, wgu, wd, swgu, swd = (wl.hidden, wl.logits, wl.bias, wl.wgu, wl.wd, wl.swgu, wl.swd)
 
-    fp8 = None if args.only_primary else fp8_down(wl, args.steps, args.warmup, ev)
+    fp8 = None if args.only_primary and not args.fp8 else fp8_down(wl, args.steps, args.warmup, ev)
     if fp8 is not None:
         fp8["bf16_down_ms"] = round(stage_ms["down"], 4)
         print(f"# fp8 down: {fp8['gemm_ms']:.3f} ms (bf16 {stage_ms['down']:.3f} ms)", file=sys.stderr, flush=True)
