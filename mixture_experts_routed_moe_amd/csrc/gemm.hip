@@ -1,23 +1,29 @@
 // Grouped GEMM C[e] = A[e] @ W[e]^T for the routed experts on bf16 MFMA.
 //
-// Work decomposition: one workgroup per (padded row block bx, column tile nt).
-// The row block is decoded from the dispatch tables (row recovery of the
-// tutorial's contract); blocks past an expert's rows, or past the last
-// expert, have no rows and return at once. A is the compact [numel, K]
-// layout: rows past the block's valid count are never stored, so an expert's
-// last, partial tile needs no padding copy.
+// Work decomposition: a workgroup computes one row tile by one column tile
+// of one expert. Row tiles are found from the dispatch tables (the compact
+// expert-major row space that the routing tables define); a tile past an
+// expert's rows, or past the last expert, has no rows and returns at once. A
+// is the compact [numel, K] layout: rows past a tile's valid count are never
+// stored, so an expert's last, partial tile needs no padding copy.
 //
-// Two kernels:
-//  * grouped_gemm_pipe_kernel, 128-row blocks (the production path): a
-//    128 x 256 tile fed by direct-to-LDS loads through a multi-stage ring, see
-//    the comment above it;
-//  * grouped_gemm_kernel, any block_m in {64, 128} and narrow outputs: a
-//    simpler register-staged double buffer, 128 x 128 tile, four wave64s in a
-//    2x2 arrangement each accumulating (BM/2) x 64 with
-//    v_mfma_f32_32x32x16_bf16. A and W tiles are K-contiguous in LDS, 128
-//    bytes per row, with the eight 16-byte chunks of row r stored at chunk
-//    position c ^ g(r) (see row_xor) so the fragment reads are free of LDS bank
-//    conflicts.
+// Five kernels, chosen per launch by launch() below:
+//  * grouped_gemm_wide_kernel (the production path for 128-row blocks): 256 x
+//    256 tiles, eight waves, direct-to-LDS loads through a ring of stages, the
+//    tile order of wide_sched.h; see the comment above it;
+//  * grouped_gemm_pipe_kernel: 128 x 256 tiles on the same kind of ring, for
+//    dense launches with too few 256-row tiles to fill the chip, K not a
+//    multiple of 64, and operands past the wide kernel's 32-bit offsets;
+//  * grouped_gemm_kernel, any block_m in {64, 128}: a simpler
+//    register-staged double buffer, 128 x 128 tile, four wave64s in a 2x2
+//    arrangement each accumulating (BM/2) x 64 with v_mfma_f32_32x32x16_bf16.
+//    A and W tiles are K-contiguous in LDS, 128 bytes per row, with the eight
+//    16-byte chunks of row r stored at chunk position c ^ g(r) (see row_xor)
+//    so the fragment reads are free of LDS bank conflicts;
+//  * grouped_gemv_kernel: a handful of rows per expert (decode), streaming
+//    the weights with fp32 dot products;
+//  * dense_skinny_kernel: one dense group of 5 to 32 rows, K split over the
+//    waves of a workgroup.
 //
 // Fused SwiGLU: the W rows of a tile are gate rows and the matching up rows F
 // positions further; each wave holds gate columns and the matching up columns
@@ -480,6 +486,20 @@ constexpr int kWideW = 256;
 __device__ __forceinline__ int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 constexpr int kWideSlotBytes = kWideRows * 128;
+// K rotation of the small-row tiles (wide_stage_tile): when rows are a
+// multiple of 4 KiB long (K a multiple of 2048), expert g walks its K blocks
+// from block (g * kWideKRot) mod nk and wraps around. Tiles that walk K in
+// step put all their requests at one offset inside each 4 KiB, and HBM serves
+// such a stream at about 4.4 TB/s instead of 6.1 (a load-only stream of the
+// Qwen3-shaped decode gate_up's weights, 805 MB: 183 -> 133 us with one start
+// per expert); 7 is odd, so 32 consecutive experts start at 32 different
+// 128-byte offsets of a 4 KiB row. All tiles of an expert share the start,
+// so the ones that share its weights or rows stay in step. Measured
+// (interleaved): Qwen3 decode gate_up 0.192 -> 0.153 ms, Kimi-K2 T = 512 down
+// 1.945 -> 1.867 ms, Qwen3 prefill gate_up 0.336 -> 0.331 ms, the
+// DeepSeek-V3 shapes unchanged. Rotating the full tiles too, or rows of other
+// lengths (the 14 KiB rows of K = 7168), made the prefill GEMMs 1-4% slower.
+constexpr int kWideKRot = 7;
 // The operand with three slots is loaded two steps ahead, the other one step:
 // the weights, the stream that comes from HBM (interleaved against three A
 // slots: routed gate_up 2.828 -> 2.770 ms on the DeepSeek-V3 routing, Qwen3
@@ -805,7 +825,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
                                                 const uint16_t* __restrict__ Wb, const int32_t* __restrict__ go_g,
                                                 int64_t m_off, int rows, int nt,
                                                 int K, int up_row, int ldc, uint16_t* __restrict__ C,
-                                                const int32_t* __restrict__ gather, int gather_k) {
+                                                const int32_t* __restrict__ gather, int gather_k, int k0) {
   using SS = StageShape<AR>;
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
   constexpr int TMW = SS::TMW, TNW = SS::TNW, WR = SS::WR, WC = SS::WC, KS = SS::KS;
@@ -871,7 +891,9 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
 
   const int nk = K / BK;
   auto issue = [&](int kt, int slot_base, int first, int count) __attribute__((always_inline)) {
-    const int ko = kt * BK * 2;
+    // step kt reads K block (kt + k0) mod nk
+    const int kr = kt + k0;
+    const int ko = (kr >= nk ? kr - nk : kr) * BK * 2;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
       if (j < first || j >= first + count) continue;
@@ -1044,10 +1066,13 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
   // the group's offset is read by the tile after its first weight loads are out
   const int32_t* go_g = tb.gs == nullptr ? nullptr : tb.go + g;
+  // the small-row tiles' first K block (see kWideKRot)
+  const int k0 = K % 2048 == 0 ? (g * kWideKRot) % (K / 64) : 0;
   if (rows <= 64)
-    wide_stage_tile<FUSED, 64, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+    wide_stage_tile<FUSED, 64, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k, k0);
   else if (rows <= kWideRows / 2)
-    wide_stage_tile<FUSED, 128, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+    wide_stage_tile<FUSED, 128, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k,
+                                    k0);
   else
     wide_ring_tile<FUSED, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
 }
@@ -1159,6 +1184,16 @@ __global__ __launch_bounds__(256) void grouped_gemv_kernel(const uint16_t* __res
   const int col = nt * kGemvCols + wr;
   const uint16_t* wg = W + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(col) * K;
   const uint16_t* wu = W + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(FUSED ? up_row + col : col) * K;
+  // K rotation as in the wide kernel's small-row tiles (kWideKRot): with rows
+  // a multiple of 4 KiB long the weight rows are read from element k_rot (a
+  // multiple of kGemvUnroll steps) to the end, then from 0; a gate column and
+  // its up column take the same start, so the fused result is the SwiGLU of
+  // the unfused one
+  int k_rot = 0;
+  if (K % 2048 == 0) {
+    const int pair = FUSED ? nt : nt % max(1, ldc / 2 / kGemvCols);
+    k_rot = ((g * kWideKRot + pair) * kGemvUnroll) % (K / 64) * 64;
+  }
   for (int r0 = 0; r0 < rows; r0 += kGemvRows) {
     const int nr = min(kGemvRows, rows - r0);
     const uint16_t* arow[kGemvRows];
@@ -1201,9 +1236,12 @@ __global__ __launch_bounds__(256) void grouped_gemv_kernel(const uint16_t* __res
         }
       }
     };
-    int kb = 0;
-    for (; kb + 64 * kGemvUnroll <= K; kb += 64 * kGemvUnroll) block(kb, Ic<kGemvUnroll>{});
-    for (; kb < K; kb += 64) block(kb, Ic<1>{});
+    auto run = [&](int kb, int k_end) __attribute__((always_inline)) {
+      for (; kb + 64 * kGemvUnroll <= k_end; kb += 64 * kGemvUnroll) block(kb, Ic<kGemvUnroll>{});
+      for (; kb < k_end; kb += 64) block(kb, Ic<1>{});
+    };
+    run(k_rot, K);
+    run(0, k_rot);
     // the 8 lanes of a weight row are consecutive: reduce over lanes 1, 2, 4 apart
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r)
@@ -1283,6 +1321,12 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, kSkinnyOcc) void dense_skinny_ke
     for (int e = 0; e < 16; ++e) acc[b][e] = 0.0f;
   const int nk = K / 64;
   const int n_my = wave < nk ? (nk - wave + kSkinnyWaves - 1) / kSkinnyWaves : 0;
+  // K rotation as in the wide kernel's small-row tiles (kWideKRot): with rows
+  // a multiple of 4 KiB long the steps start at k_rot, a multiple of the wave
+  // count (every wave keeps its steps, and the partial sums their order), the
+  // same for a gate column and its up column
+  int k_rot = 0;
+  if (K % 2048 == 0) k_rot = (FUSED ? nt : nt % max(1, ldc / 2 / kSkinnyCols)) * kSkinnyWaves % nk;
   if (n_my > 0) {
     uint4 bw[D][NB][4], ba[D][4];
     // loads of this wave's step s into slot d (steps past the last reload it
@@ -1291,7 +1335,8 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, kSkinnyOcc) void dense_skinny_ke
     // with the loop's into one block
     auto issue = [&](auto dd, int s, auto site) __attribute__((always_inline)) {
       constexpr int d = decltype(dd)::value;
-      const int ko = (min(s, n_my - 1) * kSkinnyWaves + wave) * 64;
+      const int kr = min(s, n_my - 1) * kSkinnyWaves + wave + k_rot;
+      const int ko = (kr >= nk ? kr - nk : kr) * 64;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bw[d][0][j] = *reinterpret_cast<const uint4*>(w0 + ko + j * 8);
@@ -1399,8 +1444,9 @@ int launch(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, int E
   // an expert's tile of at most 64 or 128 rows runs a ring of deeper stages
   // (wide_stage_tile), which beat the 128-row kernel on the decode-like
   // shapes too (interleaved: Kimi-K2 T = 512 gate_up 3.64 -> 3.59 ms, down
-  // 2.09 -> 1.97 ms; Qwen3 decode 0.201 -> 0.189 / 0.094 -> 0.089 ms)
-  // few rows (at most 4 in one dense group, or numel <= E / 10 over the
+  // 2.09 -> 1.97 ms; Qwen3 decode 0.201 -> 0.189 / 0.094 -> 0.089 ms).
+  //
+  // Few rows (at most 4 in one dense group, or numel <= E / 10 over the
   // experts: one decode token's top-k): the weight-streaming kernel (at 256
   // rows over 384 experts the row-tile kernels are faster)
   const bool few_rows = tb.gs ? numel * 100 <= kGemvGroupedPct * static_cast<int64_t>(E) : numel <= kGemvMaxRows;

@@ -512,6 +512,66 @@ def test_grouped_gemm_small_expert_tiles(K):
     assert_bf16_close(bits(y), oracle.grouped_gemm(bits(x), bits(wd), gs, go), f"down K={K}")
 
 
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_k_rotation_4k_rows(K):
+    """Rows a multiple of 4 KiB long (K = 2048, 4096): the 256-row kernel's
+    small-row tiles, the few-row kernel and the skinny kernel walk K from a
+    per-expert (or per-column-tile) start and wrap around. 48 experts of 1 ..
+    129 rows (their starts cover all 32 or 64 K blocks; 64/65- and
+    128/129-row tiles; empty experts) and a 300-row expert (a full tile, not
+    rotated, and a rotated 44-row one); 8 single-row experts among 160 (the
+    few-row kernel); dense groups of 3 and 20 rows (few-row and skinny
+    kernels). gate_up (H = K) fused and unfused, and down (F = K), against
+    the oracle."""
+    d = dev()
+    say("K rotation", K)
+    F, Hd = 128, 256
+    rng = np.random.default_rng(K + 1)
+
+    def check(x, tb, gs, go, key, label):
+        E = len(gs)
+        wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, K), K ** -0.5, d)
+        wd = moe_synth.normal_bf16(key + 2, (E, Hd, K), K ** -0.5, d)
+        if tb is None:
+            wgu, wd = wgu[0], wd[0]
+        gu = mx.grouped_gemm_gate_up(x, wgu, tb, 128, 128, fuse_swiglu=False)
+        wgu3, wd3 = (wgu[None], wd[None]) if tb is None else (wgu, wd)
+        assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(wgu3), gs, go), f"{label} gate_up K={K}")
+        h = mx.grouped_gemm_gate_up(x, wgu, tb, 128, 128, fuse_swiglu=True)
+        assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F)), label
+        y = mx.grouped_gemm_down(x, wd, tb, 128, 128)
+        assert_bf16_close(bits(y), oracle.grouped_gemm(bits(x), bits(wd3), gs, go), f"{label} down K={K}")
+
+    # small-row tiles of the 256-row kernel
+    E = 49
+    sizes = rng.integers(1, 130, E)
+    sizes[[3, 11]] = 0
+    sizes[[5, 6, 7, 8]] = [64, 65, 128, 129]
+    sizes[40] = 300
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    ids_np = ids_np[rng.permutation(ids_np.size)][:, None]
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    assert list(gs) == list(sizes)
+    key = moe_synth.tensor_key(91, K)
+    check(moe_synth.normal_bf16(key, (ids_np.shape[0], K), 1.0, d), tb, gs, go, key, "small tiles")
+    # few-row kernel: one row in each of 8 experts among 160
+    E = 160
+    sizes = np.zeros(E, np.int64)
+    sizes[[2, 33, 70, 101, 127, 140, 150, 159]] = 1
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)[:, None]
+    assert ids_np.shape[0] * 10 <= E
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    key = moe_synth.tensor_key(92, K)
+    check(moe_synth.normal_bf16(key, (ids_np.shape[0], K), 1.0, d), tb, gs, go, key, "few-row grouped")
+    # dense groups: few-row (3 rows) and skinny (20 rows) kernels
+    for numel in (3, 20):
+        key = moe_synth.tensor_key(93, K, numel)
+        one, zero = np.array([numel], np.int32), np.array([0], np.int32)
+        check(moe_synth.normal_bf16(key, (numel, K), 1.0, d), None, one, zero, key, f"dense {numel} rows")
+
+
 @pytest.mark.parametrize("H,F,extra_empty", [(256, 256, 0), (512, 384, 0), (256, 256, 20)])
 def test_grouped_gemm_expert_size_edges(H, F, extra_empty):
     """extra_empty appends empty experts; with 20 of them the rows per expert
