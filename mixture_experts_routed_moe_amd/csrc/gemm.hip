@@ -1121,11 +1121,12 @@ int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
 // shared expert, a few tokens spread over many experts) the time is the weight
 // stream, and 128- or 256-row tiles split the output into too few workgroups
 // to reach HBM bandwidth (28 for a 7168 x 18432 down projection). One
-// 256-thread workgroup per (group, 32 output columns): 8 lanes per weight row
-// each read 16 bytes a step, so a row's lanes cover 128 contiguous bytes, with
-// kGemvUnroll steps in flight per lane, and fp32 dot products against the
-// group's rows, kGemvRows at a time (the rows are few: read from L2).
-constexpr int kGemvCols = 32;
+// 256-thread workgroup per (group, 256 / LPR output columns): LPR lanes per
+// weight row each read 16 bytes a step, so a row's lanes cover LPR * 16
+// contiguous bytes, with kGemvUnroll steps in flight per lane, and fp32 dot
+// products against the group's rows, kGemvRows at a time (the rows are few:
+// read from L2).
+constexpr int kGemvCols = 32;   // output columns of a workgroup at 8 lanes per row
 constexpr int kGemvRows = 4;
 constexpr int kGemvUnroll = 4;
 
@@ -1159,11 +1160,90 @@ __device__ __forceinline__ bool find_nonempty(const int32_t* __restrict__ gs, in
   return false;
 }
 
-template <bool FUSED>
+// The passes of a few-row workgroup over its group's rows, RP rows a pass
+// (the weights are streamed once per pass).
+template <bool FUSED, int LPR, int RP>
+__device__ __forceinline__ void gemv_rows(const uint16_t* __restrict__ A, const uint16_t* __restrict__ wg,
+                                          const uint16_t* __restrict__ wu, const Tables& tb, int64_t m0, int rows,
+                                          int K, int k_rot, int kc, int col, int ldc, uint16_t* __restrict__ C) {
+  constexpr int STEP = LPR * 8;
+  constexpr int BLOCK = STEP * kGemvUnroll;
+  for (int r0 = 0; r0 < rows; r0 += RP) {
+    const int nr = min(RP, rows - r0);
+    const uint16_t* arow[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) arow[r] = A + moe::a_row(tb, m0 + r0 + min(r, nr - 1)) * K;
+    float acc_g[RP], acc_u[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) acc_g[r] = acc_u[r] = 0.0f;
+    // K in steps of STEP (LPR lanes x 8 values): whole blocks of kGemvUnroll
+    // steps with every weight load, then every activation load (L1/L2 hits),
+    // issued before the arithmetic; then the remaining steps one at a time
+    auto block = [&](int kb, auto unroll) __attribute__((always_inline)) {
+      constexpr int U = decltype(unroll)::value;
+      uint4 vg[U], vu[U], va[U][RP];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = kb + u * STEP + kc * 8;
+        vg[u] = *reinterpret_cast<const uint4*>(wg + k);
+        if (FUSED) vu[u] = *reinterpret_cast<const uint4*>(wu + k);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+          va[u][r] = *reinterpret_cast<const uint4*>(arow[r] + kb + u * STEP + kc * 8);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float fg[8], fu[8];
+        bf16x8_to_f32(vg[u], fg);
+        if (FUSED) bf16x8_to_f32(vu[u], fu);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          float fa[8];
+          bf16x8_to_f32(va[u][r], fa);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            acc_g[r] += fa[i] * fg[i];
+            if (FUSED) acc_u[r] += fa[i] * fu[i];
+          }
+        }
+      }
+    };
+    auto run = [&](int kb, int k_end) __attribute__((always_inline)) {
+      for (; kb + BLOCK <= k_end; kb += BLOCK) block(kb, Ic<kGemvUnroll>{});
+      for (; kb < k_end; kb += STEP) block(kb, Ic<1>{});
+    };
+    run(k_rot, K);
+    run(0, k_rot);
+    // the LPR lanes of a weight row are consecutive: reduce over lanes 1, 2, 4, ... apart
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+      for (int d = 1; d < LPR; d <<= 1) {
+        acc_g[r] += __shfl_xor(acc_g[r], d);
+        if (FUSED) acc_u[r] += __shfl_xor(acc_u[r], d);
+      }
+    if (kc == 0) {
+#pragma unroll
+      for (int r = 0; r < RP; ++r) {
+        if (r >= nr) break;
+        uint16_t* crow = C + (m0 + r0 + r) * ldc;
+        if (FUSED)
+          crow[col] = moe::swiglu_bf16(moe::f32_to_bf16(acc_g[r]), moe::f32_to_bf16(acc_u[r]));
+        else
+          crow[col] = moe::f32_to_bf16(acc_g[r]);
+      }
+    }
+  }
+}
+
+template <bool FUSED, int LPR>
 __global__ __launch_bounds__(256) void grouped_gemv_kernel(const uint16_t* __restrict__ A,
                                                            const uint16_t* __restrict__ W, Tables tb, int E,
                                                            int64_t numel, int n_tiles, int K, int64_t w_stride,
                                                            int up_row, int ldc, uint16_t* __restrict__ C) {
+  constexpr int COLS = 256 / LPR;        // output columns (weight rows) of a workgroup
   // grid: min(numel, E) expert slots (at most that many experts have rows)
   // by the column tiles; slot k takes the k-th expert with rows
   const int k = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
@@ -1180,99 +1260,50 @@ __global__ __launch_bounds__(256) void grouped_gemv_kernel(const uint16_t* __res
     rows = tb.gs[g];
   }
   if (rows <= 0) return;
-  const int t = threadIdx.x, wr = t >> 3, kc = t & 7;
-  const int col = nt * kGemvCols + wr;
+  const int t = threadIdx.x, wr = t / LPR, kc = t % LPR;
+  const int col = nt * COLS + wr;
   const uint16_t* wg = W + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(col) * K;
   const uint16_t* wu = W + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(FUSED ? up_row + col : col) * K;
   // K rotation as in the wide kernel's small-row tiles (kWideKRot): with rows
   // a multiple of 4 KiB long the weight rows are read from element k_rot (a
-  // multiple of kGemvUnroll steps) to the end, then from 0; a gate column and
-  // its up column take the same start, so the fused result is the SwiGLU of
-  // the unfused one
+  // whole unrolled block) to the end, then from 0; a gate column and its up
+  // column take the same start, so the fused result is the SwiGLU of the
+  // unfused one
+  constexpr int BLOCK = LPR * 8 * kGemvUnroll;   // K elements of an unrolled block
   int k_rot = 0;
-  if (K % 2048 == 0) {
-    const int pair = FUSED ? nt : nt % max(1, ldc / 2 / kGemvCols);
-    k_rot = ((g * kWideKRot + pair) * kGemvUnroll) % (K / 64) * 64;
+  if (K % 2048 == 0 && K % BLOCK == 0) {
+    const int pair = FUSED ? nt : nt % max(1, ldc / 2 / COLS);
+    k_rot = (g * kWideKRot + pair) % (K / BLOCK) * BLOCK;
   }
-  for (int r0 = 0; r0 < rows; r0 += kGemvRows) {
-    const int nr = min(kGemvRows, rows - r0);
-    const uint16_t* arow[kGemvRows];
-#pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) arow[r] = A + moe::a_row(tb, m0 + r0 + min(r, nr - 1)) * K;
-    float acc_g[kGemvRows], acc_u[kGemvRows];
-#pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) acc_g[r] = acc_u[r] = 0.0f;
-    // K in steps of 64 (8 lanes x 8 values): whole blocks of kGemvUnroll
-    // steps with every weight load, then every activation load (L1/L2 hits),
-    // issued before the arithmetic; then the remaining steps one at a time
-    auto block = [&](int kb, auto unroll) __attribute__((always_inline)) {
-      constexpr int U = decltype(unroll)::value;
-      uint4 vg[U], vu[U], va[U][kGemvRows];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = kb + u * 64 + kc * 8;
-        vg[u] = *reinterpret_cast<const uint4*>(wg + k);
-        if (FUSED) vu[u] = *reinterpret_cast<const uint4*>(wu + k);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int r = 0; r < kGemvRows; ++r)
-          va[u][r] = *reinterpret_cast<const uint4*>(arow[r] + kb + u * 64 + kc * 8);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float fg[8], fu[8];
-        bf16x8_to_f32(vg[u], fg);
-        if (FUSED) bf16x8_to_f32(vu[u], fu);
-#pragma unroll
-        for (int r = 0; r < kGemvRows; ++r) {
-          float fa[8];
-          bf16x8_to_f32(va[u][r], fa);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            acc_g[r] += fa[i] * fg[i];
-            if (FUSED) acc_u[r] += fa[i] * fu[i];
-          }
-        }
-      }
-    };
-    auto run = [&](int kb, int k_end) __attribute__((always_inline)) {
-      for (; kb + 64 * kGemvUnroll <= k_end; kb += 64 * kGemvUnroll) block(kb, Ic<kGemvUnroll>{});
-      for (; kb < k_end; kb += 64) block(kb, Ic<1>{});
-    };
-    run(k_rot, K);
-    run(0, k_rot);
-    // the 8 lanes of a weight row are consecutive: reduce over lanes 1, 2, 4 apart
-#pragma unroll
-    for (int r = 0; r < kGemvRows; ++r)
-#pragma unroll
-      for (int d = 1; d < 8; d <<= 1) {
-        acc_g[r] += __shfl_xor(acc_g[r], d);
-        if (FUSED) acc_u[r] += __shfl_xor(acc_u[r], d);
-      }
-    if (kc == 0) {
-#pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) {
-        if (r >= nr) break;
-        uint16_t* crow = C + (m0 + r0 + r) * ldc;
-        if (FUSED)
-          crow[col] = moe::swiglu_bf16(moe::f32_to_bf16(acc_g[r]), moe::f32_to_bf16(acc_u[r]));
-        else
-          crow[col] = moe::f32_to_bf16(acc_g[r]);
-      }
-    }
-  }
+  // one row (a decode token's expert, or a one-token dense group): the
+  // single-row passes, with a quarter of the activation loads
+  if (rows == 1)
+    gemv_rows<FUSED, LPR, 1>(A, wg, wu, tb, m0, rows, K, k_rot, kc, col, ldc, C);
+  else
+    gemv_rows<FUSED, LPR, kGemvRows>(A, wg, wu, tb, m0, rows, K, k_rot, kc, col, ldc, C);
 }
 
+// Lanes per weight row: 32 (8 rows a workgroup) when K is a multiple of 256,
+// else 8 (32 rows). The bytes in flight are the launch's weight rows times
+// the lanes per row times 64, which at 8 lanes left a one-token dense down
+// projection (7168 rows) far short of what HBM needs; on the one-token
+// Kimi-K2 shapes, with the single-row passes (interleaved, ms): shared
+// gate_up 0.120 -> 0.088, shared down 0.088 -> 0.053, routed gate_up 0.092
+// -> 0.080, routed down 0.061 -> 0.049.
 template <bool FUSED>
 int launch_gemv(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int K, int64_t w_stride,
                 int up_row, int ldc, uint16_t* C, hipStream_t stream, const char* name) {
-  const int n_tiles = ldc / kGemvCols;
+  const bool wide_rows = K % (32 * 8) == 0 && ldc % (256 / 32) == 0;
+  const int n_tiles = ldc / (wide_rows ? 256 / 32 : 256 / 8);
   const int64_t slots = tb.gs ? std::min<int64_t>(numel, E) : 1;
   const int64_t blocks = slots * n_tiles;
   if (blocks > 0x7FFFFFFF) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
-  grouped_gemv_kernel<FUSED><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(A, W, tb, E, numel, n_tiles, K,
-                                                                                w_stride, up_row, ldc, C);
+  if (wide_rows)
+    grouped_gemv_kernel<FUSED, 32><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(A, W, tb, E, numel, n_tiles, K,
+                                                                                      w_stride, up_row, ldc, C);
+  else
+    grouped_gemv_kernel<FUSED, 8><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(A, W, tb, E, numel, n_tiles, K,
+                                                                                     w_stride, up_row, ldc, C);
   return moe::check_launch(name);
 }
 
