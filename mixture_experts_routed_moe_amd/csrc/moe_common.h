@@ -40,6 +40,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2,
+// 4 and 8 (lanes shifted in from outside a 16-lane row add 0), then lane 15
+// of each row added to the next row and lane 31 to the upper two rows.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  int v = x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // The project's fp32 exponential. Every SwiGLU (standalone, fused into the
 // gate_up GEMM epilogue, fused into the FP8 quantizer) evaluates exactly this
 // sequence of IEEE binary32 operations, so their results agree bit for bit:

@@ -20,20 +20,6 @@ constexpr int kWideEgMinRowTiles = 32;  // ... and this many row tiles
 constexpr int kWideGroup = 16;        // tiles of a fixed group (the other mapping)
 constexpr int kWideGnMax = 8;         // column tiles of a fixed group, at most
 
-// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2,
-// 4 and 8 (lanes shifted in from outside a 16-lane row add 0), then lane 15
-// of each row added to the next row and lane 31 to the upper two rows.
-__device__ __forceinline__ int wave_incl_sum(int x) {
-  int v = x;
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
-  return v;
-}
-
 // Expert g, tile q inside it and the expert's row count n of the p-th 256-row
 // tile, counting ceil(gs[e] / 256) tiles per expert in expert order. The
 // group sizes of up to kFindBatch * 64 experts are loaded at once (one load

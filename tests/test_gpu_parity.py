@@ -1019,14 +1019,15 @@ def test_tile_quant_random_groups_and_overwrite(per_tile):
 
 
 @pytest.mark.parametrize("per_tile,swiglu,n_groups,K", [(False, False, 64, 2048), (True, False, 64, 2048),
-                                                        (False, True, 64, 2048), (False, False, 400, 256)])
+                                                        (False, True, 64, 2048), (False, False, 400, 256),
+                                                        (True, False, 700, 256)])
 def test_tile_quant_paired_blocks_overwrite(per_tile, swiglu, n_groups, K):
     """A grouped launch large enough that each workgroup takes two adjacent
     column blocks (over 2048 blocks; the per-tile SwiGLU form stays
-    unpaired; 400 groups take seven rounds of the group-size scan): random
-    ragged groups,
-    outputs pre-filled so every byte the contract covers must be written,
-    including the zero columns of the padded tails."""
+    unpaired; the group-size scan loads 512 sizes at a time, so 700 groups
+    take two passes of it): random ragged groups, outputs pre-filled so every
+    byte the contract covers must be written, including the zero columns of
+    the padded tails."""
     d = dev()
     rng = np.random.default_rng(95 + n_groups)
     sizes = rng.choice([0, 1, 5, 127, 128, 129, 300, 513, 1000], size=n_groups).astype(np.int32)
