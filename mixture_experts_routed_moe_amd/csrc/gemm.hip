@@ -229,6 +229,22 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(lds), 16, 0, 0);
 }
 
+// The buffer form of the direct-to-LDS load (buffer_load_dwordx4 ... lds):
+// 16 bytes per lane from the resource's base + voff + soff (voff per lane,
+// soff wave-uniform) into lds + 16 * lane. The step offset goes in as a
+// scalar, and, not being a FLAT instruction, it leaves the compiler's LDS
+// waits exact: while a global_load_lds is in flight the compiler waits for
+// every outstanding LDS read (lgkmcnt(0)) before an MFMA, the prefetched
+// fragments of the next sub-step included. Resource: stride 0, the largest
+// record count (the callers' offsets stay below 2^32), the gfx9 raw-buffer
+// word 3.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, static_cast<int>(voff), soff, 0, 0);
+}
+
 // Wait until at most N DMA loads of this wave are outstanding and its LDS
 // reads have returned, then barrier: after it, every wave's loads up to that
 // point have landed in LDS and every wave is done reading the slots it read
@@ -633,16 +649,17 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   constexpr int kBFragRow[4] = {0, 32, FUSED ? kWideW / 2 : 64, FUSED ? kWideW / 2 + 32 : 96};
 
   const int nk = K / BK;
-  const char* a_base = nullptr;  // set once the row offset is known (after W(0) is out)
+  const __amdgpu_buffer_rsrc_t w_rsrc = dma_rsrc(w_base);
+  __amdgpu_buffer_rsrc_t a_rsrc = w_rsrc;  // set once the row offset is known (after W(0) is out)
   // the operand with three slots runs two steps ahead (its loads are issued
   // last in a step), the other one step ahead
   constexpr int FIRST = kWideWDeep ? A_LOADS : B_LOADS;   // loads of the one-ahead operand
   constexpr int LAST = kWideWDeep ? B_LOADS : A_LOADS;    // loads of the two-ahead operand
   auto load_a = [&](int kt, int slot, int i) __attribute__((always_inline)) {
-    dma16(a_base + kt * BK * 2 + a_off[i], smem + a_lds0 + slot * kWideSlotBytes + i * RPL * ROWB);
+    dma16b(a_rsrc, a_off[i], kt * BK * 2, smem + a_lds0 + slot * kWideSlotBytes + i * RPL * ROWB);
   };
   auto load_w = [&](int kt, int slot, int i) __attribute__((always_inline)) {
-    dma16(w_base + kt * BK * 2 + b_off[i], smem + b_lds0 + slot * kWideSlotBytes + i * RPL * ROWB);
+    dma16b(w_rsrc, b_off[i], kt * BK * 2, smem + b_lds0 + slot * kWideSlotBytes + i * RPL * ROWB);
   };
   // FUSED: the SiLU table (32 KiB, one slot) takes the place of W(nk) in the
   // W slot that step would have used, loaded during step nk - 2 like a W part
@@ -650,9 +667,10 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   // step lands it
   static_assert(moe::kSiluTabMid * 4 == kWideSlotBytes && moe::kSiluTabMid / 4 / (64 * NW) == B_LOADS,
                 "the table loads like one W step");
+  const __amdgpu_buffer_rsrc_t tab_rsrc = dma_rsrc(g_gemm_silu_tab.v);
   auto load_tab = [&](int slot, int i) __attribute__((always_inline)) {
     const int c = (i * NW + wave) * 64;  // a wave-wide load fills 64 consecutive 16-byte pieces
-    dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab.v) + c + lane, smem + kWideWRing + slot * kWideSlotBytes + c * 16);
+    dma16b(tab_rsrc, static_cast<uint32_t>((c + lane) * 16), 0, smem + kWideWRing + slot * kWideSlotBytes + c * 16);
   };
   // prologue: W(0), which needs only the expert and the column tile, goes out
   // before the loads the A rows depend on (the group offset, then the
@@ -660,7 +678,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) load_w(0, 0, i);
   const int64_t m_start = (go_g ? static_cast<int64_t>(*go_g) : 0) + m_off;
-  a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
+  a_rsrc = dma_rsrc(gather ? A : A + m_start * K);
   wide_a_offsets<A_LOADS, NW, RPL>(a_off, gather, gather_k, m_start, rows, K, wave, lrow, lpos);
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) load_a(0, 0, i);
@@ -850,8 +868,9 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   const int lrow = lane / CPR;
   const int lpos = lane % CPR;
 
-  const char* a_base = nullptr;  // set once the row offset is known (after W(0) is out)
-  const char* w_base = reinterpret_cast<const char*>(Wb + static_cast<int64_t>(nt) * (FUSED ? kWideW / 2 : kWideW) * K);
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      dma_rsrc(Wb + static_cast<int64_t>(nt) * (FUSED ? kWideW / 2 : kWideW) * K);
+  __amdgpu_buffer_rsrc_t a_rsrc = w_rsrc;  // set once the row offset is known (after W(0) is out)
   uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
@@ -898,9 +917,9 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
     for (int j = 0; j < L; ++j) {
       if (j < first || j >= first + count) continue;
       if (j < B_LOADS)
-        dma16(w_base + ko + b_off[j], smem + slot_base + b_lds0 + j * RPL * ROWB);
+        dma16b(w_rsrc, b_off[j], ko, smem + slot_base + b_lds0 + j * RPL * ROWB);
       else
-        dma16(a_base + ko + a_off[j - B_LOADS], smem + slot_base + a_lds0 + (j - B_LOADS) * RPL * ROWB);
+        dma16b(a_rsrc, a_off[j - B_LOADS], ko, smem + slot_base + a_lds0 + (j - B_LOADS) * RPL * ROWB);
     }
   };
   // prologue: steps 0 .. S-2, W(0) first: it needs only the expert and the
@@ -909,7 +928,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   // that of issue(), so the waits are unchanged
   issue(0, 0, 0, B_LOADS);
   const int64_t m_start = (go_g ? static_cast<int64_t>(*go_g) : 0) + m_off;
-  a_base = reinterpret_cast<const char*>(gather ? A : A + m_start * K);
+  a_rsrc = dma_rsrc(gather ? A : A + m_start * K);
   wide_a_offsets<A_LOADS, NW, RPL>(a_off, gather, gather_k, m_start, rows, K, wave, lrow, lpos);
   issue(0, 0, B_LOADS, A_LOADS);
   if (nk > 1) issue(1, STAGE, 0, L);
@@ -967,7 +986,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
 #pragma unroll
     for (int i = 0; i < moe::kSiluTabMid / 4 / (64 * NW); ++i) {
       const int c = (i * NW + wave) * 64;
-      dma16(reinterpret_cast<const float4*>(g_gemm_silu_tab.v) + c + lane, smem + kTabOff + c * 16);
+      dma16b(dma_rsrc(g_gemm_silu_tab.v), static_cast<uint32_t>((c + lane) * 16), 0, smem + kTabOff + c * 16);
     }
   }
   if constexpr (KS == 2) {
