@@ -289,7 +289,8 @@ int fp8_block_quant_weights(const uint16_t* w, int64_t rows, int K, uint8_t* q, 
  * the decoded products, each operand times its scale, rounded once. The four
  * dispatch tables as for grouped_gemm_down (all NULL: one dense group, E = 1).
  * N and K multiples of 128, block_m = 128, padding_m a multiple of 128;
- * qa, qw, y 16-byte aligned. */
+ * qa, qw, y 16-byte aligned. MOE_ERR_UNSUPPORTED when numel * K or N * K
+ * (the A codes, one group's weight codes) reach 2^32 bytes. */
 int grouped_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                      const int32_t* group_sizes, const int32_t* group_offsets, const int32_t* group_padded_offsets,
                      const int32_t* group_idx_for_bx, int64_t numel, int E, int N, int K, int padding_m,
@@ -313,7 +314,8 @@ int grouped_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
  * Tables as for grouped_gemm_gate_up (NULL tables: one dense group, E = 1,
  * no sorted_pair). Limits: block_m == 128; H % 128 == 0; F % 128 == 0;
  * 16-byte aligned qa, qw, out. MOE_ERR_INVALID_ARG for inconsistent sizes or
- * tables; MOE_ERR_UNSUPPORTED for block_m != 128. */
+ * tables; MOE_ERR_UNSUPPORTED for block_m != 128, or when a_rows * H or
+ * 2F * H (the activation codes, one group's weight codes) reach 2^32 bytes. */
 int grouped_gemm_gate_up_fp8(const uint8_t* qa, const float* sa, int64_t a_rows, const int32_t* sorted_pair,
                              int top_k, const uint8_t* qw, const float* sw, const int32_t* group_sizes,
                              const int32_t* group_offsets, const int32_t* group_padded_offsets,

@@ -32,11 +32,20 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int f8_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // direct-to-LDS loads: lane i writes lds + 16 i (or + 4 i)
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+// The buffer form of the direct-to-LDS load (buffer_load_dword[x4] ... lds):
+// bytes from the resource's base + voff + soff into lds + size * lane. Unlike
+// the FLAT form it leaves the compiler's LDS waits exact while loads are in
+// flight, and takes the K step as a scalar offset; per-lane offsets are 32
+// bits (the hosts check that the A codes and one group's weight codes stay
+// below 4 GiB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
+__device__ __forceinline__ void dmab16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, static_cast<int>(voff), soff, 0, 0);
+}
+__device__ __forceinline__ void dmab4(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, static_cast<int>(voff), soff, 0, 0);
 }
 
 template <int N>
@@ -142,13 +151,12 @@ __device__ __forceinline__ void fp8_tile(uint8_t* smem, const uint8_t* __restric
   const int lrow = lane >> 3, lpos = lane & 7;
 
   // this wave's A rows (A_LD x 8) and 32 W rows of every step
-  const uint8_t* a_src[A_LD];
-  const uint8_t* w_src[4];
+  uint32_t a_src[A_LD], w_src[4];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int r = wave * (AR / 4) + i * 8 + lrow;
     const int rr = min(r, rows - 1);
-    a_src[i] = qa + moe::a_row(tb, m_start + rr) * K + (lpos ^ f8_swz(r)) * 16;
+    a_src[i] = static_cast<uint32_t>(moe::a_row(tb, m_start + rr) * K) + static_cast<uint32_t>((lpos ^ f8_swz(r)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -157,12 +165,15 @@ __device__ __forceinline__ void fp8_tile(uint8_t* smem, const uint8_t* __restric
     const int64_t wr = FUSED ? (r < kT / 2 ? static_cast<int64_t>(nt) * (kT / 2) + r
                                            : static_cast<int64_t>(up_row) + nt * (kT / 2) + (r - kT / 2))
                              : static_cast<int64_t>(nt) * kT + r;
-    w_src[i] = qw + (static_cast<int64_t>(g) * N + wr) * K + (lpos ^ f8_swz(r)) * 16;
+    w_src[i] = static_cast<uint32_t>(wr * K) + static_cast<uint32_t>((lpos ^ f8_swz(r)) * 16);
   }
   // the AR A row scales of a step, 64 a wave: waves past them reload the
   // first 64 into their own scratch slot
   const bool real_scale = wave * 64 < AR;
-  const float* sa_src = sa + moe::a_row(tb, m_start + min((real_scale ? wave * 64 : 0) + lane, rows - 1)) * nkb;
+  const uint32_t sa_src =
+      static_cast<uint32_t>(moe::a_row(tb, m_start + min((real_scale ? wave * 64 : 0) + lane, rows - 1)) * nkb * 4);
+  const __amdgpu_buffer_rsrc_t a_rsrc = f8_rsrc(qa), sa_rsrc = f8_rsrc(sa);
+  const __amdgpu_buffer_rsrc_t w_rsrc = f8_rsrc(qw + static_cast<int64_t>(g) * N * K);
   const int sa_dst = real_scale ? R::A_BYTES + kT * kT + wave * 64 * 4 : -1;
   uint8_t* const scratch = smem + kF8Lds - kF8Scratch + wave * 64 * 4;
   // the weight scale block of each of the wave's two 32-row MFMA blocks (128-row
@@ -175,10 +186,10 @@ __device__ __forceinline__ void fp8_tile(uint8_t* smem, const uint8_t* __restric
   auto issue = [&](int kb, int st) __attribute__((always_inline)) {
     uint8_t* base = smem + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) dma16(a_src[i] + kb * kT, base + (wave * (AR / 4) + i * 8) * kT);
+    for (int i = 0; i < A_LD; ++i) dmab16(a_rsrc, a_src[i], kb * kT, base + (wave * (AR / 4) + i * 8) * kT);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(w_src[i] + kb * kT, base + R::A_BYTES + (wave * 32 + i * 8) * kT);
-    dma4(sa_src + kb, sa_dst >= 0 ? base + sa_dst : scratch);
+    for (int i = 0; i < 4; ++i) dmab16(w_rsrc, w_src[i], kb * kT, base + R::A_BYTES + (wave * 32 + i * 8) * kT);
+    dmab4(sa_rsrc, sa_src, kb * 4, sa_dst >= 0 ? base + sa_dst : scratch);
   };
 
   floatx16 acc[TM][2];
@@ -336,6 +347,8 @@ extern "C" int grouped_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_
   if (!dense && (E < 1 || padding_m <= 0 || padding_m % kT != 0))
     return fail(MOE_ERR_INVALID_ARG, "%s: E=%d padding_m=%d (a positive multiple of 128)", name, E, padding_m);
   if (numel >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: numel >= 2^31", name);
+  if (numel * K >= (int64_t(1) << 32) || static_cast<int64_t>(N) * K >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: the A codes or one group's weight codes reach 4 GiB", name);
   if (numel == 0) return MOE_OK;
   if (!qa || !sa || !qw || !sw || !y) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
   if (!aligned16(qa) || !aligned16(qw) || !aligned16(y))
@@ -375,6 +388,8 @@ extern "C" int grouped_gemm_gate_up_fp8(const uint8_t* qa, const float* sa, int6
     return fail(MOE_ERR_INVALID_ARG, "%s: a_rows=%lld must be numel (compact rows) or numel/top_k (gather)", name,
                 (long long)a_rows);
   if (numel >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: numel >= 2^31", name);
+  if (a_rows * H >= (int64_t(1) << 32) || int64_t(2) * F * H >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: the A codes or one group's weight codes reach 4 GiB", name);
   if (numel == 0) return MOE_OK;
   if (!qa || !sa || !qw || !sw || !out) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
   if (!aligned16(qa) || !aligned16(qw) || !aligned16(out))

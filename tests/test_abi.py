@@ -130,6 +130,9 @@ def test_argument_errors_return_before_launch(lib):
     assert lib.grouped_gemm_fp8(*[None] * 8, 64, 1, 256, 128, 128, 64, None, None) == -2    # block_m != 128
     assert lib.grouped_gemm_fp8(*[None] * 8, 64, 2, 256, 128, 128, 128, None, None) == -1   # dense needs E=1
     assert lib.grouped_gemm_fp8(*[None] * 8, 0, 1, 256, 128, 128, 128, None, None) == 0
+    # 32-bit load offsets: A codes or one group's weight codes of 2^32 bytes are refused
+    assert lib.grouped_gemm_fp8(*[None] * 8, 1 << 21, 1, 256, 2048, 128, 128, None, None) == -2   # numel * K
+    assert lib.grouped_gemm_fp8(*[None] * 8, 64, 1, 1 << 20, 4096, 128, 128, None, None) == -2    # N * K
     # FP8 gate_up: a_rows must be numel (compact) or numel / top_k (gather); block_m 128 only
     lib.grouped_gemm_gate_up_fp8.argtypes = ([P, P, c.c_int64, P, c.c_int, P, P] + [P] * 4 + [c.c_int64] +
                                              [c.c_int] * 6 + [P, P])
@@ -141,6 +144,8 @@ def test_argument_errors_return_before_launch(lib):
                                         128, 128, 1, None, None) == -1   # gather without tables
     assert lib.grouped_gemm_gate_up_fp8(None, None, 0, 16, 2, None, None, 1, 1, 1, 1, 0, 2, 256, 256, 128, 128, 1,
                                         None, None) == 0         # nothing to do
+    assert lib.grouped_gemm_gate_up_fp8(None, None, 1 << 20, None, 1, None, None, None, None, None, None, 1 << 20, 1,
+                                        4096, 256, 128, 128, 1, None, None) == -2   # a_rows * H reaches 2^32
     # routing limits
     lib.moe_topk_softmax.argtypes = [P, P, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int, P, P, P]
     assert lib.moe_topk_softmax(None, None, 4, 2048, 8, 0, 1, None, None, None) == -2
