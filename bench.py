@@ -679,14 +679,19 @@ def main():
 
 
 def gemm_source_sha() -> str:
-    """First 16 hex digits of the sha256 over the GEMM kernels' sources
-    (gemm.hip, then wide_sched.h, then moe_common.h): the revision a traffic
-    figure belongs to."""
+    """First 16 hex digits of the sha256 over the GEMM kernels' code (gemm.hip,
+    then wide_sched.h, then moe_common.h, each with its // comments, trailing
+    blanks and empty lines removed; the files hold no // inside a string and
+    no block comment): the revision a traffic figure belongs to, unchanged by
+    an edit of comments only."""
     import hashlib
     h = hashlib.sha256()
     for name in ("gemm.hip", "wide_sched.h", "moe_common.h"):
-        with open(os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mixture_experts_routed_moe_amd", "csrc", name), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -461,8 +461,9 @@ __global__ __launch_bounds__(kThreads, OCC) void grouped_gemm_pipe_kernel(
 // rows (8 accumulator tiles), so while one wave of a SIMD waits on a load
 // issue, a barrier or an LDS read, the other keeps the matrix core busy
 // (measured on the DeepSeek-V3-shaped routed gate_up: 2.83 ms against 3.02
-// ms with four 128 x 128 waves). A wave whose rows are all past the tile's
-// valid rows skips its MFMAs.
+// ms with four 128 x 128 waves). In the small-row rings a wave whose rows
+// are all past the tile's valid rows skips its MFMAs; a full tile has more
+// than 128 valid rows, and its waves compute every row tile.
 //
 // An expert's only or last tile often has 128 rows or fewer (most experts of
 // a skewed routing have a few rows): such a tile loads only 64 or 128 A rows
