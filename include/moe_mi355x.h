@@ -164,7 +164,15 @@ int moe_permute(const uint16_t* hidden, const int32_t* sorted_pair, const int32_
  * block_m). Passing group_sizes = NULL (and the other three tables NULL)
  * treats A as one dense group of numel rows with E = 1 (the shared expert,
  * TileOPs #778 "SharedExpertMLPKernel").
- * Limits: block_m in {64, 128}; H % 64 == 0; F % 64 == 0; numel < 2^31. */
+ * Limits: block_m in {64, 128}; H % 64 == 0; F % 64 == 0; numel < 2^31.
+ * Streams: some shapes run a persistent kernel (a fixed grid that claims its
+ * tiles from device counters); each stream has its own counters (the first
+ * 64 streams used; later streams, and hipStreamPerThread, take the kernel
+ * with one workgroup per tile), and launches on one stream run in order. So
+ * calls on different streams may overlap, but one graph captured from these
+ * calls must not be replayed on two streams at the same time, nor replayed
+ * while a call on its capture stream runs (the same holds for
+ * grouped_gemm_gate_up_gather and grouped_gemm_down). */
 int grouped_gemm_gate_up(const uint16_t* x_perm, const uint16_t* w_gate_up,
                          const int32_t* group_sizes, const int32_t* group_offsets,
                          const int32_t* group_padded_offsets, const int32_t* group_idx_for_bx,

@@ -1,7 +1,8 @@
 // Grouped GEMM C[e] = A[e] @ W[e]^T for the routed experts on bf16 MFMA.
 //
 // Work decomposition: a workgroup computes one row tile by one column tile
-// of one expert. Row tiles are found from the dispatch tables (the compact
+// of one expert at a time (the persistent form of the 256-row kernel walks a
+// list of them). Row tiles are found from the dispatch tables (the compact
 // expert-major row space that the routing tables define); a tile past an
 // expert's rows, or past the last expert, has no rows and returns at once. A
 // is the compact [numel, K] layout: rows past a tile's valid count are never
@@ -10,7 +11,10 @@
 // Five kernels, chosen per launch by launch() below:
 //  * grouped_gemm_wide_kernel (the production path for 128-row blocks): 256 x
 //    256 tiles, eight waves, direct-to-LDS loads through a ring of stages, the
-//    tile order of wide_sched.h; see the comment above it;
+//    tile order of wide_sched.h; see the comment above it. Its persistent
+//    form, grouped_gemm_wide_persistent_kernel, runs the same tile bodies on
+//    a grid of one workgroup per CU that claims tiles at run time (chosen for
+//    small experts, see launch_wide);
 //  * grouped_gemm_pipe_kernel: 128 x 256 tiles on the same kind of ring, for
 //    dense launches with too few 256-row tiles to fill the chip, K not a
 //    multiple of 64, and operands past the wide kernel's 32-bit offsets;
@@ -30,6 +34,8 @@
 // in separate accumulators, so the epilogue pairs them in registers:
 // h = bf16(silu(bf16(g)) * bf16(u)).
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "moe_common.h"
 #include "wide_sched.h"
@@ -583,12 +589,12 @@ struct Ic {
   static constexpr int value = V;
 };
 
-template <bool FUSED, int NW>
+template <bool FUSED, int NW, typename KDone>
 __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ Wb, const int32_t* __restrict__ go_g,
                                                int64_t m_off, int rows, int nt,
                                                int K, int up_row, int ldc, uint16_t* __restrict__ C,
-                                               const int32_t* __restrict__ gather, int gather_k) {
+                                               const int32_t* __restrict__ gather, int gather_k, KDone&& k_done) {
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
   constexpr int AROWS = kWideRows;
   constexpr int WM = NW / 2;                         // wave rows (two wave columns)
@@ -754,6 +760,7 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
     if (kt + 4 < nk) step(Ic<4 % kWideASlots>{}, Ic<4 % kWideWSlots>{}, kt + 4);
     if (kt + 5 < nk) step(Ic<5 % kWideASlots>{}, Ic<5 % kWideWSlots>{}, kt + 5);
   }
+  k_done();
 
   // FUSED with a single K step (no step nk - 2): the table goes into the last
   // W slot once every wave is past its last fragment read
@@ -839,12 +846,13 @@ struct StageShape<128> {
   static constexpr int TMW = 2, WR = 2, TNW = 4, WC = 2, KS = 2;
 };
 
-template <bool FUSED, int AR, int NW>
+template <bool FUSED, int AR, int NW, typename KDone>
 __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* __restrict__ A,
                                                 const uint16_t* __restrict__ Wb, const int32_t* __restrict__ go_g,
                                                 int64_t m_off, int rows, int nt,
                                                 int K, int up_row, int ldc, uint16_t* __restrict__ C,
-                                                const int32_t* __restrict__ gather, int gather_k, int k0) {
+                                                const int32_t* __restrict__ gather, int gather_k, int k0,
+                                                KDone&& k_done) {
   using SS = StageShape<AR>;
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
   constexpr int TMW = SS::TMW, TNW = SS::TNW, WR = SS::WR, WC = SS::WC, KS = SS::KS;
@@ -977,6 +985,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
       if (kt + 3 < nk) step(Ic<3>{}, kt + 3);
     }
   }
+  k_done();
 
   // FUSED: the SiLU table goes into the ring's last 32 KiB once every wave is
   // past its last fragment read (above the K-split exchange)
@@ -1070,18 +1079,22 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   }
 }
 
-template <bool FUSED, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel,
-    moe::WideGrid wg, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C) {
-  constexpr int SMEM = kWideLds;
-  static_assert(SMEM <= 160 * 1024, "LDS ring too large");
-  static_assert(SMEM >= 128 * 1024, "the half-tile exchange needs 128 KiB");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-
+// Slot w of the wide mapping: the tile body for its row count (nothing for a
+// slot past the last tile).
+//
+// k_done() runs once per call: after the tile's last MFMA step, before its
+// epilogue (or at once for an empty slot).
+template <bool FUSED, int NW, typename KDone>
+__device__ __forceinline__ void wide_tile(uint8_t* smem, const uint16_t* __restrict__ A,
+                                          const uint16_t* __restrict__ W, const Tables& tb, int E, int64_t numel,
+                                          const moe::WideGrid& wg, int K, int64_t w_stride, int up_row, int ldc,
+                                          uint16_t* __restrict__ C, int w, KDone&& k_done) {
   int g, nt;
   int64_t m_off, r;  // the tile's first row inside its group, rows left from there
-  if (!moe::wide_tile_at(tb, E, numel, wg, blockIdx.x, g, nt, m_off, r)) return;
+  if (!moe::wide_tile_at(tb, E, numel, wg, w, g, nt, m_off, r)) {
+    k_done();
+    return;
+  }
   const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
   // the group's offset is read by the tile after its first weight loads are out
@@ -1089,12 +1102,84 @@ __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
   // the small-row tiles' first K block (see kWideKRot)
   const int k0 = K % 2048 == 0 ? (g * kWideKRot) % (K / 64) : 0;
   if (rows <= 64)
-    wide_stage_tile<FUSED, 64, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k, k0);
+    wide_stage_tile<FUSED, 64, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k, k0,
+                                   k_done);
   else if (rows <= kWideRows / 2)
     wide_stage_tile<FUSED, 128, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k,
-                                    k0);
+                                    k0, k_done);
   else
-    wide_ring_tile<FUSED, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k);
+    wide_ring_tile<FUSED, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k, k_done);
+}
+
+constexpr int kWideLdsUsed = kWideLds;
+static_assert(kWideLdsUsed <= 160 * 1024, "LDS ring too large");
+static_assert(kWideLdsUsed >= 128 * 1024, "the half-tile exchange needs 128 KiB");
+
+// One workgroup per slot of the mapping (the hardware places workgroup w on
+// XCD w % 8, as the mapping assumes).
+template <bool FUSED, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel,
+    moe::WideGrid wg, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWideLdsUsed];
+  wide_tile<FUSED, NW>(smem, A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C, static_cast<int>(blockIdx.x),
+                       [] {});
+}
+
+// Persistent form: a fixed grid of one workgroup per CU (the ring takes the
+// CU's whole LDS) walks the same slots. The slots w = 8 j + x of XCD x are
+// handed out in the order of j, as the hardware hands out a one-tile-per-
+// workgroup grid: workgroup b (on XCD x = b % 8) starts with j = b / 8 and
+// then takes j = G / 8 + c, where c is its claim on XCD x's counter (G the
+// grid, a multiple of 8), until j passes the last slot. A workgroup claims
+// its next slot after the last MFMA step of its current tile, so the atomic's
+// round trip is hidden behind the tile's epilogue, and the result goes to the
+// other waves through LDS once the tile is done. (Claiming when a tile starts
+// reserves the next slot a whole tile early and broke the order's timing:
+// 2% slower; claiming after the epilogue was no faster.)
+//
+// Counters: kClaimSlots x 8 in device memory, zero when the code object is
+// loaded. A workgroup that starts inside the slot range claims until a claim
+// fails, so a launch makes exactly nx claims on each of its counters (nx the
+// slots per XCD: the successful ones, nx - G / 8 if positive, plus one failed
+// claim per such workgroup, min(G / 8, nx)); the claim that returns nx - 1 is
+// the last and puts the counter back to zero. Every launch thus finds and
+// leaves its counters at zero, with no reset launch (also under graph
+// replay). Launches that run at the same time need different counters: the
+// host gives each stream its own slot, and launches on one stream run in
+// order.
+constexpr int kClaimSlots = 64;
+__device__ uint32_t g_wide_claims[kClaimSlots * 8];
+
+template <bool FUSED, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_persistent_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel,
+    moe::WideGrid wg, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int slot) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWideLdsUsed];
+  // the slots of the actual row tiles (the host's m_tiles is an upper bound)
+  if (tb.gs != nullptr) wg.m_tiles = moe::wide_row_tiles(tb.gs, E);
+  const int x = static_cast<int>(blockIdx.x & 7);
+  const int nx = static_cast<int>(moe::wide_blocks(wg, wg.m_tiles) >> 3);
+  uint32_t* claim = g_wide_claims + slot * 8 + x;
+  const int g8 = static_cast<int>(gridDim.x >> 3);
+  int j = static_cast<int>(blockIdx.x >> 3);
+  while (j < nx) {
+    uint32_t c = 0;
+    wide_tile<FUSED, NW>(smem, A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C, j * 8 + x, [&] {
+      if (threadIdx.x == 0) c = atomicAdd(claim, 1u);
+    });
+    // every wave is past its LDS reads of the tile (no DMA load is in flight
+    // at a tile's end)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (threadIdx.x == 0) {
+      if (c == static_cast<uint32_t>(nx - 1)) atomicExch(claim, 0u);
+      *reinterpret_cast<volatile int*>(smem) = g8 + static_cast<int>(c);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    j = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(smem));
+    // read before the next tile's loads overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
 }
 
 // Group shape for the tile order: GN column tiles (a divisor of n_tiles, at
@@ -1124,6 +1209,55 @@ int launch_pipe(const uint16_t* A, const uint16_t* W, Tables tb, int64_t numel, 
 
 constexpr int kWideWaves = 8;
 
+// The claim counters of the streams seen so far: stream i (in order of
+// first use, on any device) owns slot i. -1 once every slot is taken, and
+// for hipStreamPerThread, whose one handle names a different stream in each
+// host thread.
+int claim_slot(hipStream_t stream) {
+  static std::mutex mu;
+  static hipStream_t seen[kClaimSlots];
+  static int n = 0;
+  if (stream == hipStreamPerThread) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (seen[i] == stream) return i;
+  if (n == kClaimSlots) return -1;
+  seen[n] = stream;
+  return n++;
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// The wide GEMMs run persistent when an expert's weight matrix (K x the
+// output columns, bf16) is at most kPersistentMaxExpertBytes and the experts
+// hold at least kPersistentMinRows rows on average (numel / E), the mapping
+// has more slots than the grid of one workgroup per CU and the stream has a
+// claim slot; otherwise one workgroup per slot. Measured against one
+// workgroup per slot (interleaved runs, bit-identical outputs):
+//  * Qwen3-shaped prefill (6 MiB experts of 256 rows on average): gate_up
+//    0.300 -> 0.293 ms, down 0.172 -> 0.168 ms, the forward 0.520 -> 0.499 ms;
+//  * slower: the DeepSeek-V3 and Kimi-K2 shapes (29 to 59 MiB experts), 1 to
+//    3% (DeepSeek-V3 gate_up 2.737 -> 2.779 ms, down 1.433 -> 1.449 ms); the
+//    Qwen3-shaped decode (32 rows per expert) 2%; the aligned 16 MiB experts
+//    of 1024 rows (K = 4096, N = 2048) 3%; the 8 MiB ones (K = 1024, N =
+//    4096) even.
+// Claiming from one counter for all XCDs instead, which loses the order's
+// L2 sharing, was slower on every shape.
+constexpr int64_t kPersistentMaxExpertBytes = int64_t(8) << 20;
+constexpr int64_t kPersistentMinRows = 128;
+
 template <bool FUSED>
 int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int n_tiles, int K,
                 int64_t w_stride, int up_row, int ldc, uint16_t* C, hipStream_t stream, const char* name) {
@@ -1131,8 +1265,16 @@ int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t 
   int64_t blocks;
   if (!moe::wide_grid(numel, E, tb.gs != nullptr, n_tiles, wg, blocks))
     return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
-  grouped_gemm_wide_kernel<FUSED, kWideWaves><<<static_cast<unsigned>(blocks), 64 * kWideWaves, 0, stream>>>(
-      A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C);
+  const int grid = device_cus() / 8 * 8;
+  const bool persistent = static_cast<int64_t>(K) * n_tiles * kWideW * 2 <= kPersistentMaxExpertBytes &&
+                          numel >= kPersistentMinRows * E;
+  const int slot = persistent && grid > 0 && blocks > grid ? claim_slot(stream) : -1;
+  if (slot >= 0)
+    grouped_gemm_wide_persistent_kernel<FUSED, kWideWaves><<<static_cast<unsigned>(grid), 64 * kWideWaves, 0, stream>>>(
+        A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C, slot);
+  else
+    grouped_gemm_wide_kernel<FUSED, kWideWaves><<<static_cast<unsigned>(blocks), 64 * kWideWaves, 0, stream>>>(
+        A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C);
   return moe::check_launch(name);
 }
 

@@ -63,6 +63,32 @@ struct WideGrid {
   int eg;        // 1: the expert-aware mapping
 };
 
+// Workgroup slots of the mapping (tiles past the last row tile included) for
+// m_tiles row tiles; a multiple of 8.
+__host__ __device__ inline int64_t wide_blocks(const WideGrid& wg, int64_t m_tiles) {
+  if (wg.eg) return (m_tiles + 7) / 8 * 8 * wg.n_tiles;
+  const int64_t groups = (m_tiles + wg.gm - 1) / wg.gm * (wg.n_tiles / wg.gn);
+  return (groups + 7) / 8 * 8 * wg.gm * wg.gn;
+}
+
+// Row tiles of the grouped row space, sum over e of ceil(gs[e] / 256),
+// computed by each wave on its own (same batched loads as find_wide_tile).
+__device__ __forceinline__ int wide_row_tiles(const int32_t* __restrict__ gs, int E) {
+  const int lane = threadIdx.x & 63;
+  int t = 0;
+  for (int base0 = 0; base0 < E; base0 += 64 * kFindBatch) {
+    int cnt[kFindBatch];
+#pragma unroll
+    for (int b = 0; b < kFindBatch; ++b) {
+      const int e = base0 + b * 64 + lane;
+      cnt[b] = e < E ? gs[e] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < kFindBatch; ++b) t += (cnt[b] + (kWideRows - 1)) / kWideRows;
+  }
+  return __builtin_amdgcn_readlane(wave_incl_sum(t), 63);
+}
+
 // Geometry and grid size for numel compact rows over E groups (grouped: with
 // dispatch tables) and n_tiles column tiles; false if the grid is too large.
 inline bool wide_grid(int64_t numel, int E, bool grouped, int n_tiles, WideGrid& wg, int64_t& blocks) {
@@ -80,11 +106,10 @@ inline bool wide_grid(int64_t numel, int E, bool grouped, int n_tiles, WideGrid&
   // 2.44 ms and down 1.31 -> 1.28 ms (interleaved A/B); with 6 or 8 (the Qwen3
   // shapes) the fixed 16-tile groups are as fast or faster
   const int eg = n_tiles >= kWideEgMinCols && m_tiles >= kWideEgMinRowTiles;
-  const int64_t groups = ceil_div(m_tiles, gm) * (n_tiles / gn);
-  blocks = eg ? ceil_div(m_tiles, 8) * 8 * n_tiles : ceil_div(groups, 8) * 8 * gm * gn;
-  if (blocks > 0x7FFFFFFF || m_tiles > 0x7FFFFFFF) return false;
+  if (m_tiles > 0x7FFFFFFF) return false;
   wg = WideGrid{static_cast<int>(m_tiles), n_tiles, gm, gn, eg};
-  return true;
+  blocks = wide_blocks(wg, m_tiles);
+  return blocks <= 0x7FFFFFFF;
 }
 
 // The tile of workgroup w: expert g, column tile nt, first row m_off inside

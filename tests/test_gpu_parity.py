@@ -449,6 +449,78 @@ def test_grouped_gemm_wide_expert_groups(fused):
         assert_bf16_close(bits(y), oracle.grouped_gemm(bits(xp), bits(wd), gs, go), "down (16 col tiles)")
 
 
+def test_wide_persistent_claims_repeat_streams_graph():
+    """The 256-row kernel runs persistent (one workgroup per CU claiming
+    tiles from per-stream counters that each launch returns to zero) when its
+    tile list outnumbers the CUs. Outputs pre-filled with NaN bits so a
+    skipped tile shows: the first call against the oracle, then the same
+    bytes from repeated calls, from calls of another shape in between, from
+    two streams at once and from three replays of a captured graph."""
+    d = dev()
+    sizes = [0, 1, 127, 128, 129, 255, 256, 257, 700, 1300, 2100, 513, 1025]
+    E, H, F = len(sizes), 128, 2048
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    ids_np = ids_np[np.random.default_rng(12).permutation(ids_np.size)][:, None]
+    tb = mx.moe_align(_t(ids_np, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    T = ids_np.shape[0]
+    key = moe_synth.tensor_key(78, 0)
+    xp = moe_synth.normal_bf16(key, (T, H), 1.0, d)
+    wgu = moe_synth.normal_bf16(key + 1, (E, 2 * F, H), H ** -0.5, d)
+    # a second shape between the calls: 40 experts of 0 .. 600 rows, 8 column
+    # tiles (the fixed tile groups), also above one tile per CU
+    sizes_o = np.random.default_rng(13).integers(0, 601, 40)
+    ids_o = np.repeat(np.arange(40, dtype=np.int32), sizes_o)[:, None]
+    tbo = mx.moe_align(_t(ids_o, d), 40, 128, 128)
+    xo = moe_synth.normal_bf16(key + 2, (ids_o.shape[0], 256), 1.0, d)
+    wo = moe_synth.normal_bf16(key + 3, (40, 2048, 256), 256 ** -0.5, d)
+    gso, goo = host(tbo["group_sizes"]), host(tbo["group_offsets"])
+
+    def nan_like(n, cols):
+        return torch.full((n, cols), -1, dtype=torch.int16, device=d).view(torch.bfloat16)
+
+    def run(out, stream=None):
+        out.view(torch.int16).fill_(-1)
+        if stream is None:
+            return mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, True, out)
+        with torch.cuda.stream(stream):
+            return mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, True, out)
+
+    h1 = run(nan_like(T, F))
+    gu = mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, False)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(xp), bits(wgu), gs, go), "gate_up")
+    assert np.array_equal(bits(h1), oracle.swiglu(bits(gu), F))
+    gu_o = mx.grouped_gemm_gate_up(xo, wo, tbo, 128, 128, False)
+    assert_bf16_close(bits(gu_o), oracle.grouped_gemm(bits(xo), bits(wo), gso, goo), "gate_up (40 experts)")
+    ref_other = mx.grouped_gemm_gate_up(xo, wo, tbo, 128, 128, True)
+    assert np.array_equal(bits(ref_other), oracle.swiglu(bits(gu_o), 1024))
+    for i in range(3):
+        o = mx.grouped_gemm_gate_up(xo, wo, tbo, 128, 128, True)
+        assert torch.equal(o, ref_other), f"other shape, call {i}"
+        assert torch.equal(run(nan_like(T, F)), h1), f"repeat {i}"
+    s1, s2 = torch.cuda.Stream(d), torch.cuda.Stream(d)
+    s1.wait_stream(torch.cuda.current_stream(d))
+    s2.wait_stream(torch.cuda.current_stream(d))
+    outs = [(nan_like(T, F), s1), (nan_like(T, F), s2), (nan_like(T, F), s1), (nan_like(T, F), s2)]
+    for o, s in outs:
+        run(o, s)
+    torch.cuda.synchronize()
+    for i, (o, _) in enumerate(outs):
+        assert torch.equal(o, h1), f"two streams, output {i}"
+    g_out = nan_like(T, F)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mx.grouped_gemm_gate_up(xp, wgu, tb, 128, 128, True, g_out)
+    for i in range(3):
+        g_out.view(torch.int16).fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_out, h1), f"graph replay {i}"
+        assert torch.equal(run(nan_like(T, F)), h1), f"eager after replay {i}"
+    say("persistent wide kernel: repeats, two streams and graph replays identical")
+
+
 @pytest.mark.parametrize("n_out", [4096, 256])
 def test_grouped_gemm_more_than_512_experts(n_out):
     """700 experts: the tile search loads the group sizes 512 at a time, so the
