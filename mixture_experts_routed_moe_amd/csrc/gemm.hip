@@ -788,7 +788,10 @@ __device__ __forceinline__ void wide_ring_tile(uint8_t* smem, const uint16_t* __
   // gate_up 1-2% faster (DeepSeek-V3 2.753 -> 2.726 ms, Qwen3 prefill 0.284
   // -> 0.278 ms); the unfused down 2-11% slower (DeepSeek-V3 1.435 -> 1.469
   // ms, Qwen3 prefill 0.166 -> 0.184 ms), whose stores then touch 32 rows
-  // at 16 bytes each
+  // at 16 bytes each. Staging the unfused 256 x 256 tile through LDS for
+  // whole 16-byte row stores (16 per lane instead of 128 two-byte ones) left
+  // the down projection's time unchanged (DeepSeek-V3 1.450 -> 1.448 ms,
+  // Kimi-K2 T=4096 and the aligned GLM-5 shapes within 0.3%).
   auto store = [&](auto use_tab) __attribute__((always_inline)) {
     constexpr bool TAB = decltype(use_tab)::value != 0;
 #pragma unroll
