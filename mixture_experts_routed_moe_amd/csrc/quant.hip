@@ -236,17 +236,20 @@ __global__ __launch_bounds__(kQuantThreads) void tile_quant_kernel(const uint16_
   const int lrow0 = rg * 4;   // this thread's first row inside the block
 
   // all 8 (SWIGLU) or 4 loads first; rows past the block's valid rows read
-  // its last row (in bounds) and are masked
+  // its last row (in bounds) and are masked. The input is read once, so the
+  // loads are non-temporal (same bytes; interleaved, MALL flushed: 131072 x
+  // 6144 over 256 groups 696.7 -> 690.0 us per block, 906 -> 899 us per tile,
+  // SwiGLU 131072 x 8192 708.7 -> 690.1 us; M = 32768 unchanged, 89.8 -> 89.7 us)
   uint4 gb[NB][4], ub[SWIGLU ? NB : 1][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = r0 + min(lrow0 + i, rows - 1);
     const uint16_t* rp = x + m * (SWIGLU ? 2 : 1) * K;
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) gb[cb][i] = *reinterpret_cast<const uint4*>(rp + (fb0 + cb) * kTile + cg * 8);
+    for (int cb = 0; cb < NB; ++cb) gb[cb][i] = moe::load_stream16(rp + (fb0 + cb) * kTile + cg * 8);
     if (SWIGLU) {
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) ub[cb][i] = *reinterpret_cast<const uint4*>(rp + K + (fb0 + cb) * kTile + cg * 8);
+      for (int cb = 0; cb < NB; ++cb) ub[cb][i] = moe::load_stream16(rp + K + (fb0 + cb) * kTile + cg * 8);
     }
   }
   if (SWIGLU) load_silu_table(tab, tid, kQuantThreads);
