@@ -521,6 +521,33 @@ def test_wide_persistent_claims_repeat_streams_graph():
     say("persistent wide kernel: repeats, two streams and graph replays identical")
 
 
+def test_wide_persistent_more_streams_than_claim_slots():
+    """The library keeps claim counters for 64 streams; calls on later streams
+    take the one-workgroup-per-tile kernel. 72 new streams (past the 64 slots
+    whatever this process used before), each call's output pre-filled with NaN
+    bits: every output equal to the first call's bytes, whichever kernel ran."""
+    d = dev()
+    sizes = np.random.default_rng(14).integers(0, 601, 40)
+    ids = np.repeat(np.arange(40, dtype=np.int32), sizes)[:, None]
+    tb = mx.moe_align(_t(ids, d), 40, 128, 128)
+    key = moe_synth.tensor_key(77, 0)
+    x = moe_synth.normal_bf16(key, (ids.shape[0], 256), 1.0, d)
+    w = moe_synth.normal_bf16(key + 1, (40, 2048, 256), 256 ** -0.5, d)
+    ref = mx.grouped_gemm_gate_up(x, w, tb, 128, 128, True)
+    streams = [torch.cuda.Stream(d) for _ in range(72)]
+    outs = []
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream(d))
+        o = torch.full_like(ref.view(torch.int16), -1).view(torch.bfloat16)
+        s.wait_stream(torch.cuda.current_stream(d))
+        with torch.cuda.stream(s):
+            mx.grouped_gemm_gate_up(x, w, tb, 128, 128, True, o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref), f"stream {i}"
+
+
 @pytest.mark.parametrize("n_out", [4096, 256])
 def test_grouped_gemm_more_than_512_experts(n_out):
     """700 experts: the tile search loads the group sizes 512 at a time, so the
