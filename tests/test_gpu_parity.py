@@ -548,6 +548,40 @@ def test_wide_persistent_more_streams_than_claim_slots():
         assert torch.equal(o, ref), f"stream {i}"
 
 
+@pytest.mark.parametrize("case", ["700_experts", "dense"])
+def test_wide_persistent_against_oracle(case):
+    """The persistent form on shapes the forwards do not reach: 700 experts of
+    100-200 rows (the tile count scans the group sizes in several 512-expert
+    batches; two K steps), and one dense group of 65536 rows (no tables). Fused
+    and unfused, outputs pre-filled with NaN bits, against the oracle."""
+    d = dev()
+    key = moe_synth.tensor_key(76, 0 if case == "dense" else 1)
+    if case == "dense":
+        E, H, F, n = 1, 256, 256, 65536
+        tb = None
+        x = moe_synth.normal_bf16(key, (n, H), 1.0, d)
+        w = moe_synth.normal_bf16(key + 1, (2 * F, H), H ** -0.5, d)
+        gs, go = np.array([n], dtype=np.int32), np.array([0], dtype=np.int32)
+        w3 = w.view(1, 2 * F, H)
+    else:
+        E, H, F = 700, 128, 128
+        sizes = np.random.default_rng(15).integers(100, 201, E)
+        ids = np.repeat(np.arange(E, dtype=np.int32), sizes)
+        ids = ids[np.random.default_rng(16).permutation(ids.size)][:, None]
+        tb = mx.moe_align(_t(ids, d), E, 128, 128)
+        gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+        n = ids.shape[0]
+        x = moe_synth.normal_bf16(key, (n, H), 1.0, d)
+        w = moe_synth.normal_bf16(key + 1, (E, 2 * F, H), H ** -0.5, d)
+        w3 = w
+    gu = torch.full((n, 2 * F), -1, dtype=torch.int16, device=d).view(torch.bfloat16)
+    mx.grouped_gemm_gate_up(x, w, tb, 128, 128, False, gu)
+    assert_bf16_close(bits(gu), oracle.grouped_gemm(bits(x), bits(w3), gs, go), f"gate_up ({case})")
+    h = torch.full((n, F), -1, dtype=torch.int16, device=d).view(torch.bfloat16)
+    mx.grouped_gemm_gate_up(x, w, tb, 128, 128, True, h)
+    assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
+
+
 @pytest.mark.parametrize("n_out", [4096, 256])
 def test_grouped_gemm_more_than_512_experts(n_out):
     """700 experts: the tile search loads the group sizes 512 at a time, so the
