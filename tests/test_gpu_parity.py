@@ -1298,11 +1298,13 @@ SHARED_SMALL = moe_synth.MoEConfig(85, "shared_small", T=64, H=256, F=128, E=16,
                                    block_m=128, shared_F=384, scoring="sigmoid")
 
 
-@pytest.mark.parametrize("name,side,fp8", [("qwen3_decode", False, False), ("shared_small", False, False),
-                                           ("shared_small", True, False), ("shared_small", True, True)])
+@pytest.mark.parametrize("name,side,fp8", [("qwen3_decode", False, False), ("qwen3_prefill", False, False),
+                                           ("shared_small", False, False), ("shared_small", True, False),
+                                           ("shared_small", True, True)])
 def test_forward_graph_replay(name, side, fp8):
     """The forward captured as a HIP graph (with the shared expert forked onto
-    a second stream for side=True, both routed GEMMs in FP8 for fp8=True):
+    a second stream for side=True, both routed GEMMs in FP8 for fp8=True; the
+    Qwen3-shaped prefill's routed GEMMs run the persistent 256-row kernel):
     every replay, with eager work of the program between replays, gives the
     eager forward's bytes; new inputs written into the static tensors give
     the eager forward of those inputs (for bf16, matching the oracle)."""
