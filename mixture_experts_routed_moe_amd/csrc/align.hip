@@ -3,7 +3,8 @@
 // the stable expert-major permutation).
 //
 // Three launches over chunks of 1024 (token, slot) pairs, each linear in the
-// number of pairs:
+// number of pairs (inputs of at most 2 chunks take one launch instead,
+// align_small_kernel):
 //   1. count: per-chunk expert histogram counts[c][e] (LDS atomics; counts
 //             are order-free).
 //   2. scan:  per expert, the exclusive prefix of counts over chunks, in
@@ -199,6 +200,114 @@ __global__ __launch_bounds__(kChunk) void align_rank_kernel(
   }
 }
 
+// Inputs of at most kSmallChunks chunks: the same tables from one workgroup,
+// in one launch (the three launches' cost at a decode batch is their launch
+// and latency, not their work). Histogram with LDS atomics, the block-wide
+// scans of the rank kernel, then the chunks in order, each ranked as in the
+// rank kernel with a running per-expert base, so positions follow pair order
+// exactly as there. Measured against the three launches (interleaved, whole
+// forwards, same bytes): Kimi-K2-shaped T = 1 0.270 -> 0.262 ms, T = 32
+// unchanged; at four chunks (the Qwen3-shaped decode, 4096 pairs) the chunks
+// ranked one after another cost as much as the launches (0.2500 -> 0.2514
+// ms), so the one-launch form stops at two.
+constexpr int kSmallChunks = 2;
+
+__global__ __launch_bounds__(kChunk) void align_small_kernel(
+    const int32_t* __restrict__ ids, int numel, int E, int id_bits, int padding_m, int block_m, int m_blocks,
+    int32_t* __restrict__ group_sizes, int32_t* __restrict__ group_offsets,
+    int32_t* __restrict__ group_padded_offsets, int32_t* __restrict__ group_idx_for_bx,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_row) {
+  __shared__ int s_hist[kMaxE];
+  __shared__ int s_base[kMaxE];           // compact start of the next chunk's pairs of expert e
+  __shared__ int s_gpo[kMaxE];
+  __shared__ int s_wave_cnt[kWaves][kMaxE];
+  __shared__ int s_wsum[2][kWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunks = (numel + kChunk - 1) / kChunk;
+  if (tid < E) s_hist[tid] = 0;
+  for (int i = tid; i < kWaves * E; i += kChunk) s_wave_cnt[i / E][i % E] = 0;
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int p = c * kChunk + tid;
+    if (p < numel) {
+      const int e = ids[p];
+      if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);
+    }
+  }
+  __syncthreads();
+
+  const int total = tid < E ? s_hist[tid] : 0;
+  const int padded = ((total + padding_m - 1) / padding_m) * padding_m;
+  const int inc_t = wave_inclusive_scan(total, lane);
+  const int inc_p = wave_inclusive_scan(padded, lane);
+  if (lane == 63) {
+    s_wsum[0][wave] = inc_t;
+    s_wsum[1][wave] = inc_p;
+  }
+  __syncthreads();
+  int pre_t = 0, pre_p = 0;
+  for (int w = 0; w < wave; ++w) {
+    pre_t += s_wsum[0][w];
+    pre_p += s_wsum[1][w];
+  }
+  if (tid < E) {
+    const int go = pre_t + inc_t - total;
+    const int gpo = pre_p + inc_p - padded;
+    s_base[tid] = go;
+    s_gpo[tid] = gpo;
+    group_sizes[tid] = total;
+    group_offsets[tid] = go;
+    group_padded_offsets[tid] = gpo;
+  }
+  __syncthreads();
+  for (int bx = tid; bx < m_blocks; bx += kChunk) {
+    const int64_t x = static_cast<int64_t>(bx) * block_m;
+    int lo = 0, hi = E;  // invariant: s_gpo[lo] <= x (s_gpo[0] == 0)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_gpo[mid] <= x) lo = mid; else hi = mid;
+    }
+    group_idx_for_bx[bx] = lo;
+  }
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int p = c * kChunk + tid;
+    int e = (p < numel) ? ids[p] : 0;
+    const bool valid = (p < numel) && e >= 0 && e < E;
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint64_t below = peers & ((1ull << lane) - 1ull);
+    if (valid && below == 0) s_wave_cnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    int chunk_total = 0;  // this chunk's pairs of expert tid
+    if (tid < E) {
+      for (int w = 0; w < kWaves; ++w) {
+        const int cnt = s_wave_cnt[w][tid];
+        s_wave_cnt[w][tid] = chunk_total;
+        chunk_total += cnt;
+      }
+    }
+    __syncthreads();
+    if (valid) {
+      const int pos = s_base[e] + s_wave_cnt[wave][e] + __popcll(below);
+      sorted_pair[pos] = p;
+      pair_to_row[p] = pos;
+    }
+    __syncthreads();
+    if (tid < E) {
+      s_base[tid] += chunk_total;
+      for (int w = 0; w < kWaves; ++w) s_wave_cnt[w][tid] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 extern "C" size_t moe_align_workspace_bytes(int64_t numel, int E) {
@@ -219,6 +328,12 @@ int align_launch(const int32_t* topk_ids, int64_t numel, int E, int padding_m, i
   const int nchunks = numel > 0 ? static_cast<int>(ceil_div(numel, kChunk)) : 1;
   int id_bits = 1;
   while ((1 << id_bits) < E) ++id_bits;
+  if (nchunks <= kSmallChunks) {
+    align_small_kernel<<<1, kChunk, 0, stream>>>(topk_ids, static_cast<int>(numel), E, id_bits, padding_m, block_m,
+                                                 static_cast<int>(m_blocks), group_sizes, group_offsets,
+                                                 group_padded_offsets, group_idx_for_bx, sorted_pair, pair_to_row);
+    return check_launch("moe_align(small)");
+  }
   align_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_ids, static_cast<int>(numel), E, counts);
   int rc = check_launch("moe_align(count)");
   if (rc) return rc;

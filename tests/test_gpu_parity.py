@@ -105,6 +105,10 @@ def _align_cases(golden_dir):
     yield "pad128_block64", np.stack([rng.permutation(16)[:4] for _ in range(777)]).astype(np.int32), 16, 128, 64
     yield "E1", np.zeros((50, 1), np.int32), 1, 16, 16
     yield "E1000", np.stack([rng.permutation(1000)[:8] for _ in range(2100)]).astype(np.int32), 1000, 32, 32
+    # around the one-launch form's limit of two 1024-pair chunks
+    yield "two_chunks", np.stack([rng.permutation(64)[:2] for _ in range(750)]).astype(np.int32), 64, 128, 128
+    yield "2048_pairs", np.stack([rng.permutation(48)[:2] for _ in range(1024)]).astype(np.int32), 48, 128, 128
+    yield "2049_pairs", rng.integers(0, 48, (2049, 1)).astype(np.int32), 48, 128, 64
     for name in ("tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill", "kimi_k2_t4096"):
         cfg = moe_synth.CONFIGS[name]
         bias = moe_synth.expert_bias(cfg)
