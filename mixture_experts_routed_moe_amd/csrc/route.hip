@@ -2,7 +2,8 @@
 //
 // Each lane holds ceil(E/64) routing logits (router score plus the optional
 // per-expert bias) in registers. k rounds of a wave-wide argmax (value, then
-// lower expert id) pick the experts in descending order; the selected logits
+// lower expert id; DPP max reductions, no LDS permutes) pick the experts in
+// descending order; the selected logits
 // stay in the lane that equals their slot. Scores: softmax over all E (the
 // sum over every lane's logits), or the logistic sigmoid of each logit;
 // renormalised weights divide by the selected experts' score sum, which for
@@ -13,11 +14,28 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-__device__ __forceinline__ void better(float& bv, int& be, float ov, int oe) {
-  if (ov > bv || (ov == bv && oe < be)) {
-    bv = ov;
-    be = oe;
-  }
+// Largest of the 64 lanes' values, in every lane: DPP row shifts by 1, 2, 4
+// and 8, then the row broadcasts (as wave_incl_sum, with max; lanes shifted
+// in from outside a row give 0, which is at most every value), then lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  uint32_t v = x;
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Order-preserving code of a logit: for numbers, a > b iff key(a) > key(b)
+// as unsigned integers, and a == b (-0 and +0 included) iff the keys are
+// equal; every number's code is at least 2, a NaN's is 1 (below every
+// number), and 0 marks nothing.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 1u;
+  const uint32_t b = __float_as_uint(f) == 0x80000000u ? 0u : __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 __device__ __forceinline__ float wave_sum(float s) {
@@ -45,21 +63,31 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_softmax_kernel(
   float my_v = -INFINITY;
   int my_e = 0;
   float top_v = 0.0f;
+  // each round: the largest remaining logit (a wave max over order-preserving
+  // codes), then the lowest expert id holding it (a wave max over 1024 - id),
+  // both DPP reductions; the winner's logit is read from its lane
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
+    uint32_t mk = 0;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u)) better(bv, be, v[i], e);
+      if (e < E && !((taken >> i) & 1u)) mk = max(mk, order_key(v[i]));
     }
+    const uint32_t top = wave_max_u32(mk);
+    uint32_t lid = 0;  // 1024 - the lowest id of this lane whose logit has the top code
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      better(bv, be, ov, oe);
+    for (int i = VPT - 1; i >= 0; --i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u) && order_key(v[i]) == top) lid = 1024u - static_cast<uint32_t>(e);
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    const int be = 1024 - static_cast<int>(wave_max_u32(lid));
+    const int bi = be >> 6;
+    float sel = v[0];
+#pragma unroll
+    for (int i = 1; i < VPT; ++i)
+      if (i == bi) sel = v[i];
+    const float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel), be & 63));
+    if ((be & 63) == lane) taken |= 1u << bi;
     if (lane == j) {
       my_v = bv;
       my_e = be;
