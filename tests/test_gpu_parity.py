@@ -78,6 +78,28 @@ def test_route_ties_and_small_shapes():
 
 
 @pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
+def test_route_signed_zero_ties_and_infinities(scoring):
+    """The argmax rounds compare order-preserving codes of the logits: -0 and
+    +0 tie (the lower id first, as the oracle's stable sort), -inf entries
+    rank last, large magnitudes keep their order."""
+    d = dev()
+    rng = np.random.default_rng(4)
+    T, E, k = 64, 200, 8
+    vals = np.array([0.0, -0.0, -np.inf, 3.0e38, -3.0e38, 1.0e-38, -1.0e-38, 0.5, -0.5], np.float32)
+    logits = vals[rng.integers(0, vals.size, size=(T, E))]
+    logits[:, 0] = np.float32(-0.0)          # every row holds signed zeros and at least one finite logit
+    logits[0] = np.float32(-0.0)             # a row of -0 only
+    logits[1, ::2] = np.float32(0.0)         # alternating +0 / -0
+    logits[1, 1::2] = np.float32(-0.0)
+    logits[2] = -np.inf
+    logits[2, 150:] = np.float32(-0.0)       # -inf everywhere but 50 zeros
+    ids, w = mx.moe_topk_softmax(_t(logits, d), k, scoring=scoring)
+    rid, rw = oracle.route(logits, k, None, scoring)
+    assert np.array_equal(host(ids), rid)
+    np.testing.assert_allclose(host(w), rw, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
 @pytest.mark.parametrize("renormalize", [True, False])
 def test_route_scoring_bias_renormalize(scoring, renormalize):
     d = dev()
