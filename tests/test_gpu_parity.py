@@ -131,6 +131,8 @@ def _align_cases(golden_dir):
     yield "two_chunks", np.stack([rng.permutation(64)[:2] for _ in range(750)]).astype(np.int32), 64, 128, 128
     yield "2048_pairs", np.stack([rng.permutation(48)[:2] for _ in range(1024)]).astype(np.int32), 48, 128, 128
     yield "2049_pairs", rng.integers(0, 48, (2049, 1)).astype(np.int32), 48, 128, 64
+    yield "E1000_two_chunks", np.stack([rng.permutation(1000)[:2] for _ in range(1000)]).astype(np.int32), 1000, 128, 128
+    yield "eight_chunks", np.stack([rng.permutation(32)[:8] for _ in range(1024)]).astype(np.int32), 32, 128, 128
     for name in ("tiny", "qwen3_decode", "qwen3_prefill", "dsv3_prefill", "kimi_k2_t4096"):
         cfg = moe_synth.CONFIGS[name]
         bias = moe_synth.expert_bias(cfg)
