@@ -870,13 +870,20 @@ struct StageShape<128> {
   static constexpr int TMW = 2, WR = 2, TNW = 4, WC = 2, KS = 2;
 };
 
-template <bool FUSED, int AR, int NW, typename KDone>
+//
+// NC column tiles (nt .. nt + NC - 1, unfused tiles of at most 64 rows and
+// K / 64 a multiple of the ring depth): the ring runs on over NC x K / 64
+// steps, column tile c's weights one tile stride further, and each column
+// tile is stored at its last step while the next one's first steps are in
+// flight, so a short-K launch pays the tile's setup (the tile search, the
+// group offset, the first loads' latency) once per NC tiles.
+template <bool FUSED, int AR, int NW, typename KDone, int NC = 1>
 __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* __restrict__ A,
                                                 const uint16_t* __restrict__ Wb, const int32_t* __restrict__ go_g,
                                                 int64_t m_off, int rows, int nt,
                                                 int K, int up_row, int ldc, uint16_t* __restrict__ C,
                                                 const int32_t* __restrict__ gather, int gather_k, int k0,
-                                                KDone&& k_done) {
+                                                KDone&& k_done, Ic<NC> = {}) {
   using SS = StageShape<AR>;
   constexpr int BK = 64, CPR = 8, ROWB = 128, RPL = 8;
   constexpr int TMW = SS::TMW, TNW = SS::TNW, WR = SS::WR, WC = SS::WC, KS = SS::KS;
@@ -892,6 +899,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   static_assert(WR * WC * KS == NW && WR * TMW * 32 == AR && WC * TNW * 32 == kWideW, "wave layout");
   static_assert(S >= 3 && S <= 4 && (S - 2) * L <= 63, "ring");
   static_assert(A_LOADS >= 1 && AR % (NW * RPL) == 0, "A loads");
+  static_assert(NC == 1 || (!FUSED && KS == 1), "column-tile runs: unfused, one K group");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -942,15 +950,18 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   };
 
   const int nk = K / BK;
-  auto issue = [&](int kt, int slot_base, int first, int count) __attribute__((always_inline)) {
-    // step kt reads K block (kt + k0) mod nk
-    const int kr = kt + k0;
+  const int nkv = nk * NC;  // steps over all NC column tiles
+  const int w_col = kWideW * K * 2;  // bytes of one column tile's weight rows
+  auto issue = [&](int kv, int slot_base, int first, int count) __attribute__((always_inline)) {
+    // step kv reads K block (kt + k0) mod nk of column tile c (kv = c nk + kt)
+    const int c = NC == 1 ? 0 : kv / nk;
+    const int kr = kv - c * nk + k0;
     const int ko = (kr >= nk ? kr - nk : kr) * BK * 2;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
       if (j < first || j >= first + count) continue;
       if (j < B_LOADS)
-        dma16b(w_rsrc, b_off[j], ko, smem + slot_base + b_lds0 + j * RPL * ROWB);
+        dma16b(w_rsrc, b_off[j], ko + c * w_col, smem + slot_base + b_lds0 + j * RPL * ROWB);
       else
         dma16b(a_rsrc, a_off[j - B_LOADS], ko, smem + slot_base + a_lds0 + (j - B_LOADS) * RPL * ROWB);
     }
@@ -964,9 +975,9 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   a_rsrc = dma_rsrc(gather ? A : A + m_start * K);
   wide_a_offsets<A_LOADS, NW, RPL>(a_off, gather, gather_k, m_start, rows, K, wave, lrow, lpos);
   issue(0, 0, B_LOADS, A_LOADS);
-  if (nk > 1) issue(1, STAGE, 0, L);
+  if (nkv > 1) issue(1, STAGE, 0, L);
   if constexpr (S > 3) {
-    if (nk > 2) issue(2, 2 * STAGE, 0, L);
+    if (nkv > 2) issue(2, 2 * STAGE, 0, L);
   }
 
   bf16x8_t af[2][TMW], bfr[2][TNW];
@@ -974,7 +985,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
     constexpr int SL = decltype(slot_c)::value;
     constexpr int SL_NEXT = (SL + S - 1) % S;  // step kt + S - 1 reuses the slot of step kt - 1
     // steps kt+1 .. kt+S-2 (those that exist) may still be in flight
-    const int later = nk - 1 - kt;
+    const int later = nkv - 1 - kt;
     if (later >= S - 2) wait_dma_barrier<(S - 2) * L>();
     else wait_dma_barrier_dyn<L, S - 3>(later);
     auto read_frags = [&](int i, int buf) __attribute__((always_inline)) {
@@ -985,7 +996,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
       for (int tn = 0; tn < TNW; ++tn)
         bfr[buf][tn] = *reinterpret_cast<const bf16x8_t*>(smem + b_rd[i] + SL * STAGE + b_frag_row(tn) * ROWB);
     };
-    const bool ahead = kt + S - 1 < nk;
+    const bool ahead = kt + S - 1 < nkv;
     read_frags(0, 0);
 #pragma unroll
     for (int i = 0; i < MY_NS; ++i) {
@@ -1002,12 +1013,37 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
       if (ahead) issue(kt + S - 1, SL_NEXT * STAGE, i * PER, PER);
     }
   };
-  for (int kt = 0; kt < nk; kt += S) {
-    step(Ic<0>{}, kt);
-    if (kt + 1 < nk) step(Ic<1>{}, kt + 1);
-    if (kt + 2 < nk) step(Ic<2>{}, kt + 2);
-    if constexpr (S > 3) {
-      if (kt + 3 < nk) step(Ic<3>{}, kt + 3);
+  // column tile c, then (NC > 1) its store while the next one's loads fly;
+  // the slots follow kt mod S because nk is then a multiple of S
+  for (int c = 0; c < NC; ++c) {
+    const int kb = c * nk;
+    for (int kt = 0; kt < nk; kt += S) {
+      step(Ic<0>{}, kb + kt);
+      if (kt + 1 < nk) step(Ic<1>{}, kb + kt + 1);
+      if (kt + 2 < nk) step(Ic<2>{}, kb + kt + 2);
+      if constexpr (S > 3) {
+        if (kt + 3 < nk) step(Ic<3>{}, kb + kt + 3);
+      }
+    }
+    if constexpr (NC > 1) {
+      if (c + 1 < NC) {
+        const int row_a = wr * TMW * 32;
+#pragma unroll
+        for (int tm = 0; tm < TMW; ++tm) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row_a + tm * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+            if (row < rows) {
+              uint16_t* crow = C + (m_start + row) * ldc;
+#pragma unroll
+              for (int tn = 0; tn < TNW; ++tn)
+                crow[(nt + c) * kWideW + wc * TNW * 32 + tn * 32 + (lane & 31)] = moe::f32_to_bf16(acc[tm][tn][r]);
+            }
+#pragma unroll
+            for (int tn = 0; tn < TNW; ++tn) acc[tm][tn][r] = 0.0f;
+          }
+        }
+      }
     }
   }
   k_done();
@@ -1092,7 +1128,7 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
           uint16_t* crow = C + (m_start + row) * ldc;
 #pragma unroll
           for (int tn = 0; tn < TNW; ++tn)
-            crow[nt * kWideW + wc * TNW * 32 + tn * 32 + (lane & 31)] = moe::f32_to_bf16(acc[tm][tn][r]);
+            crow[(nt + NC - 1) * kWideW + wc * TNW * 32 + tn * 32 + (lane & 31)] = moe::f32_to_bf16(acc[tm][tn][r]);
         }
       }
     }
@@ -1114,22 +1150,14 @@ __device__ __forceinline__ void wide_stage_tile(uint8_t* smem, const uint16_t* _
   }
 }
 
-// Slot w of the wide mapping: the tile body for its row count (nothing for a
-// slot past the last tile).
-//
-// k_done() runs once per call: after the tile's last MFMA step, before its
-// epilogue (or at once for an empty slot).
+// The tile of expert g, rows m_off .. m_off + min(r, 256) of its group, by
+// column tile nt: the tile body for its row count. k_done() runs once: after
+// the tile's last MFMA step, before its epilogue.
 template <bool FUSED, int NW, typename KDone>
-__device__ __forceinline__ void wide_tile(uint8_t* smem, const uint16_t* __restrict__ A,
-                                          const uint16_t* __restrict__ W, const Tables& tb, int E, int64_t numel,
-                                          const moe::WideGrid& wg, int K, int64_t w_stride, int up_row, int ldc,
-                                          uint16_t* __restrict__ C, int w, KDone&& k_done) {
-  int g, nt;
-  int64_t m_off, r;  // the tile's first row inside its group, rows left from there
-  if (!moe::wide_tile_at(tb, E, numel, wg, w, g, nt, m_off, r)) {
-    k_done();
-    return;
-  }
+__device__ __forceinline__ void wide_tile_body(uint8_t* smem, const uint16_t* __restrict__ A,
+                                               const uint16_t* __restrict__ W, const Tables& tb, int K,
+                                               int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C, int g,
+                                               int nt, int64_t m_off, int64_t r, KDone&& k_done) {
   const int rows = r >= kWideRows ? kWideRows : static_cast<int>(r);
   const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
   // the group's offset is read by the tile after its first weight loads are out
@@ -1146,19 +1174,63 @@ __device__ __forceinline__ void wide_tile(uint8_t* smem, const uint16_t* __restr
     wide_ring_tile<FUSED, NW>(smem, A, Wb, go_g, m_off, rows, nt, K, up_row, ldc, C, tb.gather, tb.gather_k, k_done);
 }
 
+// ring depth of the 64-row stage tiles (four 40 KiB stages)
+constexpr int kSmallRowStages = kWideLds / (64 * 128 + kWideW * 128);
+static_assert(kSmallRowStages == 4, "64-row stage ring");
+
+// Slot w of the wide mapping: the tile body for its row count (nothing for a
+// slot past the last tile). With NC == 2 (unfused only) the slot covers
+// column tiles 2 nt and 2 nt + 1: one continued ring (wide_stage_tile's NC) for an unfused
+// tile of at most 64 rows when K / 64 is a multiple of its depth, else the
+// two tiles one after the other.
+//
+// k_done() runs once per call: after the slot's last MFMA step, before its
+// epilogue (or at once for an empty slot).
+template <bool FUSED, int NW, int NC = 1, typename KDone>
+__device__ __forceinline__ void wide_tile(uint8_t* smem, const uint16_t* __restrict__ A,
+                                          const uint16_t* __restrict__ W, const Tables& tb, int E, int64_t numel,
+                                          const moe::WideGrid& wg, int K, int64_t w_stride, int up_row, int ldc,
+                                          uint16_t* __restrict__ C, int w, KDone&& k_done) {
+  int g, nt;
+  int64_t m_off, r;  // the tile's first row inside its group, rows left from there
+  if (!moe::wide_tile_at(tb, E, numel, wg, w, g, nt, m_off, r)) {
+    k_done();
+    return;
+  }
+  static_assert(NC == 1 || (NC == 2 && !FUSED), "column-tile pairs: unfused");
+  if constexpr (NC == 2) {
+    {
+      if (r <= 64 && (K / 64) % kSmallRowStages == 0) {
+        const uint16_t* Wb = W + static_cast<int64_t>(g) * w_stride;
+        const int32_t* go_g = tb.gs == nullptr ? nullptr : tb.go + g;
+        const int k0 = K % 2048 == 0 ? (g * kWideKRot) % (K / 64) : 0;
+        wide_stage_tile<false, 64, NW>(smem, A, Wb, go_g, m_off, static_cast<int>(r), 2 * nt, K, up_row, ldc, C,
+                                       tb.gather, tb.gather_k, k0, k_done, Ic<2>{});
+        return;
+      }
+    }
+    wide_tile_body<FUSED, NW>(smem, A, W, tb, K, w_stride, up_row, ldc, C, g, 2 * nt, m_off, r, [] {});
+    // every wave is past its LDS reads before the second tile's loads land
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    wide_tile_body<FUSED, NW>(smem, A, W, tb, K, w_stride, up_row, ldc, C, g, 2 * nt + 1, m_off, r, k_done);
+    return;
+  }
+  wide_tile_body<FUSED, NW>(smem, A, W, tb, K, w_stride, up_row, ldc, C, g, nt, m_off, r, k_done);
+}
+
 constexpr int kWideLdsUsed = kWideLds;
 static_assert(kWideLdsUsed <= 160 * 1024, "LDS ring too large");
 static_assert(kWideLdsUsed >= 128 * 1024, "the half-tile exchange needs 128 KiB");
 
 // One workgroup per slot of the mapping (the hardware places workgroup w on
-// XCD w % 8, as the mapping assumes).
-template <bool FUSED, int NW>
+// XCD w % 8, as the mapping assumes); NC column tiles per slot.
+template <bool FUSED, int NW, int NC>
 __global__ __launch_bounds__(64 * NW, 1) void grouped_gemm_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, Tables tb, int E, int64_t numel,
     moe::WideGrid wg, int K, int64_t w_stride, int up_row, int ldc, uint16_t* __restrict__ C) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWideLdsUsed];
-  wide_tile<FUSED, NW>(smem, A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C, static_cast<int>(blockIdx.x),
-                       [] {});
+  wide_tile<FUSED, NW, NC>(smem, A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C, static_cast<int>(blockIdx.x),
+                           [] {});
 }
 
 // Persistent form: a fixed grid of one workgroup per CU (the ring takes the
@@ -1292,23 +1364,35 @@ int device_cus() {
 // L2 sharing, was slower on every shape.
 constexpr int64_t kPersistentMaxExpertBytes = int64_t(8) << 20;
 constexpr int64_t kPersistentMinRows = 128;
+constexpr int kPairMaxK = 1024;
+constexpr int64_t kPairMaxRows = 64;
 
 template <bool FUSED>
 int launch_wide(const uint16_t* A, const uint16_t* W, Tables tb, int E, int64_t numel, int n_tiles, int K,
                 int64_t w_stride, int up_row, int ldc, uint16_t* C, hipStream_t stream, const char* name) {
+  // column-tile pairs: unfused grouped launches of short K (at most 16 steps)
+  // whose experts average at most 64 rows, so most slots are small-row tiles
+  // whose setup is a large part of their time
+  const int nc = !FUSED && tb.gs != nullptr && K <= kPairMaxK && n_tiles % 2 == 0 &&
+                         numel <= kPairMaxRows * static_cast<int64_t>(E)
+                     ? 2
+                     : 1;
   moe::WideGrid wg;
   int64_t blocks;
-  if (!moe::wide_grid(numel, E, tb.gs != nullptr, n_tiles, wg, blocks))
+  if (!moe::wide_grid(numel, E, tb.gs != nullptr, n_tiles / nc, wg, blocks))
     return moe::fail(MOE_ERR_UNSUPPORTED, "%s: grid too large", name);
   const int grid = device_cus() / 8 * 8;
   const bool persistent = static_cast<int64_t>(K) * n_tiles * kWideW * 2 <= kPersistentMaxExpertBytes &&
                           numel >= kPersistentMinRows * E;
-  const int slot = persistent && grid > 0 && blocks > grid ? claim_slot(stream) : -1;
+  const int slot = nc == 1 && persistent && grid > 0 && blocks > grid ? claim_slot(stream) : -1;
   if (slot >= 0)
     grouped_gemm_wide_persistent_kernel<FUSED, kWideWaves><<<static_cast<unsigned>(grid), 64 * kWideWaves, 0, stream>>>(
         A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C, slot);
+  else if (nc == 2)
+    grouped_gemm_wide_kernel<false, kWideWaves, 2><<<static_cast<unsigned>(blocks), 64 * kWideWaves, 0, stream>>>(
+        A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C);
   else
-    grouped_gemm_wide_kernel<FUSED, kWideWaves><<<static_cast<unsigned>(blocks), 64 * kWideWaves, 0, stream>>>(
+    grouped_gemm_wide_kernel<FUSED, kWideWaves, 1><<<static_cast<unsigned>(blocks), 64 * kWideWaves, 0, stream>>>(
         A, W, tb, E, numel, wg, K, w_stride, up_row, ldc, C);
   return moe::check_launch(name);
 }

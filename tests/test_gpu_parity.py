@@ -610,6 +610,31 @@ def test_wide_persistent_against_oracle(case):
     assert np.array_equal(bits(h), oracle.swiglu(bits(gu), F))
 
 
+@pytest.mark.parametrize("K", [768, 192])
+def test_down_column_tile_pairs(K):
+    """Unfused grouped launches of short K whose experts average at most 64
+    rows give each workgroup two adjacent 256-column tiles: one continued
+    ring for the tiles of at most 64 rows when K / 64 is a multiple of the
+    ring depth (K = 768), else the two tiles in turn (K = 192, and the
+    experts of 100 and 300 rows). Output pre-filled with NaN bits, against
+    the oracle."""
+    d = dev()
+    E, H = 40, 512
+    sizes = np.random.default_rng(17).integers(0, 41, E)
+    sizes[3], sizes[7], sizes[11] = 100, 300, 64
+    ids = np.repeat(np.arange(E, dtype=np.int32), sizes)
+    ids = ids[np.random.default_rng(18).permutation(ids.size)][:, None]
+    assert ids.shape[0] <= 64 * E
+    tb = mx.moe_align(_t(ids, d), E, 128, 128)
+    gs, go = host(tb["group_sizes"]), host(tb["group_offsets"])
+    key = moe_synth.tensor_key(75, K)
+    h = moe_synth.normal_bf16(key, (ids.shape[0], K), 1.0, d)
+    wd = moe_synth.normal_bf16(key + 1, (E, H, K), K ** -0.5, d)
+    y = torch.full((ids.shape[0], H), -1, dtype=torch.int16, device=d).view(torch.bfloat16)
+    mx.grouped_gemm_down(h, wd, tb, 128, 128, y)
+    assert_bf16_close(bits(y), oracle.grouped_gemm(bits(h), bits(wd), gs, go), f"down K={K}")
+
+
 @pytest.mark.parametrize("n_out", [4096, 256])
 def test_grouped_gemm_more_than_512_experts(n_out):
     """700 experts: the tile search loads the group sizes 512 at a time, so the
